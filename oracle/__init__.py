@@ -1,0 +1,248 @@
+"""CPU oracle for the quantized recurrent-state update (test infrastructure).
+
+Only the tests, ``__graft_entry__.smoke()`` and the bench's ``cpu_baseline``
+leg may import this package.  The product path (``mamba_decode_amd``) never
+does, and this package never imports the product path.
+
+The arithmetic lives in ``ssq_oracle.c`` (plain single-threaded C, built with
+``-O2 -ffp-contract=off``); this module builds it with gcc when needed and
+marshals numpy arrays into it.  States are kept unpacked: one int32 code per
+entry plus one fp32 scale and zero point per row, or a plain fp32 state for the
+unquantized control.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass, field
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ssq_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+CFLAGS = ["-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+          "-Wall", "-Wextra", "-Wno-unused-parameter"]
+
+# format name -> (bits, asymmetric); bits == 0 is the fp32 control
+FORMATS = {
+    "fp32": (0, 0),
+    "int8_sym": (8, 0),
+    "int8_asym": (8, 1),
+    "int4_sym": (4, 0),
+    "int4_asym": (4, 1),
+}
+
+
+def build(force: bool = False) -> str:
+    """Compile ``ssq_oracle.c`` into ``liboracle.so`` next to it."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def bind(path: str):
+    """Load an oracle shared library from ``path`` and declare its C signatures."""
+    L = ctypes.CDLL(path)
+    f32p = ctypes.POINTER(ctypes.c_float)
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    ci, cl = ctypes.c_int, ctypes.c_int64
+    L.orc_decay.argtypes = [ctypes.c_float, ctypes.c_float]
+    L.orc_decay.restype = ctypes.c_float
+    L.orc_quantize_row.argtypes = [f32p, ci, ci, ci, i32p, f32p, f32p, f32p]
+    L.orc_quantize_row.restype = None
+    L.orc_quantize_rows.argtypes = [cl, ci, ci, ci, f32p, i32p, f32p, f32p, f32p]
+    L.orc_quantize_rows.restype = None
+    L.orc_dequantize_rows.argtypes = [cl, ci, i32p, f32p, f32p, f32p]
+    L.orc_dequantize_rows.restype = None
+    L.orc_mamba2_step.argtypes = [ci, ci, ci, ci, ci, ci, ci, i32p, f32p, f32p, f32p,
+                                  f32p, f32p, f32p, f32p, f32p, f32p, f32p, ci, f32p, f32p]
+    L.orc_mamba2_step.restype = ci
+    L.orc_mamba2_scan.argtypes = [ci, ci, ci, ci, ci, ci, ci, ci, i32p, f32p, f32p, f32p,
+                                  f32p, f32p, f32p, f32p, f32p, f32p, f32p, ci]
+    L.orc_mamba2_scan.restype = ci
+    L.orc_mamba2_rows_scan.argtypes = [cl, ci, ci, ci, ci, i32p, f32p, f32p, f32p, f32p,
+                                       f32p, f32p, f32p, f32p, f32p, f32p, ci]
+    L.orc_mamba2_rows_scan.restype = ci
+    L.orc_delta_step.argtypes = [ci, ci, ci, ci, ci, ci, i32p, f32p, f32p, f32p, f32p, f32p,
+                                 f32p, f32p, f32p, f32p, ci, f32p, f32p]
+    L.orc_delta_step.restype = ci
+    return L
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        _lib = bind(build())
+    return _lib
+
+
+def _f(a):
+    if a is None:
+        return None
+    assert a.dtype == np.float32 and a.flags.c_contiguous, (a.dtype, a.flags)
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+
+
+def _i(a):
+    if a is None:
+        return None
+    assert a.dtype == np.int32 and a.flags.c_contiguous
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def _c32(a):
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+@dataclass
+class State:
+    """One layer's state for every row: ``code`` [rows][n] int32, ``scale``/``zero`` [rows]
+    (quantized), or ``h`` [rows][n] fp32 (``fmt == 'fp32'``)."""
+    fmt: str
+    rows: int
+    n: int
+    code: np.ndarray | None = None
+    scale: np.ndarray | None = None
+    zero: np.ndarray | None = None
+    h: np.ndarray | None = None
+    shape: tuple = field(default=())
+
+    @property
+    def bits(self):
+        return FORMATS[self.fmt][0]
+
+    @property
+    def asym(self):
+        return FORMATS[self.fmt][1]
+
+    def copy(self) -> "State":
+        c = lambda a: None if a is None else a.copy()  # noqa: E731
+        return State(self.fmt, self.rows, self.n, c(self.code), c(self.scale), c(self.zero),
+                     c(self.h), self.shape)
+
+    def dequant(self) -> np.ndarray:
+        """The fp32 value the state stands for, [rows][n]."""
+        if self.fmt == "fp32":
+            return self.h.copy()
+        out = np.empty((self.rows, self.n), np.float32)
+        lib().orc_dequantize_rows(self.rows, self.n, _i(self.code), _f(self.scale),
+                                  _f(self.zero), _f(out))
+        return out
+
+
+def quantize_rows(h: np.ndarray, fmt: str, bits: int | None = None, asym: int | None = None,
+                  with_v: bool = False):
+    """Refit and round every row of ``h`` [rows][n]; returns (code, scale, zero[, v])."""
+    h = _c32(h)
+    rows, n = h.shape
+    if bits is None:
+        bits, asym = FORMATS[fmt]
+    code = np.empty((rows, n), np.int32)
+    s = np.empty(rows, np.float32)
+    z = np.empty(rows, np.float32)
+    v = np.empty((rows, n), np.float32) if with_v else None
+    lib().orc_quantize_rows(rows, n, bits, asym, _f(h), _i(code), _f(s), _f(z), _f(v))
+    return (code, s, z, v) if with_v else (code, s, z)
+
+
+def dequantize_rows(code, s, z) -> np.ndarray:
+    code = np.ascontiguousarray(code, np.int32)
+    rows, n = code.shape
+    out = np.empty((rows, n), np.float32)
+    lib().orc_dequantize_rows(rows, n, _i(code), _f(_c32(s)), _f(_c32(z)), _f(out))
+    return out
+
+
+def make_state(fmt: str, rows: int, n: int, init: np.ndarray | None = None) -> State:
+    """A state of ``rows`` rows of ``n`` entries: zero, or ``init`` [rows][n] quantized."""
+    if fmt == "fp32":
+        h = np.zeros((rows, n), np.float32) if init is None else _c32(init).reshape(rows, n).copy()
+        return State(fmt, rows, n, h=h)
+    if init is None:
+        return State(fmt, rows, n, code=np.zeros((rows, n), np.int32),
+                     scale=np.zeros(rows, np.float32), zero=np.zeros(rows, np.float32))
+    code, s, z = quantize_rows(_c32(init).reshape(rows, n), fmt)
+    return State(fmt, rows, n, code=code, scale=s, zero=z)
+
+
+def decay(dt: float, A: float) -> float:
+    return lib().orc_decay(ctypes.c_float(dt), ctypes.c_float(A))
+
+
+def _ro(readout: str) -> int:
+    if readout not in ("post", "pre"):
+        raise ValueError("readout must be 'post' or 'pre'")
+    return 1 if readout == "pre" else 0
+
+
+def mamba2_step(st: State, x, dt, A, Bm, Cm, D, readout: str = "post", diag: bool = False):
+    """One decode token of one layer.  ``x`` [B][H][P], ``dt`` [B][H], ``A``/``D`` [H],
+    ``Bm``/``Cm`` [B][G][N]; updates ``st`` in place and returns ``y`` [B][H][P]
+    (plus the pre-rounding row and the rounded fp32 values when ``diag``)."""
+    x, dt, A, Bm, Cm, D = map(_c32, (x, dt, A, Bm, Cm, D))
+    Bsz, H, P = x.shape
+    G, N = Bm.shape[1], Bm.shape[2]
+    assert st.rows == Bsz * H * P and st.n == N
+    y = np.empty((Bsz, H, P), np.float32)
+    hpre = np.empty((st.rows, N), np.float32) if diag else None
+    vq = np.empty((st.rows, N), np.float32) if diag and st.fmt != "fp32" else None
+    rc = lib().orc_mamba2_step(Bsz, H, G, P, N, st.bits, st.asym, _i(st.code), _f(st.scale),
+                               _f(st.zero), _f(st.h), _f(x), _f(dt), _f(A), _f(Bm), _f(Cm), _f(D),
+                               _f(y), _ro(readout), _f(hpre), _f(vq))
+    assert rc == 0
+    return (y, hpre, vq) if diag else y
+
+
+def mamba2_scan(st: State, x, dt, A, Bm, Cm, D, readout: str = "post"):
+    """``T`` tokens, the state rounded after each.  ``x`` [B][T][H][P], ``dt`` [B][T][H],
+    ``Bm``/``Cm`` [B][T][G][N]; returns ``y`` [B][T][H][P]."""
+    x, dt, A, Bm, Cm, D = map(_c32, (x, dt, A, Bm, Cm, D))
+    Bsz, T, H, P = x.shape
+    G, N = Bm.shape[2], Bm.shape[3]
+    assert st.rows == Bsz * H * P and st.n == N
+    y = np.empty((Bsz, T, H, P), np.float32)
+    rc = lib().orc_mamba2_scan(Bsz, T, H, G, P, N, st.bits, st.asym, _i(st.code), _f(st.scale),
+                               _f(st.zero), _f(st.h), _f(x), _f(dt), _f(A), _f(Bm), _f(Cm), _f(D),
+                               _f(y), _ro(readout))
+    assert rc == 0
+    return y
+
+
+def mamba2_rows_scan(st: State, x, dt, A, Bm, Cm, D, readout: str = "post"):
+    """``T`` tokens for independent rows with per-row inputs: ``x``/``dt`` [R][T], ``A``/``D`` [R],
+    ``Bm``/``Cm`` [R][T][N]; returns ``y`` [R][T]."""
+    x, dt, A, Bm, Cm, D = map(_c32, (x, dt, A, Bm, Cm, D))
+    R, T = x.shape
+    N = Bm.shape[2]
+    assert st.rows == R and st.n == N
+    y = np.empty((R, T), np.float32)
+    rc = lib().orc_mamba2_rows_scan(R, T, N, st.bits, st.asym, _i(st.code), _f(st.scale),
+                                    _f(st.zero), _f(st.h), _f(x), _f(dt), _f(A), _f(Bm), _f(Cm),
+                                    _f(D), _f(y), _ro(readout))
+    assert rc == 0
+    return y
+
+
+def delta_step(st: State, q, k, v, alpha, beta, Bsz: int, H: int, readout: str = "post",
+               diag: bool = False):
+    """One delta-rule step for ``Bsz*H`` matrices of ``dk`` rows by ``dv``: ``q``/``k`` [B][H][dk],
+    ``v`` [B][H][dv], ``alpha``/``beta`` [B][H]; returns ``o`` [B][H][dv]."""
+    q, k, v, alpha, beta = map(_c32, (q, k, v, alpha, beta))
+    dk, dv = k.shape[-1], v.shape[-1]
+    assert st.rows == Bsz * H * dk and st.n == dv
+    o = np.empty((Bsz, H, dv), np.float32)
+    Spre = np.empty((st.rows, dv), np.float32) if diag else None
+    vq = np.empty((st.rows, dv), np.float32) if diag and st.fmt != "fp32" else None
+    rc = lib().orc_delta_step(Bsz, H, dk, dv, st.bits, st.asym, _i(st.code), _f(st.scale),
+                              _f(st.zero), _f(st.h), _f(q), _f(k), _f(v), _f(alpha), _f(beta),
+                              _f(o), _ro(readout), _f(Spre), _f(vq))
+    assert rc == 0
+    return (o, Spre, vq) if diag else o

@@ -1,0 +1,477 @@
+/*
+ * ssq_oracle.c -- the CPU oracle for the quantized recurrent-state update.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file: only the tests, the smoke check and the bench's CPU
+ * baseline do.  It shares no code, header, table or constant with the GPU
+ * library; it is plain, single-threaded C built with -ffp-contract=off, so
+ * that every fp32 operation below is exactly one IEEE rounding and fmaf()
+ * appears only where the evaluation order says "fused".
+ *
+ * What it computes (sources are the pages on recurrent-state quantization):
+ *
+ *  Mamba-2 layer, per row (sequence b, head h, head-dim p) of N state
+ *  entries -- "ssm-state-quantization" README, Setup:
+ *    lambda = exp(dt*A)                          decay of the head
+ *    h'_n   = lambda*h_n + dt*x*B_n              write of the token
+ *    y      = sum_n C_n*r_n + D*x                readout, r = the state after
+ *                                                quantization (the README reads
+ *                                                the output from the quantized
+ *                                                state) or, as an option, before
+ *  The row is then refit and rounded to nearest (Setup, quantizer bullets):
+ *    symmetric  grid [-amax, amax], step amax/(2^(b-1)-1), codes in
+ *               [-(2^(b-1)-1), 2^(b-1)-1]
+ *    asymmetric grid [min, max], step (max-min)/(2^b-1), integer zero point,
+ *               codes in [0, 2^b-1]
+ *  refit every step from the new fp32 row.
+ *
+ *  Delta rule (GDN/KDA-style), one dk x dv matrix S per (sequence, head) --
+ *  "Mamba state quantization for inference", sections "Mamba state
+ *  quantization changes persistent state" and "Quantization error returns on
+ *  the next token": decay plus a delta-rule correction write the next state,
+ *    S' = alpha*(I - beta*k*k^T)*S + beta*k*v^T,   o = S'^T q,
+ *  each key channel i (a row of S over the value dimension) quantized like a
+ *  Mamba-2 row.
+ *
+ * Fixed fp32 evaluation order (the pages give the formulas, not the rounding
+ * order; fl() is one fp32 rounding):
+ *    lambda = fl32(exp_double(fl(dt*A)))          exp taken in double
+ *    w      = fl(dt*x)
+ *    quantized row (scale s, zero z, codes c):
+ *      d_n  = fl(c_n - z)                         exact for |z| < 2^24
+ *      h'_n = fma(fl(lambda*s), d_n, fl(w*B_n))   decay acts on the row's scale
+ *    fp32 row:  h'_n = fma(lambda, h_n, fl(w*B_n))
+ *    refit, asymmetric: mn, mx = min/max h'; s' = fl(fl(mx-mn)/(2^b-1));
+ *      inv = fl(1/s'); z' = -rne(fl(mn*inv));
+ *      c'_n = clamp(rne(fl(h'_n*inv) + z'), 0, 2^b-1), the sum exact and the
+ *      tie going to the even code
+ *    refit, symmetric: s' = fl(amax/(2^(b-1)-1)); inv = fl(1/s');
+ *      c'_n = clamp(rne(fl(h'_n*inv)), -(2^(b-1)-1), 2^(b-1)-1)
+ *    degenerate rows: if s' is zero or subnormal the row carries no usable
+ *      step.  Asymmetric rows are then stored as the constant mn (s' = |mn|,
+ *      z' = -sign(mn), all codes 0, which dequantizes to mn exactly);
+ *      symmetric rows are stored as zero (s' = 0, codes 0).
+ *    dequantized value: fl(s*fl(c - z)).
+ *    Readouts (y, o) are output only: they are accumulated here in double and
+ *    rounded once, so they are the most accurate value any order can give.
+ *    Delta rule: u_j = RN32(sum_i k_i*S_ij) with the products and the sum
+ *      taken in double (for a quantized S, S_ij = s_i*(c_ij - z_i) as a real
+ *      number); w_j = fl(beta*fl(v_j - fl(alpha*u_j)));
+ *      S'_ij = fma(fl(alpha*s_i), d_ij, fl(k_i*w_j)) (quantized) or
+ *      fma(alpha, S_ij, fl(k_i*w_j)) (fp32).
+ */
+#include <float.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#if defined(__FAST_MATH__)
+#error "the oracle must be built without -ffast-math"
+#endif
+
+/* ------------------------------------------------------------------------ */
+/* decay                                                                    */
+/* ------------------------------------------------------------------------ */
+
+float orc_decay(float dt, float A)
+{
+    float e = dt * A; /* fl(dt*A) */
+    return (float)exp((double)e);
+}
+
+/* ------------------------------------------------------------------------ */
+/* one row: refit and round to nearest                                       */
+/* ------------------------------------------------------------------------ */
+
+static float sign_of(float c)
+{
+    if (c > 0.0f)
+        return 1.0f;
+    if (c < 0.0f)
+        return -1.0f;
+    return 0.0f;
+}
+
+/* Quantize the n entries of h with a b-bit grid (bits in 2..8).  Writes the
+ * integer codes, the scale and the zero point (0 for the symmetric grid).
+ * v_out, if not NULL, receives fl(h_n*inv): the fp32 value that is rounded. */
+void orc_quantize_row(const float *h, int n, int bits, int asym, int32_t *code, float *s_out,
+                      float *z_out, float *v_out)
+{
+    int i;
+    if (asym) {
+        const float cmax = (float)((1 << bits) - 1);
+        float mn = h[0], mx = h[0];
+        for (i = 1; i < n; ++i) {
+            if (h[i] < mn)
+                mn = h[i];
+            if (h[i] > mx)
+                mx = h[i];
+        }
+        float range = mx - mn;
+        float s = range / cmax;
+        if (!(s >= FLT_MIN)) {
+            *s_out = fabsf(mn);
+            *z_out = -sign_of(mn);
+            for (i = 0; i < n; ++i) {
+                code[i] = 0;
+                if (v_out)
+                    v_out[i] = 0.0f;
+            }
+            return;
+        }
+        float inv = 1.0f / s;
+        float vmin = mn * inv;
+        float z = -nearbyintf(vmin);
+        for (i = 0; i < n; ++i) {
+            float v = h[i] * inv;
+            /* v + z is exact in double: v has 24 significant bits and z is an integer */
+            double t = nearbyint((double)v + (double)z);
+            if (t < 0.0)
+                t = 0.0;
+            if (t > (double)cmax)
+                t = (double)cmax;
+            code[i] = (int32_t)t;
+            if (v_out)
+                v_out[i] = v;
+        }
+        *s_out = s;
+        *z_out = z;
+    } else {
+        const float cmax = (float)((1 << (bits - 1)) - 1);
+        float amax = 0.0f;
+        for (i = 0; i < n; ++i) {
+            float a = fabsf(h[i]);
+            if (a > amax)
+                amax = a;
+        }
+        float s = amax / cmax;
+        if (!(s >= FLT_MIN)) {
+            *s_out = 0.0f;
+            *z_out = 0.0f;
+            for (i = 0; i < n; ++i) {
+                code[i] = 0;
+                if (v_out)
+                    v_out[i] = 0.0f;
+            }
+            return;
+        }
+        float inv = 1.0f / s;
+        for (i = 0; i < n; ++i) {
+            float v = h[i] * inv;
+            double t = nearbyint((double)v);
+            if (t < -(double)cmax)
+                t = -(double)cmax;
+            if (t > (double)cmax)
+                t = (double)cmax;
+            code[i] = (int32_t)t;
+            if (v_out)
+                v_out[i] = v;
+        }
+        *s_out = s;
+        *z_out = 0.0f;
+    }
+}
+
+void orc_dequantize_row(const int32_t *code, int n, float s, float z, float *out)
+{
+    int i;
+    for (i = 0; i < n; ++i) {
+        float d = (float)code[i] - z;
+        out[i] = s * d;
+    }
+}
+
+void orc_quantize_rows(int64_t rows, int n, int bits, int asym, const float *h, int32_t *code,
+                       float *s, float *z, float *v_out)
+{
+    int64_t r;
+    for (r = 0; r < rows; ++r)
+        orc_quantize_row(h + r * n, n, bits, asym, code + r * n, s + r, z + r,
+                         v_out ? v_out + r * n : NULL);
+}
+
+void orc_dequantize_rows(int64_t rows, int n, const int32_t *code, const float *s, const float *z,
+                         float *out)
+{
+    int64_t r;
+    for (r = 0; r < rows; ++r)
+        orc_dequantize_row(code + r * n, n, s[r], z[r], out + r * n);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Mamba-2: one token for one row                                            */
+/* ------------------------------------------------------------------------ */
+
+/* bits == 0: fp32 state in h (code/s/z unused).  Otherwise the row's codes,
+ * scale and zero point are read and replaced.  hpre (optional) receives the
+ * new row before rounding, vq (optional) the fp32 values that were rounded.
+ * Returns y. */
+static float mamba2_row_step(int N, int bits, int asym, int32_t *code, float *s, float *z,
+                             float *h, float x, float dt, float A, const float *Bn,
+                             const float *Cn, float D, int readout_pre, float *hpre, float *vq,
+                             float *work)
+{
+    int n;
+    float lam = orc_decay(dt, A);
+    float w = dt * x;
+    float dx = D * x;
+    double acc = 0.0;
+
+    if (bits == 0) {
+        for (n = 0; n < N; ++n) {
+            float wb = w * Bn[n];
+            h[n] = fmaf(lam, h[n], wb);
+            if (hpre)
+                hpre[n] = h[n];
+            acc += (double)Cn[n] * (double)h[n];
+        }
+        return (float)(acc + (double)dx);
+    }
+
+    {
+        float ls = lam * (*s);
+        float zo = *z;
+        for (n = 0; n < N; ++n) {
+            float d = (float)code[n] - zo;
+            float wb = w * Bn[n];
+            work[n] = fmaf(ls, d, wb);
+            if (hpre)
+                hpre[n] = work[n];
+        }
+    }
+    if (readout_pre) {
+        for (n = 0; n < N; ++n)
+            acc += (double)Cn[n] * (double)work[n];
+    }
+    orc_quantize_row(work, N, bits, asym, code, s, z, vq);
+    if (!readout_pre) {
+        orc_dequantize_row(code, N, *s, *z, work);
+        for (n = 0; n < N; ++n)
+            acc += (double)Cn[n] * (double)work[n];
+    }
+    return (float)(acc + (double)dx);
+}
+
+/* One decode step of one layer.
+ *   code [Bsz][H][P][N] int32, s, z [Bsz][H][P]   (quantized formats)
+ *   h    [Bsz][H][P][N] fp32                       (bits == 0)
+ *   x [Bsz][H][P], dt [Bsz][H], A [H], Bm/Cm [Bsz][G][N], D [H], y [Bsz][H][P]
+ *   hpre, vq: optional [Bsz][H][P][N] diagnostics.
+ * Returns 0, or -1 on bad sizes. */
+int orc_mamba2_step(int Bsz, int H, int G, int P, int N, int bits, int asym, int32_t *code,
+                    float *s, float *z, float *h, const float *x, const float *dt, const float *A,
+                    const float *Bm, const float *Cm, const float *D, float *y, int readout_pre,
+                    float *hpre, float *vq)
+{
+    int b, hh, p;
+    float *work;
+    if (Bsz <= 0 || H <= 0 || G <= 0 || P <= 0 || N <= 0 || H % G != 0)
+        return -1;
+    work = (float *)malloc(sizeof(float) * (size_t)N);
+    if (!work)
+        return -1;
+    for (b = 0; b < Bsz; ++b)
+        for (hh = 0; hh < H; ++hh) {
+            int g = hh / (H / G);
+            const float *Bn = Bm + ((int64_t)b * G + g) * N;
+            const float *Cn = Cm + ((int64_t)b * G + g) * N;
+            float dtv = dt[(int64_t)b * H + hh];
+            for (p = 0; p < P; ++p) {
+                int64_t r = ((int64_t)b * H + hh) * P + p;
+                y[r] = mamba2_row_step(N, bits, asym, code ? code + r * N : NULL, s ? s + r : NULL,
+                                       z ? z + r : NULL, h ? h + r * N : NULL, x[r], dtv, A[hh],
+                                       Bn, Cn, D[hh], readout_pre, hpre ? hpre + r * N : NULL,
+                                       vq ? vq + r * N : NULL, work);
+            }
+        }
+    free(work);
+    return 0;
+}
+
+/* T tokens of one layer, the state rounded after every token: plain repetition
+ * of orc_mamba2_step on token-t slices.
+ *   x [Bsz][T][H][P], dt [Bsz][T][H], Bm/Cm [Bsz][T][G][N], y [Bsz][T][H][P] */
+int orc_mamba2_scan(int Bsz, int T, int H, int G, int P, int N, int bits, int asym, int32_t *code,
+                    float *s, float *z, float *h, const float *x, const float *dt, const float *A,
+                    const float *Bm, const float *Cm, const float *D, float *y, int readout_pre)
+{
+    int t, b;
+    int rc = 0;
+    size_t nx = (size_t)Bsz * H * P, ndt = (size_t)Bsz * H, nbc = (size_t)Bsz * G * N;
+    float *xs, *dts, *Bs, *Cs, *ys;
+    if (T <= 0)
+        return -1;
+    xs = (float *)malloc(sizeof(float) * nx);
+    ys = (float *)malloc(sizeof(float) * nx);
+    dts = (float *)malloc(sizeof(float) * ndt);
+    Bs = (float *)malloc(sizeof(float) * nbc);
+    Cs = (float *)malloc(sizeof(float) * nbc);
+    if (!xs || !ys || !dts || !Bs || !Cs) {
+        rc = -1;
+        goto done;
+    }
+    for (t = 0; t < T; ++t) {
+        for (b = 0; b < Bsz; ++b) {
+            memcpy(xs + (size_t)b * H * P, x + ((size_t)b * T + t) * H * P, sizeof(float) * H * P);
+            memcpy(dts + (size_t)b * H, dt + ((size_t)b * T + t) * H, sizeof(float) * H);
+            memcpy(Bs + (size_t)b * G * N, Bm + ((size_t)b * T + t) * G * N, sizeof(float) * G * N);
+            memcpy(Cs + (size_t)b * G * N, Cm + ((size_t)b * T + t) * G * N, sizeof(float) * G * N);
+        }
+        rc = orc_mamba2_step(Bsz, H, G, P, N, bits, asym, code, s, z, h, xs, dts, A, Bs, Cs, D, ys,
+                             readout_pre, NULL, NULL);
+        if (rc)
+            goto done;
+        for (b = 0; b < Bsz; ++b)
+            memcpy(y + ((size_t)b * T + t) * H * P, ys + (size_t)b * H * P, sizeof(float) * H * P);
+    }
+done:
+    free(xs);
+    free(ys);
+    free(dts);
+    free(Bs);
+    free(Cs);
+    return rc;
+}
+
+/* T tokens for R independent rows, each with its own inputs (for checking
+ * sampled rows of a large state):
+ *   code/h [R][N], s/z [R], x/dt/y [R][T], A/D [R], Bm/Cm [R][T][N] */
+int orc_mamba2_rows_scan(int64_t R, int T, int N, int bits, int asym, int32_t *code, float *s,
+                         float *z, float *h, const float *x, const float *dt, const float *A,
+                         const float *Bm, const float *Cm, const float *D, float *y,
+                         int readout_pre)
+{
+    int64_t r;
+    int t;
+    float *work = (float *)malloc(sizeof(float) * (size_t)N);
+    if (!work)
+        return -1;
+    for (r = 0; r < R; ++r)
+        for (t = 0; t < T; ++t) {
+            int64_t rt = r * T + t;
+            y[rt] = mamba2_row_step(N, bits, asym, code ? code + r * N : NULL, s ? s + r : NULL,
+                                    z ? z + r : NULL, h ? h + r * N : NULL, x[rt], dt[rt], A[r],
+                                    Bm + rt * N, Cm + rt * N, D[r], readout_pre, NULL, NULL, work);
+        }
+    free(work);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* delta rule: one step of one (sequence, head) matrix                       */
+/* ------------------------------------------------------------------------ */
+
+/* code [dk][dv], s/z [dk] (quantized) or S [dk][dv] fp32 (bits == 0); q, k [dk];
+ * v [dv]; o [dv].  Spre, vq: optional [dk][dv] diagnostics. */
+static int delta_matrix_step(int dk, int dv, int bits, int asym, int32_t *code, float *s, float *z,
+                             float *S, const float *q, const float *k, const float *v, float alpha,
+                             float beta, float *o, int readout_pre, float *Spre, float *vq)
+{
+    int i, j;
+    float *u = (float *)malloc(sizeof(float) * (size_t)dv);
+    float *w = (float *)malloc(sizeof(float) * (size_t)dv);
+    float *Sn = (float *)malloc(sizeof(float) * (size_t)dk * dv);
+    double *acc = (double *)malloc(sizeof(double) * (size_t)dv);
+    if (!u || !w || !Sn || !acc) {
+        free(u);
+        free(w);
+        free(Sn);
+        free(acc);
+        return -1;
+    }
+
+    /* u = k^T S (the state before the step) */
+    for (j = 0; j < dv; ++j) {
+        double a = 0.0;
+        for (i = 0; i < dk; ++i) {
+            if (bits == 0) {
+                a += (double)k[i] * (double)S[(int64_t)i * dv + j];
+            } else {
+                float d = (float)code[(int64_t)i * dv + j] - z[i];
+                a += ((double)k[i] * (double)s[i]) * (double)d;
+            }
+        }
+        u[j] = (float)a;
+    }
+    /* w = beta*(v - alpha*u) */
+    for (j = 0; j < dv; ++j) {
+        float au = alpha * u[j];
+        float vm = v[j] - au;
+        w[j] = beta * vm;
+    }
+    /* S' = alpha*S + k w^T */
+    for (i = 0; i < dk; ++i) {
+        if (bits == 0) {
+            for (j = 0; j < dv; ++j) {
+                float kw = k[i] * w[j];
+                Sn[(int64_t)i * dv + j] = fmaf(alpha, S[(int64_t)i * dv + j], kw);
+            }
+        } else {
+            float as = alpha * s[i];
+            for (j = 0; j < dv; ++j) {
+                float d = (float)code[(int64_t)i * dv + j] - z[i];
+                float kw = k[i] * w[j];
+                Sn[(int64_t)i * dv + j] = fmaf(as, d, kw);
+            }
+        }
+    }
+    if (Spre)
+        memcpy(Spre, Sn, sizeof(float) * (size_t)dk * dv);
+
+    for (j = 0; j < dv; ++j)
+        acc[j] = 0.0;
+    if (bits == 0 || readout_pre) {
+        for (i = 0; i < dk; ++i)
+            for (j = 0; j < dv; ++j)
+                acc[j] += (double)q[i] * (double)Sn[(int64_t)i * dv + j];
+    }
+    if (bits == 0) {
+        memcpy(S, Sn, sizeof(float) * (size_t)dk * dv);
+    } else {
+        for (i = 0; i < dk; ++i)
+            orc_quantize_row(Sn + (int64_t)i * dv, dv, bits, asym, code + (int64_t)i * dv, s + i,
+                             z + i, vq ? vq + (int64_t)i * dv : NULL);
+        if (!readout_pre) {
+            for (i = 0; i < dk; ++i) {
+                orc_dequantize_row(code + (int64_t)i * dv, dv, s[i], z[i], Sn + (int64_t)i * dv);
+                for (j = 0; j < dv; ++j)
+                    acc[j] += (double)q[i] * (double)Sn[(int64_t)i * dv + j];
+            }
+        }
+    }
+    for (j = 0; j < dv; ++j)
+        o[j] = (float)acc[j];
+
+    free(u);
+    free(w);
+    free(Sn);
+    free(acc);
+    return 0;
+}
+
+/* One delta-rule step of one layer.
+ *   code [Bsz][H][dk][dv], s/z [Bsz][H][dk] or S [Bsz][H][dk][dv]
+ *   q, k [Bsz][H][dk], v [Bsz][H][dv], alpha/beta [Bsz][H], o [Bsz][H][dv]
+ *   Spre, vq: optional [Bsz][H][dk][dv] */
+int orc_delta_step(int Bsz, int H, int dk, int dv, int bits, int asym, int32_t *code, float *s,
+                   float *z, float *S, const float *q, const float *k, const float *v,
+                   const float *alpha, const float *beta, float *o, int readout_pre, float *Spre,
+                   float *vq)
+{
+    int64_t m, nm = (int64_t)Bsz * H;
+    if (Bsz <= 0 || H <= 0 || dk <= 0 || dv <= 0)
+        return -1;
+    for (m = 0; m < nm; ++m) {
+        int64_t mat = m * dk * dv;
+        int rc = delta_matrix_step(dk, dv, bits, asym, code ? code + mat : NULL,
+                                   s ? s + m * dk : NULL, z ? z + m * dk : NULL,
+                                   S ? S + mat : NULL, q + m * dk, k + m * dk, v + m * dv,
+                                   alpha[m], beta[m], o + m * dv, readout_pre,
+                                   Spre ? Spre + mat : NULL, vq ? vq + mat : NULL);
+        if (rc)
+            return rc;
+    }
+    return 0;
+}

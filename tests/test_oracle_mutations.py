@@ -1,0 +1,108 @@
+"""The oracle's pins are sensitive: each planted mistake makes at least one pin fail.
+
+Every case copies ``oracle/ssq_oracle.c``, plants one plausible mistake in the
+copy (a dropped term, a wrong sign, a wrong index, an off-by-one grid, a
+swapped readout ...), builds it with gcc into a temporary directory, points
+the oracle binding at it and runs every test of ``test_oracle_pins``.  The
+case passes only if some pin fails.  Nothing here touches a GPU.
+"""
+import inspect
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from tests import test_oracle_pins as pins
+
+SRC = open(os.path.join(os.path.dirname(oracle.__file__), "ssq_oracle.c")).read()
+
+# (name, text in ssq_oracle.c, replacement); the text must occur exactly `count` times
+MUTATIONS = [
+    ("fp32 write term dropped", "            float wb = w * Bn[n];\n            h[n] = fmaf(lam, h[n], wb);",
+     "            float wb = 0.0f * Bn[n];\n            h[n] = fmaf(lam, h[n], wb);"),
+    ("quantized write term dropped", "            float wb = w * Bn[n];\n            work[n]",
+     "            float wb = 0.0f * Bn[n];\n            work[n]"),
+    ("zero point added instead of subtracted", "float d = (float)code[n] - zo;", "float d = (float)code[n] + zo;"),
+    ("zero point sign flipped", "float z = -nearbyintf(vmin);", "float z = nearbyintf(vmin);"),
+    ("zero point from the max", "float vmin = mn * inv;", "float vmin = mx * inv;"),
+    ("symmetric grid off by one", "const float cmax = (float)((1 << (bits - 1)) - 1);",
+     "const float cmax = (float)((1 << (bits - 1)));"),
+    ("asymmetric grid off by one", "const float cmax = (float)((1 << bits) - 1);",
+     "const float cmax = (float)((1 << bits));"),
+    ("Euler decay instead of exp", "return (float)exp((double)e);", "return (float)(1.0 + (double)e);"),
+    ("decay applied twice", "float ls = lam * (*s);", "float ls = lam * lam * (*s);"),
+    ("readouts swapped", "    if (readout_pre) {\n        for (n = 0; n < N; ++n)",
+     "    if (!readout_pre) {\n        for (n = 0; n < N; ++n)"),
+    ("D*x dropped", "float dx = D * x;", "float dx = 0.0f * x;"),
+    ("ties away from zero", "double t = nearbyint((double)v + (double)z);",
+     "double t = round((double)v + (double)z);"),
+    ("top clamp missing", "            if (t > (double)cmax)\n                t = (double)cmax;\n            code[i] = (int32_t)t;\n            if (v_out)\n                v_out[i] = v;\n        }\n        *s_out = s;\n        *z_out = z;",
+     "            code[i] = (int32_t)t;\n            if (v_out)\n                v_out[i] = v;\n        }\n        *s_out = s;\n        *z_out = z;"),
+    ("scan reads token 0 every step", "memcpy(xs + (size_t)b * H * P, x + ((size_t)b * T + t) * H * P",
+     "memcpy(xs + (size_t)b * H * P, x + ((size_t)b * T + 0) * H * P"),
+    ("group index wrong", "int g = hh / (H / G);", "int g = hh % G;"),
+    ("delta correction sign", "float vm = v[j] - au;", "float vm = v[j] + au;"),
+    ("delta decay not applied to the state", "float as = alpha * s[i];", "float as = s[i];"),
+    ("delta readout with k instead of q",
+     "                for (j = 0; j < dv; ++j)\n                    acc[j] += (double)q[i] * (double)Sn[(int64_t)i * dv + j];\n            }\n        }",
+     "                for (j = 0; j < dv; ++j)\n                    acc[j] += (double)k[i] * (double)Sn[(int64_t)i * dv + j];\n            }\n        }"),
+    ("delta u uses the wrong key index", "a += (double)k[i] * (double)S[(int64_t)i * dv + j];",
+     "a += (double)k[j % dk] * (double)S[(int64_t)i * dv + j];"),
+    ("dequantization scale dropped", "        out[i] = s * d;", "        out[i] = d;"),
+]
+
+
+def _pin_cases():
+    cases = []
+    for name, fn in inspect.getmembers(pins, inspect.isfunction):
+        if not name.startswith("test_"):
+            continue
+        marks = getattr(fn, "pytestmark", [])
+        grids = [m.args for m in marks if m.name == "parametrize"]
+        combos = [dict()]
+        for argnames, values in grids:
+            names = [a.strip() for a in argnames.split(",")]
+            new = []
+            for c in combos:
+                for v in values:
+                    vv = v if len(names) > 1 else (v,)
+                    new.append({**c, **dict(zip(names, vv))})
+            combos = new
+        for c in combos:
+            cases.append((name, fn, c))
+    return cases
+
+
+def _failing_pins(lib_path):
+    saved = oracle._lib
+    oracle._lib = oracle.bind(lib_path)
+    failed = []
+    try:
+        for name, fn, kw in _pin_cases():
+            try:
+                fn(**kw)
+            except (AssertionError, ValueError, FloatingPointError, IndexError):
+                failed.append(name)
+    finally:
+        oracle._lib = saved
+    return failed
+
+
+def test_unmutated_copy_passes_every_pin(tmp_path):
+    path = tmp_path / "liboracle_copy.so"
+    src = tmp_path / "copy.c"
+    src.write_text(SRC)
+    subprocess.check_call(["gcc", *oracle.CFLAGS, str(src), "-o", str(path), "-lm"])
+    assert _failing_pins(str(path)) == []
+
+
+@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(tmp_path, name, old, new):
+    assert SRC.count(old) == 1, f"mutation site for '{name}' not unique"
+    src = tmp_path / "mut.c"
+    src.write_text(SRC.replace(old, new))
+    path = tmp_path / "liboracle_mut.so"
+    subprocess.check_call(["gcc", *oracle.CFLAGS, str(src), "-o", str(path), "-lm"])
+    failed = _failing_pins(str(path))
+    assert failed, f"no pin caught: {name}"
