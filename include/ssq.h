@@ -1,0 +1,201 @@
+/*
+ * ssq.h -- quantized recurrent-state update on MI355X (gfx950): C ABI.
+ *
+ * A recurrent layer keeps one fixed-size state per live sequence and, for
+ * every generated token, reads it, applies the recurrence, requantizes it and
+ * writes it back ("Mamba state quantization for inference": "Recurrent state
+ * is fixed per request, not free"; the DAMP paragraph of "Mamba state
+ * quantization changes persistent state").  This library stores that state
+ * quantized per row and updates it in place with hand-written HIP kernels.
+ *
+ * Two state kinds:
+ *  - SSQ_MAMBA2: the Mamba-2 selective-SSM state, [batch][nheads][P][N] with
+ *    head dimension P and state size N.  A row is (sequence, head, p) over the
+ *    N state entries ("ssm-state-quantization" README, Setup: one scale per
+ *    row, i.e. per head and head_dim, over the 128 state entries).
+ *  - SSQ_DELTA: the delta-rule (Gated DeltaNet / Kimi Delta Attention style)
+ *    matrix state, one dk x dv matrix per (sequence, head) ("Mamba state
+ *    quantization for inference", "Mamba state quantization changes
+ *    persistent state").  A row is one key channel over the value dimension.
+ *
+ * Formats: fp32 (unquantized control), and symmetric or asymmetric per-row
+ * grids at 8 or 4 bits, refit at every step (README, Setup: symmetric grid
+ * [-amax, amax] with step amax/(2^(b-1)-1); asymmetric grid [min, max] with an
+ * integer zero point and step (max-min)/(2^b-1); Findings 1: round to
+ * nearest at 8 and 4 bits).
+ *
+ * Fixed fp32 evaluation order of one row (fl() = one fp32 rounding; results
+ * are bit-reproducible and independent of the launch configuration):
+ *   lambda = fl32(exp(fl(dt*A)))  (exp evaluated in double, rounded once)
+ *   w      = fl(dt*x)
+ *   h'_n   = fma(fl(lambda*s), fl(c_n - z), fl(w*B_n))   (quantized state)
+ *   h'_n   = fma(lambda, h_n, fl(w*B_n))                  (fp32 state)
+ *   asymmetric refit: s' = fl(fl(max-min)/(2^b-1)), inv = fl(1/s'),
+ *     z' = -rne(fl(min*inv)), c'_n = clamp(rne(fl(h'_n*inv) + z'), 0, 2^b-1)
+ *     with the sum exact and ties to the even code
+ *   symmetric refit: s' = fl(amax/(2^(b-1)-1)), inv = fl(1/s'),
+ *     c'_n = clamp(rne(fl(h'_n*inv)), -(2^(b-1)-1), 2^(b-1)-1)
+ *   a zero or subnormal s' marks a degenerate row: asymmetric rows become the
+ *     constant min (s' = |min|, z' = -sign(min), codes 0), symmetric rows zero
+ *   y = sum_n C_n*r_n + D*x, r = the dequantized new row s'*(c'-z')
+ *     (default: the README reads the output from the quantized state) or the
+ *     new row before rounding (SSQ_READ_PRE_QUANT); y and the delta-rule
+ *     output o are outputs only, their summation order is unspecified.
+ *
+ * Conventions for every call:
+ *  - Pointers named as device pointers must be device memory of the current
+ *    HIP device, fp32, contiguous, row-major in the shapes given, and 16-byte
+ *    aligned.  The caller owns every input and output buffer.
+ *  - Calls only enqueue work on `stream` (a hipStream_t passed as void*;
+ *    NULL is the null stream) and return without synchronizing.  Inputs must
+ *    stay valid until the stream has passed the call.  Calls on one state
+ *    must be ordered on one stream by the caller; distinct states are
+ *    independent.
+ *  - Every argument is validated before anything is enqueued; a rejected
+ *    call returns a non-zero status, changes nothing and leaves a detail
+ *    message for ssq_last_error().  Non-finite inputs are not checked: the
+ *    codes they produce are unspecified.
+ *  - Kernels support row_len == 128, and rows_per_head a multiple of 16 for
+ *    SSQ_MAMBA2, dk == 128 for SSQ_DELTA.
+ */
+#ifndef SSQ_H
+#define SSQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SSQ_OK = 0,
+    SSQ_ERR_INVALID_ARG = 1,   /* null pointer, non-positive size, bad alignment, ngroups not dividing nheads, T <= 0 */
+    SSQ_ERR_UNSUPPORTED = 2,   /* a size or format the kernels are not built for */
+    SSQ_ERR_KIND_MISMATCH = 3, /* a Mamba-2 call on a delta state or the reverse */
+    SSQ_ERR_ALLOC = 4,         /* device allocation failed */
+    SSQ_ERR_DEVICE = 5         /* the HIP runtime reported an error */
+} ssq_status;
+
+typedef enum {
+    SSQ_FP32 = 0,
+    SSQ_INT8_SYM = 1,  /* int8_t codes in [-127, 127], fp32 scale */
+    SSQ_INT8_ASYM = 2, /* uint8_t codes in [0, 255], fp32 scale and integer-valued fp32 zero point */
+    SSQ_INT4_SYM = 3,  /* 4-bit two's complement codes in [-7, 7], two per byte, fp32 scale */
+    SSQ_INT4_ASYM = 4  /* 4-bit codes in [0, 15], two per byte, fp32 scale and zero point */
+} ssq_format;
+
+typedef enum { SSQ_MAMBA2 = 0, SSQ_DELTA = 1 } ssq_kind;
+
+typedef enum { SSQ_READ_POST_QUANT = 0, SSQ_READ_PRE_QUANT = 1 } ssq_readout;
+
+/* Shape and format of one layer's state for all sequences of a batch. */
+typedef struct {
+    int32_t kind;          /* ssq_kind */
+    int32_t format;        /* ssq_format */
+    int32_t batch;         /* sequences */
+    int32_t nheads;        /* heads */
+    int32_t ngroups;       /* SSQ_MAMBA2: B/C groups, each shared by nheads/ngroups heads; SSQ_DELTA: 1 */
+    int32_t rows_per_head; /* SSQ_MAMBA2: head dimension P; SSQ_DELTA: key dimension dk */
+    int32_t row_len;       /* SSQ_MAMBA2: state size N; SSQ_DELTA: value dimension dv */
+} ssq_desc;
+
+/* Byte layout of a state in its storage (public, so that checkpoints and
+ * tests can read it):
+ *   codes  at codes_offset: rows x row_len*bits/8 bytes, row-major with rows
+ *          ordered [batch][nheads][rows_per_head]; int4 puts entry 2j in the
+ *          low nibble of byte j.  For SSQ_FP32 this region is the fp32 state.
+ *   scale  at scale_offset: one fp32 per row (quantized formats, else 0)
+ *   zero   at zero_offset:  one fp32 per row (asymmetric formats, else 0)
+ * Every region starts 256-byte aligned.  A zero state has all bytes 0. */
+typedef struct {
+    size_t rows;
+    size_t row_bytes;
+    size_t codes_offset;
+    size_t scale_offset;
+    size_t zero_offset;
+    size_t total_bytes;
+} ssq_layout;
+
+typedef struct ssq_state ssq_state; /* opaque handle: one layer's state */
+
+/* Size in bytes of the storage a state with this description needs (the
+ * layout's total_bytes), or 0 if the description is invalid.  For 30 delta
+ * layers of batch 256 x 32 heads x 128 x 128 fp32 this is 30 x 512 MiB =
+ * 15 GiB, the 15 GB of recurrent state at decode batch 256 reported in
+ * "Recurrent state is fixed per request, not free". */
+size_t ssq_state_bytes(const ssq_desc *desc);
+
+/* Fill *layout for desc.  SSQ_ERR_INVALID_ARG / SSQ_ERR_UNSUPPORTED as for
+ * ssq_alloc_state. */
+ssq_status ssq_state_layout(const ssq_desc *desc, ssq_layout *layout);
+
+/* Create a state.  storage: device memory of at least ssq_state_bytes(desc)
+ * bytes, 256-byte aligned, owned by the caller and outliving the handle; or
+ * NULL, and the library allocates it (hipMalloc) and frees it in
+ * ssq_free_state.  init: NULL for the zero state, else a device pointer to
+ * the fp32 state [batch][nheads][rows_per_head][row_len] that is quantized
+ * row by row with the refit above (the prompt's state written into the
+ * cache, "Mamba state quantization needs phase-aware benchmarks").  The
+ * storage is written on `stream`.  *out receives the handle. */
+ssq_status ssq_alloc_state(const ssq_desc *desc, void *storage, const float *init, void *stream,
+                           ssq_state **out);
+
+/* Destroy a handle; frees the storage only if the library allocated it.
+ * NULL is accepted.  The caller must make sure no enqueued call still uses
+ * the state. */
+ssq_status ssq_free_state(ssq_state *state);
+
+/* The description, storage pointer and layout of a state (any out pointer
+ * may be NULL). */
+ssq_status ssq_state_info(const ssq_state *state, ssq_desc *desc, void **storage, ssq_layout *layout);
+
+/* One Mamba-2 decode token for every row of the layer (README, Setup: decay
+ * lambda = exp(dt*A) per head, write dt*B*x, per-row refit every step, round
+ * to nearest; output read from the state selected by `readout`).
+ *   x [batch][nheads][P], dt [batch][nheads] (positive, already through
+ *   softplus), A [nheads] (negative), B, C [batch][ngroups][N], D [nheads];
+ *   y [batch][nheads][P] is written.  The state is updated in place. */
+ssq_status ssq_decode_step(ssq_state *state, const float *x, const float *dt, const float *A,
+                           const float *B, const float *C, const float *D, float *y,
+                           int32_t readout, void *stream);
+
+/* T Mamba-2 tokens in one launch, the state rounded after every token (the
+ * sequential per-token scan of the README's Setup, which rounds the state at
+ * every step).  Bit-identical to T calls of ssq_decode_step.
+ *   x [batch][T][nheads][P], dt [batch][T][nheads], B, C [batch][T][ngroups][N],
+ *   A, D [nheads]; y [batch][T][nheads][P] is written. */
+ssq_status ssq_scan(ssq_state *state, int32_t T, const float *x, const float *dt, const float *A,
+                    const float *B, const float *C, const float *D, float *y, int32_t readout,
+                    void *stream);
+
+/* One delta-rule step for every (sequence, head) matrix S:
+ *   S' = alpha*(I - beta*k*k^T)*S + beta*k*v^T,  o = S'^T q
+ * ("Mamba state quantization for inference": the query reads the matrix,
+ * decay and a delta-rule correction write the next version; the update
+ * S_t = A_t S_(t-1) + W_t of "Quantization error returns on the next token"),
+ * evaluated as u = k^T S (products and sum in double, rounded once),
+ * w_j = fl(beta*fl(v_j - fl(alpha*u_j))), S'_ij = fma(fl(alpha*s_i), fl(c_ij - z_i),
+ * fl(k_i*w_j)) (fp32 state: fma(alpha, S_ij, fl(k_i*w_j))), then each key row
+ * refit and rounded as above.
+ *   q, k [batch][nheads][dk], v [batch][nheads][dv], alpha, beta
+ *   [batch][nheads]; o [batch][nheads][dv] is written. */
+ssq_status ssq_delta_step(ssq_state *state, const float *q, const float *k, const float *v,
+                          const float *alpha, const float *beta, float *o, int32_t readout,
+                          void *stream);
+
+/* The fp32 value the state stands for, fl(s*fl(c - z)) per entry (the stored
+ * fp32 for SSQ_FP32): out [batch][nheads][rows_per_head][row_len]. */
+ssq_status ssq_dequant(const ssq_state *state, float *out, void *stream);
+
+/* Static text for a status code. */
+const char *ssq_status_string(ssq_status status);
+
+/* Detail of the last failed call on this thread ("" if none). */
+const char *ssq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSQ_H */

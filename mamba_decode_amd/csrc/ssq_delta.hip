@@ -1,0 +1,195 @@
+// ssq_delta.hip -- delta-rule (Gated DeltaNet / KDA style) matrix-state step
+// with the state stored quantized per key row, for gfx950.
+//
+//   S' = alpha*(I - beta*k*k^T)*S + beta*k*v^T = alpha*S + k*w^T,
+//   w  = beta*(v - alpha*u),  u = k^T S,   o = S'^T q
+// ("Mamba state quantization for inference": one dk x dv matrix per head, the
+// query reads it, decay and a delta-rule correction write the next version;
+// the kernel of the DAMP paragraph reconstructs the low-precision tier,
+// computes the recurrence in FP32, derives new quantization parameters and
+// writes the state back -- here with a single int8/int4 tier).
+//
+// Mapping: one 256-thread workgroup per (sequence, head) matrix of 128 key
+// rows x 128 values.  Thread t owns rows {t/8 + 32k : k < 4} and the 16
+// columns 16*(t%8) .. +15, so each row is held by 8 lanes of one wave and its
+// min/max and refit use DPP only.  The two column reductions (u = k^T S before
+// the update and o = S'^T q after it) cross rows: every thread reduces its four
+// rows in registers, then the 32 partial rows meet in LDS.  u is accumulated in
+// double from exact products and rounded once, so it does not depend on the
+// reduction order; o is an output only.  The whole matrix (16 KiB of int8
+// codes) is read once and written once: the kernel is bound by HBM traffic.
+#include "ssq_device.h"
+#include "ssq_internal.h"
+
+namespace ssq {
+
+template <int F, bool PRE>
+__global__ __launch_bounds__(256) void k_delta_step(DeltaArgs a)
+{
+    using Tr = Traits<F>;
+    constexpr int LPR = 8, E = 16, RG = 32, KR = 4; // lanes per row, columns per lane, row groups, rows per thread
+    constexpr int NW = Tr::quant ? E * Tr::bits / 32 : E;
+    constexpr int ROWB = Tr::quant ? 128 * Tr::bits / 8 : 512;
+    __shared__ double part_u[RG * 128]; // reused for the fp32 partials of o
+    __shared__ float u_s[128];
+
+    const int t = threadIdx.x;
+    const int rg = t >> 3, part = t & 7, j0 = part * E;
+    const int64_t mat = blockIdx.x;
+    const int64_t mrow0 = mat * 128; // first state row of the matrix
+    const float alpha = a.alpha[mat], beta = a.beta[mat];
+
+    float kk[KR], qq[KR], s_old[KR], z_old[KR];
+    float S[KR][E];
+#pragma unroll
+    for (int r = 0; r < KR; ++r) {
+        const int i = rg + RG * r;
+        kk[r] = a.k[mrow0 + i];
+        qq[r] = a.q[mrow0 + i];
+        const int64_t row = mrow0 + i;
+        if constexpr (Tr::quant) {
+            uint32_t cw[NW];
+            load_words<NW>(a.codes + row * ROWB + part * (NW * 4), cw);
+            unpack_codes<F, E>(cw, S[r]);
+            s_old[r] = a.scale[row];
+            z_old[r] = Tr::asym ? a.zero[row] : 0.0f;
+            if constexpr (Tr::asym) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) S[r][e] = S[r][e] - z_old[r]; // d = fl(c - z)
+            }
+        } else {
+            load_f32<E>(a.h32 + row * 128 + j0, S[r]);
+            s_old[r] = 1.0f;
+            z_old[r] = 0.0f;
+        }
+    }
+    float vv[E];
+    load_f32<E>(a.v + mrow0 + j0, vv);
+
+    // u = k^T S: exact products k_i*s_i*d_ij (quantized) or k_i*S_ij summed in double
+    {
+        double up[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) up[e] = 0.0;
+#pragma unroll
+        for (int r = 0; r < KR; ++r) {
+            const double kap = Tr::quant ? (double)kk[r] * (double)s_old[r] : (double)kk[r];
+#pragma unroll
+            for (int e = 0; e < E; ++e) up[e] = __builtin_fma(kap, (double)S[r][e], up[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) part_u[rg * 128 + j0 + e] = up[e];
+    }
+    __syncthreads();
+    if (t < 128) {
+        double acc = 0.0;
+#pragma unroll 8
+        for (int r = 0; r < RG; ++r) acc += part_u[r * 128 + t];
+        u_s[t] = (float)acc;
+    }
+    __syncthreads();
+
+    // w = beta*(v - alpha*u)
+    float ww[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const float au = alpha * u_s[j0 + e];
+        const float vm = vv[e] - au;
+        ww[e] = beta * vm;
+    }
+
+    // S' = alpha*S + k w^T, row by row; refit, round and store each row
+    float op[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) op[e] = 0.0f;
+#pragma unroll
+    for (int r = 0; r < KR; ++r) {
+        const int64_t row = mrow0 + rg + RG * r;
+        const float as = Tr::quant ? alpha * s_old[r] : alpha;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const float kw = kk[r] * ww[e];
+            S[r][e] = __builtin_fmaf(as, S[r][e], kw);
+        }
+        if constexpr (!Tr::quant || PRE) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) op[e] = __builtin_fmaf(qq[r], S[r][e], op[e]);
+        }
+        if constexpr (Tr::quant) {
+            float mn = 0.0f, mx = 0.0f, am = 0.0f;
+            if constexpr (Tr::asym) {
+                mn = S[r][0];
+                mx = S[r][0];
+#pragma unroll
+                for (int e = 1; e < E; ++e) {
+                    mn = fminf(mn, S[r][e]);
+                    mx = fmaxf(mx, S[r][e]);
+                }
+                mn = group_min<LPR>(mn);
+                mx = group_max<LPR>(mx);
+            } else {
+#pragma unroll
+                for (int e = 0; e < E; ++e) am = fmaxf(am, fabsf(S[r][e]));
+                am = group_max<LPR>(am);
+            }
+            const RowGrid g = refit<F>(mn, mx, am);
+            const bool slow_any = Tr::asym && __any(g.slow);
+            float f[E];
+            round_codes<F, E>(S[r], g, slow_any, f);
+            uint32_t ow[NW];
+            pack_codes<F, E>(f, ow);
+            store_words<NW>(a.codes + row * ROWB + part * (NW * 4), ow);
+            if (part == 0) {
+                a.scale[row] = g.s;
+                if constexpr (Tr::asym) a.zero[row] = g.z;
+            }
+            if constexpr (!PRE) {
+                const float qs = qq[r] * g.s;
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float cz = code_minus_z(f[e], g) - g.zadj;
+                    op[e] = __builtin_fmaf(qs, cz, op[e]);
+                }
+            }
+        } else {
+            store_f32<E>(a.h32 + row * 128 + j0, S[r]);
+        }
+    }
+
+    // o = S'^T q: 32 partial rows meet in LDS
+    float* part_o = reinterpret_cast<float*>(part_u);
+#pragma unroll
+    for (int e = 0; e < E; ++e) part_o[rg * 128 + j0 + e] = op[e];
+    __syncthreads();
+    if (t < 128) {
+        float acc = 0.0f;
+#pragma unroll 8
+        for (int r = 0; r < RG; ++r) acc += part_o[r * 128 + t];
+        a.o[mrow0 + t] = acc;
+    }
+}
+
+template <int F>
+static hipError_t launch_delta_f(DeltaArgs a, bool pre, hipStream_t st)
+{
+    const unsigned blocks = (unsigned)a.nmat;
+    if (pre)
+        hipLaunchKernelGGL((k_delta_step<F, true>), dim3(blocks), dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL((k_delta_step<F, false>), dim3(blocks), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_delta_step(int fmt, DeltaArgs a, bool pre, hipStream_t st)
+{
+    switch (fmt) {
+    case FP32: return launch_delta_f<FP32>(a, pre, st);
+    case INT8_SYM: return launch_delta_f<INT8_SYM>(a, pre, st);
+    case INT8_ASYM: return launch_delta_f<INT8_ASYM>(a, pre, st);
+    case INT4_SYM: return launch_delta_f<INT4_SYM>(a, pre, st);
+    case INT4_ASYM: return launch_delta_f<INT4_ASYM>(a, pre, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+} // namespace ssq

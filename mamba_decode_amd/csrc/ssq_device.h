@@ -1,0 +1,329 @@
+// ssq_device.h -- device building blocks of the quantized state update (gfx950).
+//
+// A state row is N = 128 entries.  LPR lanes of a wave64 cooperate on a row,
+// each holding E = 128/LPR consecutive entries in registers, so a wave covers
+// 64/LPR rows at once.  Cross-lane reductions over the LPR lanes of a row use
+// DPP (quad_perm, row_half_mirror, row_mirror), never LDS.
+//
+// Evaluation order (identical in every kernel, so that the decode step, the
+// scan and the state initialisation round the same way):
+//   lambda  = fl32(exp_double(fl(dt*A)))
+//   h'_n    = fma(fl(lambda*s), fl(c_n - z), fl(w*B_n)),  w = fl(dt*x)
+//   refit   (asymmetric) s' = fl(fl(mx-mn)/(2^b-1)), inv = fl(1/s'),
+//           z' = -rne(fl(mn*inv));  (symmetric) s' = fl(amax/(2^(b-1)-1))
+//   code    = clamp(rne(fl(h'*inv) + z')), the sum exact, ties to the even code
+//
+// The rounding uses the 1.5*2^23 trick: for |t| < 2^22, fl(t + 1.5*2^23) is
+// 1.5*2^23 + rne(t) exactly, because floats in [2^23, 2^24) are the integers.
+// Adding z' to the constant first (exact while |z'| < 2^21) rounds the exact
+// sum v + z'.  Rows with |z'| >= 2^21 (a spread below ~2^-13 of the row's
+// offset) take a slow path in which v + z' is exact by Sterbenz's lemma.
+// The clamped value's bit pattern minus that of 1.5*2^23 is the code itself,
+// so packing needs no float-to-int conversion.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssq {
+
+enum Format : int { FP32 = 0, INT8_SYM = 1, INT8_ASYM = 2, INT4_SYM = 3, INT4_ASYM = 4 };
+
+template <int F> struct Traits;
+template <> struct Traits<FP32> {
+    static constexpr bool quant = false, asym = false;
+    static constexpr int bits = 32, lo = 0, hi = 0;
+};
+template <> struct Traits<INT8_SYM> {
+    static constexpr bool quant = true, asym = false;
+    static constexpr int bits = 8, lo = -127, hi = 127;
+};
+template <> struct Traits<INT8_ASYM> {
+    static constexpr bool quant = true, asym = true;
+    static constexpr int bits = 8, lo = 0, hi = 255;
+};
+template <> struct Traits<INT4_SYM> {
+    static constexpr bool quant = true, asym = false;
+    static constexpr int bits = 4, lo = -7, hi = 7;
+};
+template <> struct Traits<INT4_ASYM> {
+    static constexpr bool quant = true, asym = true;
+    static constexpr int bits = 4, lo = 0, hi = 15;
+};
+
+constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+constexpr float kSlowZero = 2097152.0f; // 2^21
+constexpr float kFltMin = 1.17549435e-38f;
+
+// ---------------------------------------------------------------------------
+// DPP cross-lane helpers (every lane of a 16-lane DPP row is a valid source)
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// xor 1, xor 2 inside a quad; lane i <-> 7-i inside 8; lane i <-> 15-i inside 16
+template <int LPR>
+__device__ __forceinline__ float group_min(float v)
+{
+    if constexpr (LPR >= 2) v = fminf(v, dppf<0xB1>(v));
+    if constexpr (LPR >= 4) v = fminf(v, dppf<0x4E>(v));
+    if constexpr (LPR >= 8) v = fminf(v, dppf<0x141>(v));
+    if constexpr (LPR >= 16) v = fminf(v, dppf<0x140>(v));
+    return v;
+}
+template <int LPR>
+__device__ __forceinline__ float group_max(float v)
+{
+    if constexpr (LPR >= 2) v = fmaxf(v, dppf<0xB1>(v));
+    if constexpr (LPR >= 4) v = fmaxf(v, dppf<0x4E>(v));
+    if constexpr (LPR >= 8) v = fmaxf(v, dppf<0x141>(v));
+    if constexpr (LPR >= 16) v = fmaxf(v, dppf<0x140>(v));
+    return v;
+}
+// every lane of the group ends with the same sum (each step adds a value and its mirror)
+template <int LPR>
+__device__ __forceinline__ float group_sum(float v)
+{
+    if constexpr (LPR >= 2) v = v + dppf<0xB1>(v);
+    if constexpr (LPR >= 4) v = v + dppf<0x4E>(v);
+    if constexpr (LPR >= 8) v = v + dppf<0x141>(v);
+    if constexpr (LPR >= 16) v = v + dppf<0x140>(v);
+    return v;
+}
+
+__device__ __forceinline__ float readlane_f(float v, int lane)
+{
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// lambda = exp(dt*A): the fp32 product, exponentiated in double, rounded once
+__device__ __forceinline__ float decay(float dt, float A)
+{
+    const float e = dt * A;
+    return (float)exp((double)e);
+}
+
+// ---------------------------------------------------------------------------
+// codes <-> fp32 for one lane's E entries held in NW = E*bits/32 words
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float ubyte_f(uint32_t w, int k)
+{
+    return (float)((w >> (8 * k)) & 0xFFu); // v_cvt_f32_ubyte{k}
+}
+
+// c_n as float (sym: the signed code; asym: 0..2^b-1)
+template <int F, int E>
+__device__ __forceinline__ void unpack_codes(const uint32_t* w, float* c)
+{
+    if constexpr (F == INT8_ASYM) {
+#pragma unroll
+        for (int i = 0; i < E / 4; ++i)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) c[4 * i + k] = ubyte_f(w[i], k);
+    } else if constexpr (F == INT8_SYM) {
+#pragma unroll
+        for (int i = 0; i < E / 4; ++i)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) c[4 * i + k] = (float)(int)(int8_t)(w[i] >> (8 * k));
+    } else if constexpr (F == INT4_ASYM) {
+#pragma unroll
+        for (int i = 0; i < E / 8; ++i) {
+            const uint32_t lo = w[i] & 0x0F0F0F0Fu, hi = (w[i] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                c[8 * i + 2 * k] = ubyte_f(lo, k);
+                c[8 * i + 2 * k + 1] = ubyte_f(hi, k);
+            }
+        }
+    } else if constexpr (F == INT4_SYM) {
+        // two's complement nibble x becomes x + 8 after flipping its sign bit
+#pragma unroll
+        for (int i = 0; i < E / 8; ++i) {
+            const uint32_t b = w[i] ^ 0x88888888u;
+            const uint32_t lo = b & 0x0F0F0F0Fu, hi = (b >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                c[8 * i + 2 * k] = ubyte_f(lo, k) - 8.0f;
+                c[8 * i + 2 * k + 1] = ubyte_f(hi, k) - 8.0f;
+            }
+        }
+    }
+}
+
+// byte 0 of four words -> one word (v_perm_b32: bytes 0-3 of the 2nd operand, 4-7 of the 1st)
+__device__ __forceinline__ uint32_t gather_b0(uint32_t a, uint32_t b, uint32_t c, uint32_t d)
+{
+    const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0C0C0400u);
+    const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x0C0C0400u);
+    return __builtin_amdgcn_perm(cd, ab, 0x05040100u);
+}
+
+// f[e] = 1.5*2^23 + code: the low bits of its pattern are the code
+template <int F, int E>
+__device__ __forceinline__ void pack_codes(const float* f, uint32_t* w)
+{
+    if constexpr (F == INT8_ASYM || F == INT8_SYM) {
+#pragma unroll
+        for (int i = 0; i < E / 4; ++i)
+            w[i] = gather_b0(__float_as_uint(f[4 * i]), __float_as_uint(f[4 * i + 1]),
+                             __float_as_uint(f[4 * i + 2]), __float_as_uint(f[4 * i + 3]));
+    } else {
+#pragma unroll
+        for (int i = 0; i < E / 8; ++i) {
+            const uint32_t ev = gather_b0(__float_as_uint(f[8 * i]), __float_as_uint(f[8 * i + 2]),
+                                          __float_as_uint(f[8 * i + 4]), __float_as_uint(f[8 * i + 6]));
+            const uint32_t od = gather_b0(__float_as_uint(f[8 * i + 1]), __float_as_uint(f[8 * i + 3]),
+                                          __float_as_uint(f[8 * i + 5]), __float_as_uint(f[8 * i + 7]));
+            if constexpr (F == INT4_ASYM)
+                w[i] = ev | (od << 4); // codes < 16: no carry between nibbles
+            else
+                w[i] = (ev & 0x0F0F0F0Fu) | ((od << 4) & 0xF0F0F0F0u);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// refit of one row from its statistics (every lane of the row computes it)
+// ---------------------------------------------------------------------------
+struct RowGrid {
+    float s;     // stored scale
+    float z;     // stored zero point (0 for symmetric)
+    float inv;   // 1/s, or 0 for a degenerate row (all codes 0)
+    float Mz;    // 1.5*2^23 + z on the fast path
+    float zc;    // z used for coding (0 for a degenerate row)
+    float zadj;  // z for readout of a degenerate asymmetric row, else 0
+    bool slow;   // |z| >= 2^21
+};
+
+template <int F>
+__device__ __forceinline__ RowGrid refit(float mn, float mx, float amax)
+{
+    RowGrid g;
+    g.slow = false;
+    g.zadj = 0.0f;
+    if constexpr (Traits<F>::asym) {
+        constexpr float qmax = (float)Traits<F>::hi;
+        const float range = mx - mn;
+        const float s = range / qmax;
+        if (!(s >= kFltMin)) {
+            // the row is kept as the constant mn: s = |mn|, z = -sign(mn), codes 0
+            g.s = fabsf(mn);
+            g.z = -(mn > 0.0f ? 1.0f : (mn < 0.0f ? -1.0f : 0.0f));
+            g.inv = 0.0f;
+            g.zc = 0.0f;
+            g.zadj = g.z;
+            g.Mz = kMagic;
+        } else {
+            const float inv = 1.0f / s;
+            const float vmin = mn * inv;
+            const float z = -rintf(vmin);
+            g.s = s;
+            g.z = z;
+            g.inv = inv;
+            g.zc = z;
+            g.slow = fabsf(z) >= kSlowZero;
+            g.Mz = kMagic + z;
+        }
+    } else {
+        constexpr float qmax = (float)Traits<F>::hi;
+        const float s = amax / qmax;
+        g.z = 0.0f;
+        g.zc = 0.0f;
+        g.Mz = kMagic;
+        if (!(s >= kFltMin)) {
+            g.s = 0.0f;
+            g.inv = 0.0f;
+        } else {
+            g.s = s;
+            g.inv = 1.0f / s;
+        }
+    }
+    return g;
+}
+
+// f = 1.5*2^23 + clamp(rne(fl(h*inv) + z)) for E entries; `slow_any` is wave-uniform
+template <int F, int E>
+__device__ __forceinline__ void round_codes(const float* h, const RowGrid& g, bool slow_any, float* f)
+{
+    constexpr float flo = kMagic + (float)Traits<F>::lo;
+    constexpr float fhi = kMagic + (float)Traits<F>::hi;
+    if (!slow_any) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const float v = h[e] * g.inv;
+            f[e] = __builtin_amdgcn_fmed3f(v + g.Mz, flo, fhi);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const float v = h[e] * g.inv;
+            const float t = g.slow ? kMagic + rintf(v + g.zc) : v + g.Mz;
+            f[e] = __builtin_amdgcn_fmed3f(t, flo, fhi);
+        }
+    }
+}
+
+// (code - z) as float from f, exact on the fast path
+__device__ __forceinline__ float code_minus_z(float f, const RowGrid& g)
+{
+    return g.slow ? (f - kMagic) - g.zc : f - g.Mz;
+}
+
+// ---------------------------------------------------------------------------
+// vector memory helpers: NW consecutive 32-bit words at a 4*NW-byte aligned address
+// ---------------------------------------------------------------------------
+template <int NW>
+__device__ __forceinline__ void load_words(const void* p, uint32_t* w)
+{
+    if constexpr (NW % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < NW / 4; ++i) {
+            const uint4 v = reinterpret_cast<const uint4*>(p)[i];
+            w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+        }
+    } else if constexpr (NW == 2) {
+        const uint2 v = *reinterpret_cast<const uint2*>(p);
+        w[0] = v.x; w[1] = v.y;
+    } else {
+        static_assert(NW == 1, "unsupported lane width");
+        w[0] = *reinterpret_cast<const uint32_t*>(p);
+    }
+}
+
+template <int NW>
+__device__ __forceinline__ void store_words(void* p, const uint32_t* w)
+{
+    if constexpr (NW % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < NW / 4; ++i)
+            reinterpret_cast<uint4*>(p)[i] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+    } else if constexpr (NW == 2) {
+        *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
+    } else {
+        *reinterpret_cast<uint32_t*>(p) = w[0];
+    }
+}
+
+template <int E>
+__device__ __forceinline__ void load_f32(const float* p, float* v)
+{
+    static_assert(E % 4 == 0, "E must be a multiple of 4");
+#pragma unroll
+    for (int i = 0; i < E / 4; ++i) {
+        const float4 t = reinterpret_cast<const float4*>(p)[i];
+        v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
+    }
+}
+
+template <int E>
+__device__ __forceinline__ void store_f32(float* p, const float* v)
+{
+#pragma unroll
+    for (int i = 0; i < E / 4; ++i)
+        reinterpret_cast<float4*>(p)[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+}
+
+} // namespace ssq

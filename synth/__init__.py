@@ -193,9 +193,22 @@ def init_state_rows(seed: int, layer: int, rows: np.ndarray, N: int,
     return _f32(v)
 
 
-def init_state(seed: int, layer: int, nrows: int, N: int, **kw) -> np.ndarray:
-    """Initial fp32 state of rows 0..nrows-1: [nrows][N] float32 (see ``init_state_rows``)."""
-    return init_state_rows(seed, layer, np.arange(nrows, dtype=np.uint64), N, **kw)
+def init_state(seed: int, layer: int, nrows: int, N: int, threads: int = 1, **kw) -> np.ndarray:
+    """Initial fp32 state of rows 0..nrows-1: [nrows][N] float32 (see ``init_state_rows``).
+    ``threads`` > 1 draws row chunks concurrently (same values: the generator is counter based)."""
+    if threads <= 1 or nrows < 4096:
+        return init_state_rows(seed, layer, np.arange(nrows, dtype=np.uint64), N, **kw)
+    from concurrent.futures import ThreadPoolExecutor
+    out = np.empty((nrows, N), np.float32)
+    step = max(1024, (nrows + 4 * threads - 1) // (4 * threads))
+
+    def work(r0):
+        r1 = min(nrows, r0 + step)
+        out[r0:r1] = init_state_rows(seed, layer, np.arange(r0, r1, dtype=np.uint64), N, **kw)
+
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(work, range(0, nrows, step)))
+    return out
 
 
 def delta_inputs(seed: int, layer: int, Bsz: int, H: int, dk: int, dv: int, t: int = 0):

@@ -1,0 +1,126 @@
+"""GPU parity of the delta-rule path (ssq_delta_step) against the CPU oracle, through the C ABI."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import mamba_decode_amd as ssq
+    from tests import parity as par
+
+FORMATS = ["fp32", "int8_sym", "int8_asym", "int4_sym", "int4_asym"]
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def ddesc(fmt, B, H):
+    return ssq.make_desc(ssq.SSQ_DELTA, fmt, B, H, 128, 128)
+
+
+def run_delta(gst, q, k, v, al, be, readout):
+    o = torch.empty(v.shape, dtype=torch.float32, device="cuda")
+    ssq.ssq_delta_step(gst, par.dev(q), par.dev(k), par.dev(v), par.dev(al), par.dev(be), o, readout)
+    return o.cpu().numpy()
+
+
+def u_tie_rows(ost_before, k, B, H):
+    """Key rows whose update read a column sum u_j = k^T S that lies near an fp32 rounding midpoint
+    (there the double-precision sums of the two sides may round u differently).  Returns a
+    boolean per matrix: True if some column of that matrix is near a midpoint."""
+    if ost_before.fmt == "fp32":
+        S = ost_before.h.astype(np.float64)
+    else:
+        S = ost_before.scale.astype(np.float64)[:, None] * (ost_before.code - ost_before.zero[:, None])
+    S = S.reshape(B * H, 128, 128)
+    u = np.einsum("mi,mij->mj", k.reshape(B * H, 128).astype(np.float64), S)
+    uf = u.astype(np.float32)
+    nxt = np.nextafter(uf, np.where(u > uf, np.inf, -np.inf).astype(np.float32))
+    mid = (uf.astype(np.float64) + nxt.astype(np.float64)) / 2
+    near = np.abs(u - mid) <= np.abs(u) * 2.0 ** -40
+    return near.any(axis=1)
+
+
+@pytest.mark.parametrize("readout", ["post", "pre"])
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_delta_step_teacher_forced(fmt, readout):
+    B, H, T = 2, 3, 4
+    rows = B * H * 128
+    ro = ssq.SSQ_READ_PRE_QUANT if readout == "pre" else ssq.SSQ_READ_POST_QUANT
+    init = synth.init_state(91, 0, rows, 128)
+    init[5] = 0.0          # a degenerate key row
+    init[200] = 2.5        # a constant key row
+    ost = oracle.make_state(fmt, rows, 128, init)
+    gst = par.new_gpu_state(ddesc(fmt, B, H))
+    for t in range(T):
+        say(f"delta teacher-forced fmt={fmt} readout={readout} t={t}")
+        q, k, v, al, be = synth.delta_inputs(91, 0, B, H, 128, 128, t=t)
+        par.write_gpu_state(gst, ost)
+        before = ost.copy()
+        og = run_delta(gst, q, k, v, al, be, ro)
+        oo, _, vq = oracle.delta_step(ost, q, k, v, al, be, B, H, readout=readout, diag=True)
+        g = par.read_gpu_state(gst, fmt)
+        if fmt == "fp32":
+            tie = u_tie_rows(before, k, B, H)
+            same = np.array_equal(g["h"], ost.h)
+            if not same:
+                bad = np.unique(np.nonzero((g["h"] != ost.h).any(axis=1))[0] // 128)
+                assert np.all(tie[bad]), t
+        else:
+            par.check_codes(g, ost.code, ost.scale, ost.zero, vq, fmt, f"t={t}")
+        assert par.block_rel(og, oo, axis=2) <= 1e-5, t
+
+
+def test_delta_identity_and_decay_on_gpu():
+    """alpha = beta = 1 with unit k writes v at key k (fp32 state); beta = 0 is a pure decay
+    that keeps the codes of full-range rows."""
+    B, H = 2, 2
+    rows = B * H * 128
+    q, k, v, al, be = synth.delta_inputs(92, 0, B, H, 128, 128)
+    al[:] = 1
+    be[:] = 1
+    gst = par.new_gpu_state(ddesc("fp32", B, H), synth.init_state(92, 0, rows, 128))
+    o = run_delta(gst, k, k, v, al, be, ssq.SSQ_READ_POST_QUANT)
+    assert par.block_rel(o, v) <= 1e-5
+    init = synth.init_state(93, 0, rows, 128)
+    g8 = par.new_gpu_state(ddesc("int8_asym", B, H), init)
+    c0 = par.read_gpu_state(g8, "int8_asym")
+    full = c0["code"].max(axis=1) == 255
+    q, k, v, al, be = synth.delta_inputs(93, 0, B, H, 128, 128)
+    be[:] = 0
+    run_delta(g8, q, k, v, al, be, ssq.SSQ_READ_POST_QUANT)
+    c1 = par.read_gpu_state(g8, "int8_asym")
+    assert np.array_equal(c1["code"][full], c0["code"][full]) and np.array_equal(c1["zero"][full], c0["zero"][full])
+
+
+def test_delta_layer_full_size_sampled():
+    """Delta-rule layer at the footprint the pages profile: batch 256 x 32 heads x 128 x 128, int8
+    asymmetric state from a seeded random state, one step; 48 sampled matrices checked."""
+    B, H, fmt = 256, 32, "int8_asym"
+    rows = B * H * 128
+    say("delta full layer: generating init")
+    init = synth.init_state(3, 0, rows, 128, threads=8)
+    gst = par.new_gpu_state(ddesc(fmt, B, H), init)
+    mats = np.unique(np.linspace(0, B * H - 1, 48).astype(np.int64))
+    srows = (mats[:, None] * 128 + np.arange(128)).reshape(-1)
+    ost = oracle.make_state(fmt, len(srows), 128, init[srows])
+    del init
+    g0 = par.read_gpu_state(gst, fmt)
+    assert np.array_equal(g0["code"][srows], ost.code)
+    q, k, v, al, be = synth.delta_inputs(3, 0, B, H, 128, 128)
+    say("delta full layer: step")
+    og = run_delta(gst, q, k, v, al, be, ssq.SSQ_READ_POST_QUANT).reshape(B * H, 128)
+    sel = lambda a: a.reshape(B * H, *a.shape[2:])[mats][None]  # noqa: E731
+    oo, _, vq = oracle.delta_step(ost, sel(q), sel(k), sel(v), al.reshape(-1)[mats][None],
+                                  be.reshape(-1)[mats][None], 1, len(mats), diag=True)
+    g = par.read_gpu_state(gst, fmt)
+    sub = {"code": g["code"][srows], "scale": g["scale"][srows], "zero": g["zero"][srows]}
+    par.check_codes(sub, ost.code, ost.scale, ost.zero, vq, fmt, "full layer")
+    assert par.block_rel(og[mats], oo[0], axis=1) <= 1e-5
