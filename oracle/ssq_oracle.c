@@ -37,28 +37,32 @@
  * order; fl() is one fp32 rounding):
  *    lambda = fl32(exp_double(fl(dt*A)))          exp taken in double
  *    w      = fl(dt*x)
- *    quantized row (scale s, zero z, codes c):
- *      d_n  = fl(c_n - z)                         exact for |z| < 2^24
- *      h'_n = fma(fl(lambda*s), d_n, fl(w*B_n))   decay acts on the row's scale
+ *    quantized row (scale s, zero z, codes c), the decay acting on the scale:
+ *      ls   = fl(lambda*s)
+ *      h'_n = fma(ls, c_n, fma(w, B_n, -fl(ls*z)))
+ *             i.e. lambda*s*(c_n - z) + w*B_n, the offset -ls*z folded into
+ *             the write term (z = 0 for the symmetric grid)
  *    fp32 row:  h'_n = fma(lambda, h_n, fl(w*B_n))
  *    refit, asymmetric: mn, mx = min/max h'; s' = fl(fl(mx-mn)/(2^b-1));
- *      inv = fl(1/s'); z' = -rne(fl(mn*inv));
- *      c'_n = clamp(rne(fl(h'_n*inv) + z'), 0, 2^b-1), the sum exact and the
- *      tie going to the even code
+ *      inv = fl(1/s'); z' = -rne(mn*inv);
+ *      c'_n = clamp(rne(h'_n*inv + z'), 0, 2^b-1)
  *    refit, symmetric: s' = fl(amax/(2^(b-1)-1)); inv = fl(1/s');
- *      c'_n = clamp(rne(fl(h'_n*inv)), -(2^(b-1)-1), 2^(b-1)-1)
+ *      c'_n = clamp(rne(h'_n*inv), -(2^(b-1)-1), 2^(b-1)-1)
+ *    where rne() rounds the exact real value (the product h'*inv is not
+ *      rounded first) to the nearest integer, a tie going to the even code.
  *    degenerate rows: if s' is zero or subnormal the row carries no usable
  *      step.  Asymmetric rows are then stored as the constant mn (s' = |mn|,
  *      z' = -sign(mn), all codes 0, which dequantizes to mn exactly);
  *      symmetric rows are stored as zero (s' = 0, codes 0).
+ *    a zero point of zero is stored as +0.
  *    dequantized value: fl(s*fl(c - z)).
  *    Readouts (y, o) are output only: they are accumulated here in double and
  *    rounded once, so they are the most accurate value any order can give.
  *    Delta rule: u_j = RN32(sum_i k_i*S_ij) with the products and the sum
  *      taken in double (for a quantized S, S_ij = s_i*(c_ij - z_i) as a real
  *      number); w_j = fl(beta*fl(v_j - fl(alpha*u_j)));
- *      S'_ij = fma(fl(alpha*s_i), d_ij, fl(k_i*w_j)) (quantized) or
- *      fma(alpha, S_ij, fl(k_i*w_j)) (fp32).
+ *      S'_ij = fma(as_i, c_ij, fma(k_i, w_j, -fl(as_i*z_i))), as_i = fl(alpha*s_i)
+ *      (quantized) or fma(alpha, S_ij, fl(k_i*w_j)) (fp32).
  */
 #include <float.h>
 #include <math.h>
@@ -84,6 +88,23 @@ float orc_decay(float dt, float A)
 /* one row: refit and round to nearest                                       */
 /* ------------------------------------------------------------------------ */
 
+/* The integer nearest to the real number p + z (p a double, z an integer
+ * valued double), a tie going to the even result.  p - floor(p) is exact, so
+ * the decision is exact even where p + z itself is not representable. */
+static double rne_sum(double p, double z)
+{
+    double f = floor(p);
+    double r = p - f;
+    double k;
+    if (r > 0.5)
+        k = f + 1.0;
+    else if (r < 0.5)
+        k = f;
+    else
+        k = (fmod(f + z, 2.0) == 0.0) ? f : f + 1.0;
+    return k + z;
+}
+
 static float sign_of(float c)
 {
     if (c > 0.0f)
@@ -95,7 +116,8 @@ static float sign_of(float c)
 
 /* Quantize the n entries of h with a b-bit grid (bits in 2..8).  Writes the
  * integer codes, the scale and the zero point (0 for the symmetric grid).
- * v_out, if not NULL, receives fl(h_n*inv): the fp32 value that is rounded. */
+ * v_out, if not NULL, receives fl(h_n*inv), the value that is rounded (to
+ * within half an ulp: the rounding itself uses the exact product). */
 void orc_quantize_row(const float *h, int n, int bits, int asym, int32_t *code, float *s_out,
                       float *z_out, float *v_out)
 {
@@ -113,7 +135,7 @@ void orc_quantize_row(const float *h, int n, int bits, int asym, int32_t *code, 
         float s = range / cmax;
         if (!(s >= FLT_MIN)) {
             *s_out = fabsf(mn);
-            *z_out = -sign_of(mn);
+            *z_out = -sign_of(mn) + 0.0f; /* a zero zero point is stored as +0 */
             for (i = 0; i < n; ++i) {
                 code[i] = 0;
                 if (v_out)
@@ -122,12 +144,11 @@ void orc_quantize_row(const float *h, int n, int bits, int asym, int32_t *code, 
             return;
         }
         float inv = 1.0f / s;
-        float vmin = mn * inv;
-        float z = -nearbyintf(vmin);
+        /* products of two floats are exact in double */
+        float z = (float)(-rne_sum((double)mn * (double)inv, 0.0)) + 0.0f; /* +0, never -0 */
         for (i = 0; i < n; ++i) {
             float v = h[i] * inv;
-            /* v + z is exact in double: v has 24 significant bits and z is an integer */
-            double t = nearbyint((double)v + (double)z);
+            double t = rne_sum((double)h[i] * (double)inv, (double)z);
             if (t < 0.0)
                 t = 0.0;
             if (t > (double)cmax)
@@ -160,7 +181,7 @@ void orc_quantize_row(const float *h, int n, int bits, int asym, int32_t *code, 
         float inv = 1.0f / s;
         for (i = 0; i < n; ++i) {
             float v = h[i] * inv;
-            double t = nearbyint((double)v);
+            double t = rne_sum((double)h[i] * (double)inv, 0.0);
             if (t < -(double)cmax)
                 t = -(double)cmax;
             if (t > (double)cmax)
@@ -232,11 +253,10 @@ static float mamba2_row_step(int N, int bits, int asym, int32_t *code, float *s,
 
     {
         float ls = lam * (*s);
-        float zo = *z;
+        float lz = ls * (*z);
         for (n = 0; n < N; ++n) {
-            float d = (float)code[n] - zo;
-            float wb = w * Bn[n];
-            work[n] = fmaf(ls, d, wb);
+            float wb = fmaf(w, Bn[n], -lz);
+            work[n] = fmaf(ls, (float)code[n], wb);
             if (hpre)
                 hpre[n] = work[n];
         }
@@ -410,10 +430,10 @@ static int delta_matrix_step(int dk, int dv, int bits, int asym, int32_t *code, 
             }
         } else {
             float as = alpha * s[i];
+            float az = as * z[i];
             for (j = 0; j < dv; ++j) {
-                float d = (float)code[(int64_t)i * dv + j] - z[i];
-                float kw = k[i] * w[j];
-                Sn[(int64_t)i * dv + j] = fmaf(as, d, kw);
+                float kw = fmaf(k[i], w[j], -az);
+                Sn[(int64_t)i * dv + j] = fmaf(as, (float)code[(int64_t)i * dv + j], kw);
             }
         }
     }

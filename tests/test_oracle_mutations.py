@@ -21,11 +21,13 @@ SRC = open(os.path.join(os.path.dirname(oracle.__file__), "ssq_oracle.c")).read(
 MUTATIONS = [
     ("fp32 write term dropped", "            float wb = w * Bn[n];\n            h[n] = fmaf(lam, h[n], wb);",
      "            float wb = 0.0f * Bn[n];\n            h[n] = fmaf(lam, h[n], wb);"),
-    ("quantized write term dropped", "            float wb = w * Bn[n];\n            work[n]",
-     "            float wb = 0.0f * Bn[n];\n            work[n]"),
-    ("zero point added instead of subtracted", "float d = (float)code[n] - zo;", "float d = (float)code[n] + zo;"),
-    ("zero point sign flipped", "float z = -nearbyintf(vmin);", "float z = nearbyintf(vmin);"),
-    ("zero point from the max", "float vmin = mn * inv;", "float vmin = mx * inv;"),
+    ("quantized write term dropped", "float wb = fmaf(w, Bn[n], -lz);", "float wb = fmaf(0.0f, Bn[n], -lz);"),
+    ("zero-point offset not folded in", "float wb = fmaf(w, Bn[n], -lz);", "float wb = w * Bn[n];"),
+    ("zero point added instead of subtracted", "float lz = ls * (*z);", "float lz = -ls * (*z);"),
+    ("zero point sign flipped", "float z = (float)(-rne_sum((double)mn * (double)inv, 0.0)) + 0.0f;",
+     "float z = (float)(rne_sum((double)mn * (double)inv, 0.0)) + 0.0f;"),
+    ("zero point from the max", "float z = (float)(-rne_sum((double)mn * (double)inv, 0.0)) + 0.0f;",
+     "float z = (float)(-rne_sum((double)mx * (double)inv, 0.0)) + 0.0f;"),
     ("symmetric grid off by one", "const float cmax = (float)((1 << (bits - 1)) - 1);",
      "const float cmax = (float)((1 << (bits - 1)));"),
     ("asymmetric grid off by one", "const float cmax = (float)((1 << bits) - 1);",
@@ -35,8 +37,8 @@ MUTATIONS = [
     ("readouts swapped", "    if (readout_pre) {\n        for (n = 0; n < N; ++n)",
      "    if (!readout_pre) {\n        for (n = 0; n < N; ++n)"),
     ("D*x dropped", "float dx = D * x;", "float dx = 0.0f * x;"),
-    ("ties away from zero", "double t = nearbyint((double)v + (double)z);",
-     "double t = round((double)v + (double)z);"),
+    ("ties always up", "k = (fmod(f + z, 2.0) == 0.0) ? f : f + 1.0;", "k = f + 1.0;"),
+    ("rounding to the floor", "    if (r > 0.5)\n        k = f + 1.0;", "    if (r > 1.5)\n        k = f + 1.0;"),
     ("top clamp missing", "            if (t > (double)cmax)\n                t = (double)cmax;\n            code[i] = (int32_t)t;\n            if (v_out)\n                v_out[i] = v;\n        }\n        *s_out = s;\n        *z_out = z;",
      "            code[i] = (int32_t)t;\n            if (v_out)\n                v_out[i] = v;\n        }\n        *s_out = s;\n        *z_out = z;"),
     ("scan reads token 0 every step", "memcpy(xs + (size_t)b * H * P, x + ((size_t)b * T + t) * H * P",

@@ -282,6 +282,7 @@ def test_error_recurrence(fmt):
     for t in range(T):
         x, dt, Bm, Cm, A, D = synth.mamba2_step_inputs(6, 0, Bsz, H, G, P, N, t=t)
         hq_prev, hf_prev = sq.dequant().astype(F64), sf.h.astype(F64)
+        sz_prev = (sq.scale.astype(F64) * sq.zero.astype(F64))[:, None]  # the folded offset s*z
         _, htil, _ = oracle.mamba2_step(sq, x, dt, A, Bm, Cm, D, diag=True)
         oracle.mamba2_step(sf, x, dt, A, Bm, Cm, D)
         lam = np.float32(np.exp(np.float32(dt * A).astype(F64)))  # the fp32 decay [B][H]
@@ -292,8 +293,10 @@ def test_error_recurrence(fmt):
         delta = hq - hf
         R = hq - ht
         lhs = np.abs(delta - lam_r * d_prev - R)
+        # first-order rounding of both updates: the decayed term, the write, the new value,
+        # and (quantized side) the offset lambda*s*z folded into the write term
         bound = 3 * U * (np.abs(lam_r * hq_prev) + np.abs(lam_r * hf_prev) + 2 * np.abs(W)
-                         + np.abs(ht) + np.abs(hf)) + 1e-30
+                         + np.abs(ht) + np.abs(hf) + 2 * np.abs(lam_r * sz_prev)) + 1e-30
         assert np.all(lhs <= bound), t
         d_prev = delta
     # the injected residual is the rounding: at most half a step per entry
