@@ -1,0 +1,394 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantized recurrent-state update on one MI355X.
+
+Default workload (the headline): one decode token of a Mamba-2 370m-shaped
+stack -- 48 layers x 32 heads x 64 x 128, batch 256, int4 asymmetric state
+with a per-row fp32 scale and zero point, from a seeded random state
+(N(0,1) rows, 5% of rows x20).  A "step" is one token through all 48
+layers: 48 ssq_decode_step launches, captured once in a hipGraph and
+replayed.  Inputs are resident in HBM before the timed region starts.
+
+Prints ONE JSON line: state-update throughput (GB/s of algorithmic bytes:
+every state byte read and written once, plus x, y, dt, B, C), its fraction
+of the 8 TB/s HBM peak, decode steps/s, the roofline of the dominant kernel
+(per-launch duration from HIP events on the launch stream) and the CPU
+oracle timed on a bounded sample on the host.
+
+Other workloads (--workload) cover the remaining benchmark shapes; they
+print the same schema.
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "state-update GB/s + % of HBM peak; decode steps/s at batch 256"
+HBM_PEAK_GBPS = 8000.0
+
+WORKLOADS = {
+    # name: kind, layers, batch, heads, rows_per_head, format, init, tokens (scan), instances
+    "m2_370m_int4": dict(kind="m2", layers=48, B=256, H=32, P=64, fmt="int4_asym", init="random",
+                         desc="Mamba-2 370m-shaped decode step: 48 layers x 32 heads x 64 x 128, batch 256, "
+                              "int4 asymmetric state (per-row fp32 scale + zero point), seeded random state "
+                              "with 5% x20 outlier rows"),
+    "delta_int8": dict(kind="delta", layers=30, B=256, H=32, P=128, fmt="int8_asym", init="random",
+                       desc="Delta-rule (GDN/KDA-style) decode step: 30 layers x 32 heads x 128 x 128, batch 256, "
+                            "int8 asymmetric per-row state, seeded random state with 5% x20 outlier rows"),
+    "m2_8b_int8sym": dict(kind="m2", layers=8, B=256, H=128, P=64, fmt="int8_sym", init="zero", rotate=True,
+                          desc="Mamba-2 8B-shaped decode layer: 128 heads x 64 x 128, batch 256, int8 symmetric; "
+                               "8 state instances in rotation so that the state is not cache resident"),
+    "m2_8b_int4": dict(kind="m2", layers=8, B=256, H=128, P=64, fmt="int4_asym", init="zero", rotate=True,
+                       desc="Mamba-2 8B-shaped decode layer: 128 heads x 64 x 128, batch 256, int4 asymmetric; "
+                            "8 state instances in rotation so that the state is not cache resident"),
+    "m2_130m_scan_int8asym": dict(kind="scan", layers=24, B=32, H=24, P=64, fmt="int8_asym", init="zero", T=2048,
+                                  desc="Mamba-2 130m-shaped stack: 24 layers x 24 heads x 64 x 128, batch 32, "
+                                       "2048-token scan per layer, int8 asymmetric state rounded every token"),
+    "m2_130m_scan_int8sym": dict(kind="scan", layers=24, B=32, H=24, P=64, fmt="int8_sym", init="zero", T=2048,
+                                 desc="as m2_130m_scan_int8asym with the int8 symmetric grid"),
+    "m2_130m_scan_fp32": dict(kind="scan", layers=24, B=32, H=24, P=64, fmt="fp32", init="zero", T=2048,
+                              desc="as m2_130m_scan_int8asym with the fp32 control state"),
+    "m2_8b_scan_int8sym": dict(kind="scan", layers=1, B=8, H=128, P=64, fmt="int8_sym", init="zero", T=8192,
+                               desc="Mamba-2 8B-shaped layer: batch 8, 8192-token scan, int8 symmetric, state "
+                                    "rounded every token"),
+    "m2_8b_scan_int4": dict(kind="scan", layers=1, B=8, H=128, P=64, fmt="int4_asym", init="zero", T=8192,
+                            desc="Mamba-2 8B-shaped layer: batch 8, 8192-token scan, int4 asymmetric"),
+}
+
+KERNEL_NAMES = {"m2": "k_m2_step", "delta": "k_delta_step", "scan": "k_m2_scan"}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default depends on the workload)")
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="m2_370m_int4", choices=sorted(WORKLOADS))
+    ap.add_argument("--eager", action="store_true", help="time back-to-back launches instead of graph replays")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--seed", type=int, default=2)
+    return ap.parse_args()
+
+
+def src_hash() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "mamba_decode_amd", "csrc", "*"))):
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only: the state update needs no inter-GPU exchange and every "
+              f"box here has one GPU (asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mamba_decode_amd as ssq
+    import synth
+
+    wl = WORKLOADS[args.workload]
+    kind = wl["kind"]
+    steps = args.steps if args.steps is not None else (3 if kind == "scan" else 100)
+    warmup = args.warmup if args.warmup is not None else (1 if kind == "scan" else 10)
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    L, B, H, P, fmt = wl["layers"], wl["B"], wl["H"], wl["P"], wl["fmt"]
+    N = 128
+    T = wl.get("T", 1)
+    rows = B * H * P
+    fmt_id = ssq.FORMAT_NAMES[fmt]
+    skind = ssq.SSQ_DELTA if kind == "delta" else ssq.SSQ_MAMBA2
+    desc = ssq.make_desc(skind, fmt, B, H, P, N)
+    lay = ssq.ssq_state_layout(desc)
+    meta = 0 if fmt == "fp32" else (8 if fmt.endswith("asym") else 4)
+    state_bytes_layer = 2 * rows * (lay.row_bytes + meta)  # read once + written once
+    log(f"[bench] workload {args.workload}: {L} layer(s), {rows} rows/layer, {fmt}, "
+        f"{lay.total_bytes / 2**20:.1f} MiB state/layer")
+
+    # ---------------- states (seeded random or zero), resident in HBM ----------------
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed)
+    states, storages = [], []
+    for layer in range(L):
+        storage = torch.empty(lay.total_bytes, dtype=torch.uint8, device=dev)
+        if wl["init"] == "random":
+            h = torch.randn(rows, N, generator=gen, device=dev)
+            out = torch.rand(rows, 1, generator=gen, device=dev) < 0.05
+            h = torch.where(out, h * 20.0, h).contiguous()
+            st = ssq.ssq_alloc_state(desc, storage=storage, init=h)
+            torch.cuda.synchronize()
+            del h, out
+        else:
+            st = ssq.ssq_alloc_state(desc, storage=storage)
+        states.append(st)
+        storages.append(storage)
+    torch.cuda.synchronize()
+
+    # ---------------- inputs (synth, seeded), resident in HBM ----------------
+    import ctypes
+    vp = ctypes.c_void_p
+    ins, calls = [], []
+    if kind == "m2":
+        for layer in range(L):
+            x, dt, Bm, Cm, A, D = synth.mamba2_step_inputs(args.seed, layer, B, H, 1, P, N)
+            t = [torch.from_numpy(a).to(dev) for a in (x, dt, A, Bm, Cm, D)]
+            y = torch.empty(rows, device=dev)
+            ins.append((t, y))
+        io_bytes = 4 * (rows * 2 + B * H + 2 * B * N + 2 * H)
+
+        def launch(layer, stream):
+            (x, dt, A, Bm, Cm, D), y = ins[layer]
+            return ssq.lib.ssq_decode_step(states[layer].handle, vp(x.data_ptr()), vp(dt.data_ptr()),
+                                           vp(A.data_ptr()), vp(Bm.data_ptr()), vp(Cm.data_ptr()),
+                                           vp(D.data_ptr()), vp(y.data_ptr()), 0, stream)
+    elif kind == "delta":
+        for layer in range(L):
+            q, k, v, al, be = synth.delta_inputs(args.seed, layer, B, H, P, N)
+            t = [torch.from_numpy(a).to(dev) for a in (q, k, v, al, be)]
+            o = torch.empty(B * H * N, device=dev)
+            ins.append((t, o))
+        io_bytes = 4 * (B * H * (2 * P + 2 * N) + 2 * B * H)
+
+        def launch(layer, stream):
+            (q, k, v, al, be), o = ins[layer]
+            return ssq.lib.ssq_delta_step(states[layer].handle, vp(q.data_ptr()), vp(k.data_ptr()),
+                                          vp(v.data_ptr()), vp(al.data_ptr()), vp(be.data_ptr()),
+                                          vp(o.data_ptr()), 0, stream)
+    else:  # scan: one layer's inputs drawn on the device, shared by every layer
+        g2 = torch.Generator(device=dev)
+        g2.manual_seed(args.seed + 1)
+        A_np, D_np, bias = synth.mamba2_head_params(args.seed, 0, H)
+        x = torch.randn(B, T, H, P, generator=g2, device=dev)
+        dtn = torch.randn(B, T, H, generator=g2, device=dev, dtype=torch.float64)
+        dt = torch.nn.functional.softplus(dtn + torch.from_numpy(bias).to(dev)).float().contiguous()
+        Bm = (torch.randn(B, T, 1, N, generator=g2, device=dev) / N ** 0.5).contiguous()
+        Cm = (torch.randn(B, T, 1, N, generator=g2, device=dev) / N ** 0.5).contiguous()
+        A = torch.from_numpy(A_np).to(dev)
+        D = torch.from_numpy(D_np).to(dev)
+        y = torch.empty_like(x)
+        ins.append(((x, dt, A, Bm, Cm, D), y))
+        io_bytes = 4 * (2 * rows * T + B * T * H + 2 * B * T * N + 2 * H)
+
+        def launch(layer, stream):
+            (x, dt, A, Bm, Cm, D), y = ins[0]
+            return ssq.lib.ssq_scan(states[layer].handle, T, vp(x.data_ptr()), vp(dt.data_ptr()),
+                                    vp(A.data_ptr()), vp(Bm.data_ptr()), vp(Cm.data_ptr()),
+                                    vp(D.data_ptr()), vp(y.data_ptr()), 0, stream)
+    torch.cuda.synchronize()
+    bytes_per_launch = (state_bytes_layer if kind != "scan" else 0) + io_bytes
+
+    def run_step():
+        s = vp(torch.cuda.current_stream().cuda_stream)
+        for layer in range(L):
+            rc = launch(layer, s)
+            if rc != 0:
+                raise RuntimeError(f"launch failed: {ssq.ssq_last_error()}")
+
+    # ---------------- graph capture of one step ----------------
+    use_graph = not args.eager and kind != "scan"
+    graph = None
+    if use_graph:
+        run_step()  # warm the launch path before capture
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            run_step()
+        torch.cuda.synchronize()
+
+    def do_step():
+        if graph is not None:
+            graph.replay()
+        else:
+            run_step()
+
+    log(f"[bench] warmup {warmup} step(s)")
+    for _ in range(warmup):
+        do_step()
+    torch.cuda.synchronize()
+
+    # ---------------- timed region ----------------
+    log(f"[bench] timing {steps} step(s)")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        do_step()
+    e1.record()
+    e1.synchronize()
+    torch.cuda.synchronize()
+    ms_total = e0.elapsed_time(e1)
+    ms_per_step = ms_total / steps
+
+    # ---------------- eager per-launch time (events around each launch, same stream): context ----------------
+    kreps = max(1, min(steps, 20 if kind != "scan" else 2))
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(kreps * L)]
+    s = vp(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    i = 0
+    for _ in range(kreps):
+        for layer in range(L):
+            evs[i][0].record()
+            launch(layer, s)
+            evs[i][1].record()
+            i += 1
+    torch.cuda.synchronize()
+    kms = [a.elapsed_time(b) for a, b in evs]
+    eager_ms_median = float(np.median(kms))
+    # every launch of a step runs the dominant kernel, so its average duration over the
+    # timed region is the step time over the launches per step (gaps between launches
+    # included, which makes the figure conservative)
+    kernel_ms_mean = ms_per_step / L
+
+    # ---------------- copy bandwidth in the same run (context) ----------------
+    nbytes = 1 << 30
+    src = torch.empty(nbytes // 4, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    c1.record()
+    c1.synchronize()
+    copy_gbps = 2 * nbytes * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del src, dst
+
+    total_bytes_step = bytes_per_launch * L
+    value = total_bytes_step / (ms_per_step * 1e-3) / 1e9
+    state_gbps = state_bytes_layer * L / (ms_per_step * 1e-3) / 1e9 if kind != "scan" else None
+    achieved = bytes_per_launch / (kernel_ms_mean * 1e-3) / 1e9
+
+    # traffic from the committed rocprofv3 counter runs, only while the kernels are unchanged
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(tpath):
+        tr = json.load(open(tpath)).get(args.workload)
+        if tr and tr.get("src_hash") == src_hash():
+            traffic = tr.get("hbm_bytes_per_launch")
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": wl["desc"],
+            "name": args.workload,
+            "layers": L, "batch": B, "heads": H, "rows_per_head": P, "row_len": N, "format": fmt,
+            "tokens": T if kind == "scan" else 1,
+            "launch": ("hipGraph replay of " if graph is not None else "back-to-back launches of ")
+                      + f"{L} per-layer kernels per step",
+            "parallelism": "single GPU",
+        },
+        "hbm_frac": round(value / HBM_PEAK_GBPS, 4),
+        # a rotated workload times one layer on several state instances: each launch is one token
+        "decode_steps_per_s": (round(1000.0 * (L if wl.get("rotate") else 1) / ms_per_step, 2)
+                               if kind != "scan" else None),
+        "tokens_per_s": round(B * T / (ms_per_step * 1e-3 / L), 1) if kind == "scan" else None,
+        "state_GBps": round(state_gbps, 2) if state_gbps else None,
+        "copy_GBps": round(copy_gbps, 1),
+        "frac_of_copy": round(value / copy_gbps, 4),
+        "roofline": {
+            "bound": "hbm" if kind != "scan" else "alu",
+            "kernel": KERNEL_NAMES[kind] + f"<{fmt}>",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "bytes_per_launch": bytes_per_launch,
+            "kernel_ms_mean": round(kernel_ms_mean, 5),
+            "kernel_ms_source": "HIP events around the timed region, step time / launches per step",
+            "eager_launch_ms_median": round(eager_ms_median, 5),
+        },
+        "device": torch.cuda.get_device_name(0),
+    }
+    if kind == "scan":
+        # VALU roofline: lane-operations are not counted by the bench; report element updates/s
+        rec["roofline"]["element_updates_per_s"] = rows * N * T / (kernel_ms_mean * 1e-3)
+
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(args, wl, bytes_per_launch, rows)
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(args, wl, bytes_per_launch, rows_per_layer):
+    """The oracle as it stands, single-threaded, on a bounded sample of the same workload."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    kind, fmt, B, H, P, N = wl["kind"], wl["fmt"], wl["B"], wl["H"], wl["P"], 128
+    if kind == "delta":
+        nmat = 64
+        init = synth.init_state(args.seed, 0, nmat * P, N)
+        st = oracle.make_state(fmt, nmat * P, N, init)
+        q, k, v, al, be = synth.delta_inputs(args.seed, 0, 1, nmat, P, N)
+        done, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < args.cpu_seconds:
+            oracle.delta_step(st, q, k, v, al, be, 1, nmat)
+            done += nmat * P
+        sample = f"{nmat} matrices (128 x 128, {fmt}) of the delta layer, one step per call"
+    else:
+        R = 32768
+        srows = np.arange(R, dtype=np.int64)
+        init = synth.init_state_rows(args.seed, 0, srows, N) if wl["init"] == "random" else None
+        st = oracle.make_state(fmt, R, N, init)
+        T = 1
+        x, dt, Bm, Cm, A, D = synth.mamba2_rows_scan_inputs(args.seed, 0, B, T, H, 1, P, N, srows)
+        done, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < args.cpu_seconds:
+            oracle.mamba2_rows_scan(st, x, dt, A, Bm, Cm, D)
+            done += R
+        sample = f"{R} rows ({fmt}) of layer 0, one token per call"
+    el = time.perf_counter() - t0
+    rows_per_s = done / el  # row updates (one row, one token) per second
+    gbps = rows_per_s * (bytes_per_launch / (rows_per_layer * wl.get("T", 1))) / 1e9
+    out = {"value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "sample": sample + f", repeated for {el:.1f} s", "rows_per_s": round(rows_per_s, 1),
+           "cpu": _cpu_model()}
+    if kind != "scan":
+        layers = 1 if wl.get("rotate") else wl["layers"]
+        out["decode_steps_per_s"] = round(rows_per_s / (rows_per_layer * layers), 5)
+    return out
+
+
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+if __name__ == "__main__":
+    main()

@@ -38,21 +38,22 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, out: str = LIB, defines=(), build_dir: str = BUILD_DIR) -> str:
+    """Compile every source and link ``out``; ``defines`` are extra -D tuning macros."""
+    os.makedirs(build_dir, exist_ok=True)
     procs = []
     objs = []
     for src in SOURCES:
-        obj = os.path.join(BUILD_DIR, src.rsplit(".", 1)[0] + ".o")
+        obj = os.path.join(build_dir, src.rsplit(".", 1)[0] + ".o")
         objs.append(obj)
-        cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
     failed = []
     for src, p in procs:
-        out, _ = p.communicate()
-        text = out.decode(errors="replace")
+        log, _ = p.communicate()
+        text = log.decode(errors="replace")
         # the host pass does not know the gfx950 feature name: that warning is harmless
         lines = [ln for ln in text.splitlines() if "packed-fp32-ops" not in ln]
         if p.returncode != 0:
@@ -62,13 +63,13 @@ def build(verbose: bool = False) -> str:
             print("\n".join(lines))
     if failed:
         raise RuntimeError(f"hipcc failed for {failed}")
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -15,8 +15,8 @@
 // min/max and refit use DPP only.  The two column reductions (u = k^T S before
 // the update and o = S'^T q after it) cross rows: every thread reduces its four
 // rows in registers, then the 32 partial rows meet in LDS.  u is accumulated in
-// double from exact products and rounded once, so it does not depend on the
-// reduction order; o is an output only.  The whole matrix (16 KiB of int8
+// double and rounded once, so its reduction order only matters where the sum
+// lies within double rounding of an fp32 midpoint; o is an output only.  The whole matrix (16 KiB of int8
 // codes) is read once and written once: the kernel is bound by HBM traffic.
 #include "ssq_device.h"
 #include "ssq_internal.h"
@@ -50,13 +50,9 @@ __global__ __launch_bounds__(256) void k_delta_step(DeltaArgs a)
         if constexpr (Tr::quant) {
             uint32_t cw[NW];
             load_words<NW>(a.codes + row * ROWB + part * (NW * 4), cw);
-            unpack_codes<F, E>(cw, S[r]);
+            unpack_codes<F, E>(cw, S[r]); // the codes c_ij as floats
             s_old[r] = a.scale[row];
             z_old[r] = Tr::asym ? a.zero[row] : 0.0f;
-            if constexpr (Tr::asym) {
-#pragma unroll
-                for (int e = 0; e < E; ++e) S[r][e] = S[r][e] - z_old[r]; // d = fl(c - z)
-            }
         } else {
             load_f32<E>(a.h32 + row * 128 + j0, S[r]);
             s_old[r] = 1.0f;
@@ -66,11 +62,17 @@ __global__ __launch_bounds__(256) void k_delta_step(DeltaArgs a)
     float vv[E];
     load_f32<E>(a.v + mrow0 + j0, vv);
 
-    // u = k^T S: exact products k_i*s_i*d_ij (quantized) or k_i*S_ij summed in double
+    // u = k^T S in double: sum_i kap_i*c_ij - sum_i kap_i*z_i with kap_i = k_i*s_i exact
+    // (quantized), or sum_i k_i*S_ij (fp32); the z term is the same for every column
     {
         double up[E];
+        double zt = 0.0;
+        if constexpr (Tr::asym) {
 #pragma unroll
-        for (int e = 0; e < E; ++e) up[e] = 0.0;
+            for (int r = 0; r < KR; ++r) zt = __builtin_fma((double)kk[r] * (double)s_old[r], (double)z_old[r], zt);
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) up[e] = -zt;
 #pragma unroll
         for (int r = 0; r < KR; ++r) {
             const double kap = Tr::quant ? (double)kk[r] * (double)s_old[r] : (double)kk[r];
@@ -105,11 +107,18 @@ __global__ __launch_bounds__(256) void k_delta_step(DeltaArgs a)
 #pragma unroll
     for (int r = 0; r < KR; ++r) {
         const int64_t row = mrow0 + rg + RG * r;
-        const float as = Tr::quant ? alpha * s_old[r] : alpha;
+        if constexpr (Tr::quant) {
+            // alpha*s*(c - z) + k*w = fma(as, c, fma(k, w, -as*z)): the decay acts on the scale
+            const float as = alpha * s_old[r];
+            const float az = as * z_old[r];
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const float kw = kk[r] * ww[e];
-            S[r][e] = __builtin_fmaf(as, S[r][e], kw);
+            for (int e = 0; e < E; ++e) S[r][e] = __builtin_fmaf(as, S[r][e], __builtin_fmaf(kk[r], ww[e], -az));
+        } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const float kw = kk[r] * ww[e];
+                S[r][e] = __builtin_fmaf(alpha, S[r][e], kw);
+            }
         }
         if constexpr (!Tr::quant || PRE) {
 #pragma unroll
@@ -132,10 +141,16 @@ __global__ __launch_bounds__(256) void k_delta_step(DeltaArgs a)
                 for (int e = 0; e < E; ++e) am = fmaxf(am, fabsf(S[r][e]));
                 am = group_max<LPR>(am);
             }
-            const RowGrid g = refit<F>(mn, mx, am);
-            const bool slow_any = Tr::asym && __any(g.slow);
+            RowGrid g;
             float f[E];
-            round_codes<F, E>(S[r], g, slow_any, f);
+            if (__all(refit_fast<F>(mn, mx, am, g))) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) f[e] = __builtin_fmaf(S[r][e], g.inv, g.Mz);
+            } else {
+                g = refit<F>(mn, mx, am);
+                const bool slow_any = Tr::asym && __any(g.slow);
+                round_codes<F, E>(S[r], g, slow_any, f);
+            }
             uint32_t ow[NW];
             pack_codes<F, E>(f, ow);
             store_words<NW>(a.codes + row * ROWB + part * (NW * 4), ow);

@@ -8,18 +8,19 @@
 // Evaluation order (identical in every kernel, so that the decode step, the
 // scan and the state initialisation round the same way):
 //   lambda  = fl32(exp_double(fl(dt*A)))
-//   h'_n    = fma(fl(lambda*s), fl(c_n - z), fl(w*B_n)),  w = fl(dt*x)
+//   ls      = fl(lambda*s),  w = fl(dt*x)
+//   h'_n    = fma(ls, c_n, fma(w, B_n, -fl(ls*z)))   (z = 0: symmetric grid)
 //   refit   (asymmetric) s' = fl(fl(mx-mn)/(2^b-1)), inv = fl(1/s'),
-//           z' = -rne(fl(mn*inv));  (symmetric) s' = fl(amax/(2^(b-1)-1))
-//   code    = clamp(rne(fl(h'*inv) + z')), the sum exact, ties to the even code
+//           z' = -rne(mn*inv);  (symmetric) s' = fl(amax/(2^(b-1)-1))
+//   code    = clamp(rne(h'*inv + z')), the product exact, ties to the even code
 //
-// The rounding uses the 1.5*2^23 trick: for |t| < 2^22, fl(t + 1.5*2^23) is
-// 1.5*2^23 + rne(t) exactly, because floats in [2^23, 2^24) are the integers.
-// Adding z' to the constant first (exact while |z'| < 2^21) rounds the exact
-// sum v + z'.  Rows with |z'| >= 2^21 (a spread below ~2^-13 of the row's
-// offset) take a slow path in which v + z' is exact by Sterbenz's lemma.
-// The clamped value's bit pattern minus that of 1.5*2^23 is the code itself,
-// so packing needs no float-to-int conversion.
+// The rounding uses the 1.5*2^23 trick: floats in [2^23, 2^24) are the
+// integers, so fma(h, inv, 1.5*2^23 + z) is 1.5*2^23 + rne(h*inv + z) for the
+// exact product, as long as 1.5*2^23 + z is exact (|z| < 2^21 here).  Rows
+// with |z| >= 2^21 (a spread below ~2^-13 of the row's offset) take a slow
+// path in double, where h*inv + z is exact by Sterbenz's lemma.  The clamped
+// value's bit pattern minus that of 1.5*2^23 is the code itself, so packing
+// needs no float-to-int conversion.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -94,6 +95,15 @@ __device__ __forceinline__ float group_sum(float v)
     return v;
 }
 
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left alone).  Used at the end of a rarely
+// taken block that loads, so that nothing from that block is still pending where the
+// paths merge: otherwise the merge point itself must wait for every outstanding
+// vector memory operation, which on this counter includes the ring's prefetches.
+__device__ __forceinline__ void wait_vmem_all()
+{
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
 __device__ __forceinline__ float readlane_f(float v, int lane)
 {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
@@ -114,6 +124,16 @@ __device__ __forceinline__ float ubyte_f(uint32_t w, int k)
     return (float)((w >> (8 * k)) & 0xFFu); // v_cvt_f32_ubyte{k}
 }
 
+// v_and_b32 the compiler cannot see through: with a visible mask it folds the
+// shift-and-mask of each nibble into v_bfe_u32 + v_cvt_f32_ubyte0 (two ops);
+// hidden, every byte converts with a single v_cvt_f32_ubyte{k}
+__device__ __forceinline__ uint32_t and_0f(uint32_t w)
+{
+    uint32_t r;
+    asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(r) : "v"(w));
+    return r;
+}
+
 // c_n as float (sym: the signed code; asym: 0..2^b-1)
 template <int F, int E>
 __device__ __forceinline__ void unpack_codes(const uint32_t* w, float* c)
@@ -131,7 +151,7 @@ __device__ __forceinline__ void unpack_codes(const uint32_t* w, float* c)
     } else if constexpr (F == INT4_ASYM) {
 #pragma unroll
         for (int i = 0; i < E / 8; ++i) {
-            const uint32_t lo = w[i] & 0x0F0F0F0Fu, hi = (w[i] >> 4) & 0x0F0F0F0Fu;
+            const uint32_t lo = and_0f(w[i]), hi = and_0f(w[i] >> 4);
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 c[8 * i + 2 * k] = ubyte_f(lo, k);
@@ -143,7 +163,7 @@ __device__ __forceinline__ void unpack_codes(const uint32_t* w, float* c)
 #pragma unroll
         for (int i = 0; i < E / 8; ++i) {
             const uint32_t b = w[i] ^ 0x88888888u;
-            const uint32_t lo = b & 0x0F0F0F0Fu, hi = (b >> 4) & 0x0F0F0F0Fu;
+            const uint32_t lo = and_0f(b), hi = and_0f(b >> 4);
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 c[8 * i + 2 * k] = ubyte_f(lo, k) - 8.0f;
@@ -211,15 +231,15 @@ __device__ __forceinline__ RowGrid refit(float mn, float mx, float amax)
         if (!(s >= kFltMin)) {
             // the row is kept as the constant mn: s = |mn|, z = -sign(mn), codes 0
             g.s = fabsf(mn);
-            g.z = -(mn > 0.0f ? 1.0f : (mn < 0.0f ? -1.0f : 0.0f));
+            g.z = -(mn > 0.0f ? 1.0f : (mn < 0.0f ? -1.0f : 0.0f)) + 0.0f; // a zero zero point is +0
             g.inv = 0.0f;
             g.zc = 0.0f;
             g.zadj = g.z;
             g.Mz = kMagic;
         } else {
             const float inv = 1.0f / s;
-            const float vmin = mn * inv;
-            const float z = -rintf(vmin);
+            // the product of two floats is exact in double; rint rounds half to even
+            const float z = -(float)rint((double)mn * (double)inv) + 0.0f; // +0, never -0
             g.s = s;
             g.z = z;
             g.inv = inv;
@@ -244,7 +264,7 @@ __device__ __forceinline__ RowGrid refit(float mn, float mx, float amax)
     return g;
 }
 
-// f = 1.5*2^23 + clamp(rne(fl(h*inv) + z)) for E entries; `slow_any` is wave-uniform
+// f = 1.5*2^23 + clamp(rne(h*inv + z)) for E entries; `slow_any` is wave-uniform
 template <int F, int E>
 __device__ __forceinline__ void round_codes(const float* h, const RowGrid& g, bool slow_any, float* f)
 {
@@ -252,17 +272,80 @@ __device__ __forceinline__ void round_codes(const float* h, const RowGrid& g, bo
     constexpr float fhi = kMagic + (float)Traits<F>::hi;
     if (!slow_any) {
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const float v = h[e] * g.inv;
-            f[e] = __builtin_amdgcn_fmed3f(v + g.Mz, flo, fhi);
-        }
+        for (int e = 0; e < E; ++e) f[e] = __builtin_amdgcn_fmed3f(__builtin_fmaf(h[e], g.inv, g.Mz), flo, fhi);
     } else {
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-            const float v = h[e] * g.inv;
-            const float t = g.slow ? kMagic + rintf(v + g.zc) : v + g.Mz;
+            float t;
+            if (g.slow) {
+                // h*inv + z is exact in double here: h*inv lies within Qa+1 of -z and |z| >= 2^21
+                const double p = (double)h[e] * (double)g.inv + (double)g.zc;
+                t = kMagic + (float)rint(p);
+            } else {
+                t = __builtin_fmaf(h[e], g.inv, g.Mz);
+            }
             f[e] = __builtin_amdgcn_fmed3f(t, flo, fhi);
         }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fast refit: the same s, inv and z as refit(), with fewer instructions, for
+// rows inside the ranges where the shortcuts were verified exhaustively
+// (every fp32 mantissa, against IEEE division):
+//   a / Qa    = fma(fma(-q, Qa, a), r, q), q = a*r, r = RN(1/Qa)  (normal a/Qa)
+//   1 / s     = fma(fma(-s, y, 1), y, y),  y = v_rcp_f32(s)       (2^-126 < 1/s)
+//   rne(mn*inv) = fma(mn, inv, 1.5*2^23) - 1.5*2^23               (|mn*inv| < 2^22)
+// It also checks that no code leaves its range, so the rounding needs no
+// clamp: the bottom asymmetric code is 0 by construction and the largest entry
+// is the only one that can pass the top.  A row outside these conditions makes
+// its wave take refit() and round_codes() instead.
+// ---------------------------------------------------------------------------
+template <int Q>
+__device__ __forceinline__ float div_by_const(float a)
+{
+    constexpr float qf = (float)Q;
+    constexpr float r = 1.0f / (float)Q;
+    const float q = a * r;
+    return __builtin_fmaf(__builtin_fmaf(-q, qf, a), r, q);
+}
+
+__device__ __forceinline__ float recip_rn(float s)
+{
+    const float y = __builtin_amdgcn_rcpf(s);
+    return __builtin_fmaf(__builtin_fmaf(-s, y, 1.0f), y, y);
+}
+
+template <int F>
+__device__ __forceinline__ bool refit_fast(float mn, float mx, float amax, RowGrid& g)
+{
+    constexpr float lo_ok = 7.88860905e-31f; // 2^-100
+    constexpr float hi_ok = 1.26765060e+30f; // 2^100
+    g.slow = false;
+    g.zadj = 0.0f;
+    if constexpr (Traits<F>::asym) {
+        const float range = mx - mn;
+        const float s = div_by_const<Traits<F>::hi>(range);
+        const float inv = recip_rn(s);
+        const float z = kMagic - __builtin_fmaf(mn, inv, kMagic) + 0.0f;
+        g.s = s;
+        g.z = z;
+        g.inv = inv;
+        g.zc = z;
+        g.Mz = kMagic + z;
+        const float top = __builtin_fmaf(mx, inv, g.Mz);
+        return range >= lo_ok && range <= hi_ok && fabsf(z) < kSlowZero &&
+               top <= kMagic + (float)Traits<F>::hi;
+    } else {
+        const float s = div_by_const<Traits<F>::hi>(amax);
+        const float inv = recip_rn(s);
+        g.s = s;
+        g.z = 0.0f;
+        g.inv = inv;
+        g.zc = 0.0f;
+        g.Mz = kMagic;
+        const float top = __builtin_fmaf(amax, inv, kMagic);
+        return amax >= lo_ok && amax <= hi_ok && top <= kMagic + (float)Traits<F>::hi;
     }
 }
 
@@ -275,21 +358,49 @@ __device__ __forceinline__ float code_minus_z(float f, const RowGrid& g)
 // ---------------------------------------------------------------------------
 // vector memory helpers: NW consecutive 32-bit words at a 4*NW-byte aligned address
 // ---------------------------------------------------------------------------
+// The state is streamed: every byte is read once and written once per step.
+// With SSQ_NT the state's loads and stores carry the non-temporal hint.
+#ifndef SSQ_NT
+#define SSQ_NT 1
+#endif
+
+template <typename T>
+__device__ __forceinline__ T ld_stream(const T* p)
+{
+#if SSQ_NT
+    return __builtin_nontemporal_load(p);
+#else
+    return *p;
+#endif
+}
+template <typename T>
+__device__ __forceinline__ void st_stream(T* p, T v)
+{
+#if SSQ_NT
+    __builtin_nontemporal_store(v, p);
+#else
+    *p = v;
+#endif
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
 template <int NW>
 __device__ __forceinline__ void load_words(const void* p, uint32_t* w)
 {
     if constexpr (NW % 4 == 0) {
 #pragma unroll
         for (int i = 0; i < NW / 4; ++i) {
-            const uint4 v = reinterpret_cast<const uint4*>(p)[i];
+            const u32x4 v = ld_stream(reinterpret_cast<const u32x4*>(p) + i);
             w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
         }
     } else if constexpr (NW == 2) {
-        const uint2 v = *reinterpret_cast<const uint2*>(p);
+        const u32x2 v = ld_stream(reinterpret_cast<const u32x2*>(p));
         w[0] = v.x; w[1] = v.y;
     } else {
         static_assert(NW == 1, "unsupported lane width");
-        w[0] = *reinterpret_cast<const uint32_t*>(p);
+        w[0] = ld_stream(reinterpret_cast<const uint32_t*>(p));
     }
 }
 
@@ -298,12 +409,15 @@ __device__ __forceinline__ void store_words(void* p, const uint32_t* w)
 {
     if constexpr (NW % 4 == 0) {
 #pragma unroll
-        for (int i = 0; i < NW / 4; ++i)
-            reinterpret_cast<uint4*>(p)[i] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+        for (int i = 0; i < NW / 4; ++i) {
+            const u32x4 v = {w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+            st_stream(reinterpret_cast<u32x4*>(p) + i, v);
+        }
     } else if constexpr (NW == 2) {
-        *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
+        const u32x2 v = {w[0], w[1]};
+        st_stream(reinterpret_cast<u32x2*>(p), v);
     } else {
-        *reinterpret_cast<uint32_t*>(p) = w[0];
+        st_stream(reinterpret_cast<uint32_t*>(p), w[0]);
     }
 }
 

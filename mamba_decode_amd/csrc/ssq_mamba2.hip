@@ -34,33 +34,46 @@ __device__ __forceinline__ int64_t wave_id()
 }
 
 // ---------------------------------------------------------------------------
-// one row, one token: dequantize, decay + write, refit, round, pack.
-// Returns the lane's share of the readout sum (before the group reduction).
+// one row, one token: dequantize, decay + write, refit, round, pack, read out.
 // ---------------------------------------------------------------------------
 template <int F, int LPR, bool PRE>
 struct RowStep {
     static constexpr int E = 128 / LPR;
     static constexpr int NW = Traits<F>::quant ? E * Traits<F>::bits / 32 : E;
 
-    // quantized formats: cw in -> ow out, s/z in -> grid out
-    __device__ __forceinline__ static float run_q(const uint32_t* cw, float s_old, float z_old, float lam,
-                                                  float w, const float* Bv, const float* Cv, uint32_t* ow,
-                                                  RowGrid& g, bool& slow_any)
+    // B and C of the current (sequence, group): E consecutive entries each
+    struct RowIn {
+        float B[E];
+        float C[E];
+        __device__ __forceinline__ void load(const float* Bp, const float* Cp)
+        {
+            load_f32<E>(Bp, B);
+            load_f32<E>(Cp, C);
+        }
+    };
+
+    // quantized formats: the old codes as floats (h, overwritten) in -> the new packed codes
+    // ow out; returns y (valid in every lane of the row).  ls = fl(lambda*s) and
+    // lz = fl(ls*z) of the old row, w = fl(dt*x), dx = fl(D*x).
+    __device__ __forceinline__ static float run_q(float* h, float ls, float lz, float w, float dx,
+                                                  const RowIn& in, uint32_t* ow, RowGrid& g)
     {
         using Tr = Traits<F>;
-        float h[E];
-        unpack_codes<F, E>(cw, h);
-        const float ls = lam * s_old;
+        // lambda*s*(c - z) + w*B = fma(ls, c, fma(w, B, -ls*z)): the decay acts on the scale
+        if constexpr (Tr::asym) {
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const float d = Tr::asym ? h[e] - z_old : h[e];
-            const float wb = w * Bv[e];
-            h[e] = __builtin_fmaf(ls, d, wb);
+            for (int e = 0; e < E; ++e) h[e] = __builtin_fmaf(ls, h[e], __builtin_fmaf(w, in.B[e], -lz));
+        } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const float wb = w * in.B[e];
+                h[e] = __builtin_fmaf(ls, h[e], wb);
+            }
         }
         float acc = 0.0f;
         if constexpr (PRE) {
 #pragma unroll
-            for (int e = 0; e < E; ++e) acc = __builtin_fmaf(Cv[e], h[e], acc);
+            for (int e = 0; e < E; ++e) acc = __builtin_fmaf(in.C[e], h[e], acc);
         }
         float mn = 0.0f, mx = 0.0f, am = 0.0f;
         if constexpr (Tr::asym) {
@@ -78,156 +91,173 @@ struct RowStep {
             for (int e = 0; e < E; ++e) am = fmaxf(am, fabsf(h[e]));
             am = group_max<LPR>(am);
         }
-        g = refit<F>(mn, mx, am);
-        slow_any = Tr::asym && __any(g.slow);
-        float f[E];
-        round_codes<F, E>(h, g, slow_any, f);
-        pack_codes<F, E>(f, ow);
-        if constexpr (!PRE) {
-            if (!slow_any) {
+        // h becomes f = 1.5*2^23 + code in place
+        bool slow_any = false;
+        if (__all(refit_fast<F>(mn, mx, am, g))) {
+            // every row of the wave is inside the verified ranges and needs no clamp
 #pragma unroll
-                for (int e = 0; e < E; ++e) acc = __builtin_fmaf(Cv[e], f[e] - g.Mz, acc);
-            } else {
-#pragma unroll
-                for (int e = 0; e < E; ++e) acc = __builtin_fmaf(Cv[e], code_minus_z(f[e], g), acc);
-            }
+            for (int e = 0; e < E; ++e) h[e] = __builtin_fmaf(h[e], g.inv, g.Mz);
+        } else {
+            g = refit<F>(mn, mx, am);
+            slow_any = Tr::asym && __any(g.slow);
+            round_codes<F, E>(h, g, slow_any, h);
         }
-        return acc;
+        pack_codes<F, E>(h, ow);
+        if constexpr (PRE) return group_sum<LPR>(acc) + dx;
+        // y = s * sum_n C_n*(c_n - z) + dx, read from the new codes
+        if (!slow_any) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc = __builtin_fmaf(in.C[e], h[e] - g.Mz, acc);
+        } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc = __builtin_fmaf(in.C[e], code_minus_z(h[e], g), acc);
+        }
+        acc = group_sum<LPR>(acc);
+        if (__any(g.zadj != 0.0f)) {
+            // a degenerate row codes everything as 0 around z = 0 but stands for the constant -z*s
+            float cs = 0.0f;
+#pragma unroll
+            for (int e = 0; e < E; ++e) cs += in.C[e];
+            acc = acc - g.zadj * group_sum<LPR>(cs);
+        }
+        return g.s * acc + dx;
     }
 
-    // fp32 control: hv in/out
-    __device__ __forceinline__ static float run_f(float* hv, float lam, float w, const float* Bv,
-                                                  const float* Cv)
+    // fp32 control: hv in/out, returns y
+    __device__ __forceinline__ static float run_f(float* hv, float lam, float w, float dx, const RowIn& in)
     {
         float acc = 0.0f;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-            const float wb = w * Bv[e];
+            const float wb = w * in.B[e];
             hv[e] = __builtin_fmaf(lam, hv[e], wb);
-            acc = __builtin_fmaf(Cv[e], hv[e], acc);
+            acc = __builtin_fmaf(in.C[e], hv[e], acc);
         }
-        return acc;
+        return group_sum<LPR>(acc) + dx;
     }
 };
-
-// lane share of sum_n C_n over the row (only needed by degenerate asymmetric rows)
-template <int LPR, int E>
-__device__ __forceinline__ float row_csum(const float* Cv)
-{
-    float cs = 0.0f;
-#pragma unroll
-    for (int e = 0; e < E; ++e) cs += Cv[e];
-    return group_sum<LPR>(cs);
-}
-
-// final readout of a row (value valid in every lane of the row group)
-template <int F, bool PRE>
-__device__ __forceinline__ float row_y(float acc, const RowGrid& g, float csum_if_needed, float dx)
-{
-    if constexpr (!Traits<F>::quant || PRE) return acc + dx;
-    const float t = acc - g.zadj * csum_if_needed;
-    return g.s * t + dx;
-}
 
 // ---------------------------------------------------------------------------
 // decode step
 // ---------------------------------------------------------------------------
-template <int F, int LPR, bool PRE>
-__global__ __launch_bounds__(256) void k_m2_step(M2Args a)
+// Wave w takes iterations [it_base + w*K, it_base + (w+1)*K), all of them
+// valid, as straight-line code: the state words of iteration i + D are loaded
+// while iteration i is processed.  With no loop and no optional store, the
+// compiler's s_waitcnt before each use covers exactly the loads that use needs;
+// a loop-carried prefetch made it wait for younger loads as well.  Every lane
+// of a row stores the row's scale, zero point and y (the same value to the same
+// address), so no store sits behind a branch either.  Leftover iterations (fewer
+// than K) are run by a second launch with K = 1.
+template <int F, int LPR, bool PRE, int K, int D>
+__global__ __launch_bounds__(256) void k_m2_step(M2Args a, int64_t it_base)
 {
     using Tr = Traits<F>;
     using RS = RowStep<F, LPR, PRE>;
     constexpr int E = RS::E, NW = RS::NW, RPW = 64 / LPR, ROWB = RowBytes<F>::value;
+    constexpr int NS = Tr::quant ? NW : E; // registers per slot for the row's words
+    constexpr int DD = D < K ? D : K;
     const int lane = threadIdx.x & 63, sub = lane / LPR, part = lane % LPR;
-    const int64_t it0 = wave_id() * a.iters_per_wave;
-    if (it0 >= a.total_iters) return;
-    const int64_t it1 = min(it0 + (int64_t)a.iters_per_wave, a.total_iters);
+    const int64_t it0 = it_base + wave_id() * K;
+    if (it0 + K > a.total_iters) return;
+
+    const int ipH = a.P / RPW; // iterations per head (RPW divides P)
+    int64_t bh = it0 / ipH;
+    int jh = (int)(it0 - bh * ipH);
+    int h = (int)(bh % a.H);
+    int64_t b = bh / a.H;
     const int64_t nbh = (int64_t)a.Bsz * a.H;
-    const int64_t bh0 = (it0 * RPW) / a.P;
-
-    // decay of up to 64 heads, one per lane
-    float dt_l = 0.0f, lam_l = 0.0f;
-    if (bh0 + lane < nbh) {
-        const int64_t bh = bh0 + lane;
-        dt_l = a.dt[bh];
-        lam_l = decay(dt_l, a.A[bh % a.H]);
-    }
     const int hpg = a.H / a.G;
-    int64_t key = -1;
-    float Bv[E], Cv[E];
+    int gi = h / hpg, hg = h - gi * hpg; // B/C group of head h and the head's place in it
 
-    // state of the current row (prefetched one iteration ahead)
-    uint32_t cw[NW];
-    float hv[Tr::quant ? 1 : E];
-    float s_old = 0.0f, z_old = 0.0f, xv;
-    auto load_row = [&](int64_t it, uint32_t* w, float* hf, float& s, float& z, float& xx) {
+    uint32_t ring[DD][NS];
+    float rs[DD], rz[DD], rx[DD];
+    auto issue = [&](int slot, int64_t it) {
         const int64_t row = it * RPW + sub;
         if constexpr (Tr::quant) {
-            load_words<NW>(a.codes + row * ROWB + part * (NW * 4), w);
-            s = a.scale[row];
-            if constexpr (Tr::asym) z = a.zero[row];
+            load_words<NW>(a.codes + row * ROWB + part * (NW * 4), ring[slot]);
+            rs[slot] = ld_stream(a.scale + row);
+            if constexpr (Tr::asym) rz[slot] = ld_stream(a.zero + row);
+            else rz[slot] = 0.0f;
         } else {
-            load_f32<E>(a.h32 + row * 128 + part * E, hf);
+            load_f32<E>(a.h32 + row * 128 + part * E, reinterpret_cast<float*>(ring[slot]));
+            rs[slot] = 0.0f;
+            rz[slot] = 0.0f;
         }
-        xx = a.x[row];
+        rx[slot] = a.x[row];
     };
-    load_row(it0, cw, hv, s_old, z_old, xv);
+    // decay, dt and D of the heads this wave covers (at most K*RPW/P + 1 <= 64), one per lane,
+    // read by the iterations with v_readlane; and B, C of the first row.  Issued before the
+    // state prefetches: the memory counter retires in order, so waiting for these does not
+    // wait for the prefetches.
+    const int64_t bh0 = bh;
+    float dt_l = 0.0f, A_l = 0.0f, d_l = 0.0f;
+    if (bh0 + lane < nbh) {
+        const int64_t q = bh0 + lane;
+        const int hq = (int)(q % a.H);
+        dt_l = a.dt[q];
+        A_l = a.A[hq];
+        d_l = a.D[hq];
+    }
+    int64_t key = b * a.G + gi;
+    typename RS::RowIn rin;
+    rin.load(a.Bm + key * 128 + part * E, a.Cm + key * 128 + part * E);
+#pragma unroll
+    for (int j = 0; j < DD; ++j) issue(j, it0 + j);
+    const float lam_l = decay(dt_l, A_l);
 
-    for (int64_t it = it0; it < it1; ++it) {
-        const int64_t row0 = it * RPW;
-        const int64_t bh = row0 / a.P;
-        const int b = (int)(bh / a.H), h = (int)(bh % a.H);
-        const int64_t k = (int64_t)b * a.G + h / hpg;
-        if (k != key) {
-            key = k;
-            load_f32<E>(a.Bm + k * 128 + part * E, Bv);
-            load_f32<E>(a.Cm + k * 128 + part * E, Cv);
-        }
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+        const int j = i % DD;
+        const int64_t it = it0 + i;
+        const int64_t row = it * RPW + sub;
         const int li = (int)(bh - bh0);
         const float lam = readlane_f(lam_l, li);
         const float dtv = readlane_f(dt_l, li);
-        const float Dh = a.D[h];
-        const int64_t row = row0 + sub;
+        const float Dh = readlane_f(d_l, li);
+        float cf[E];
+        if constexpr (Tr::quant) unpack_codes<F, E>(ring[j], cf);
+        else {
+#pragma unroll
+            for (int e = 0; e < E; ++e) cf[e] = __uint_as_float(ring[j][e]);
+        }
+        const float w = dtv * rx[j];
+        const float dx = Dh * rx[j];
+        const float ls = lam * rs[j];
+        const float lz = ls * rz[j];
+        if (i + DD < K) issue(j, it + DD);
 
-        // prefetch the next row
-        uint32_t nw[NW];
-        float nh[Tr::quant ? 1 : E];
-        float ns = 0.0f, nz = 0.0f, nx = 0.0f;
-        if (it + 1 < it1) load_row(it + 1, nw, nh, ns, nz, nx);
-
-        const float w = dtv * xv;
-        const float dx = Dh * xv;
+        const int64_t k = b * a.G + gi;
+        if (k != key) {
+            // the wave crossed into another sequence or group: new B and C
+            key = k;
+            rin.load(a.Bm + k * 128 + part * E, a.Cm + k * 128 + part * E);
+            wait_vmem_all();
+        }
         if constexpr (Tr::quant) {
             uint32_t ow[NW];
             RowGrid g;
-            bool slow_any;
-            float acc = RS::run_q(cw, s_old, z_old, lam, w, Bv, Cv, ow, g, slow_any);
-            acc = group_sum<LPR>(acc);
-            float csum = 0.0f;
-            if (!PRE && Tr::asym && __any(g.zadj != 0.0f)) csum = row_csum<LPR, E>(Cv);
+            const float yv = RS::run_q(cf, ls, lz, w, dx, rin, ow, g);
             store_words<NW>(a.codes + row * ROWB + part * (NW * 4), ow);
-            if (part == 0) {
-                a.scale[row] = g.s;
-                if constexpr (Tr::asym) a.zero[row] = g.z;
-                a.y[row] = row_y<F, PRE>(acc, g, csum, dx);
-            }
+            st_stream(a.scale + row, g.s);
+            if constexpr (Tr::asym) st_stream(a.zero + row, g.z);
+            a.y[row] = yv;
         } else {
-            float acc = RS::run_f(hv, lam, w, Bv, Cv);
-            acc = group_sum<LPR>(acc);
-            store_f32<E>(a.h32 + row * 128 + part * E, hv);
-            if (part == 0) a.y[row] = acc + dx;
+            const float yv = RS::run_f(cf, lam, w, dx, rin);
+            store_f32<E>(a.h32 + row * 128 + part * E, cf);
+            a.y[row] = yv;
         }
-
-        if (it + 1 < it1) {
-#pragma unroll
-            for (int i = 0; i < NW; ++i) cw[i] = nw[i];
-            if constexpr (!Tr::quant) {
-#pragma unroll
-                for (int e = 0; e < E; ++e) hv[e] = nh[e];
+        if (++jh == ipH) {
+            jh = 0;
+            ++bh;
+            if (++h == a.H) {
+                h = 0;
+                ++b;
+                gi = 0;
+                hg = 0;
+            } else if (++hg == hpg) {
+                hg = 0;
+                ++gi;
             }
-            s_old = ns;
-            z_old = nz;
-            xv = nx;
         }
     }
 }
@@ -267,10 +297,10 @@ __global__ __launch_bounds__(256) void k_m2_scan(M2Args a)
     auto bc_ptr = [&](const float* base, int t) { return base + (((int64_t)b * T + t) * G + g) * 128 + part * E; };
     auto x_idx = [&](int t) { return (((int64_t)b * T + t) * H + h) * P + p; };
 
-    float Bv[E], Cv[E], xv;
-    load_f32<E>(bc_ptr(a.Bm, 0), Bv);
-    load_f32<E>(bc_ptr(a.Cm, 0), Cv);
-    xv = a.x[x_idx(0)];
+    // B/C of the current token; the next token's raw B/C are prefetched
+    typename RS::RowIn rin;
+    rin.load(bc_ptr(a.Bm, 0), bc_ptr(a.Cm, 0));
+    float xv = a.x[x_idx(0)];
     float dt_l = 0.0f, lam_l = 0.0f;
 
     for (int t = 0; t < T; ++t) {
@@ -298,28 +328,25 @@ __global__ __launch_bounds__(256) void k_m2_scan(M2Args a)
         if constexpr (Tr::quant) {
             uint32_t ow[NW];
             RowGrid gr;
-            bool slow_any;
-            float acc = RS::run_q(cw, s, z, lam, w, Bv, Cv, ow, gr, slow_any);
-            acc = group_sum<LPR>(acc);
-            float csum = 0.0f;
-            if (!PRE && Tr::asym && __any(gr.zadj != 0.0f)) csum = row_csum<LPR, E>(Cv);
-            yv = row_y<F, PRE>(acc, gr, csum, dx);
+            float cf[E];
+            unpack_codes<F, E>(cw, cf);
+            const float ls = lam * s;
+            const float lz = ls * z;
+            yv = RS::run_q(cf, ls, lz, w, dx, rin, ow, gr);
 #pragma unroll
             for (int i = 0; i < NW; ++i) cw[i] = ow[i];
             s = gr.s;
             z = gr.z;
         } else {
-            float acc = RS::run_f(hv, lam, w, Bv, Cv);
-            yv = group_sum<LPR>(acc) + dx;
+            yv = RS::run_f(hv, lam, w, dx, rin);
         }
         if (part == 0) a.y[x_idx(t)] = yv;
 
         if (t + 1 < T) {
 #pragma unroll
-            for (int e = 0; e < E; ++e) {
-                Bv[e] = nB[e];
-                Cv[e] = nC[e];
-            }
+            for (int e = 0; e < E; ++e) rin.B[e] = nB[e];
+#pragma unroll
+            for (int e = 0; e < E; ++e) rin.C[e] = nC[e];
             xv = nx;
         }
     }
@@ -421,33 +448,89 @@ __global__ __launch_bounds__(256) void k_zero_fill(uint4* p, int64_t n16)
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+// lanes per 128-entry row (each lane then holds 128/LPR entries) and the depth
+// of the decode step's prefetch ring: build-time tuning knobs
+#ifndef SSQ_LPR_INT4
+#define SSQ_LPR_INT4 4
+#endif
+#ifndef SSQ_LPR_INT8
+#define SSQ_LPR_INT8 4
+#endif
+#ifndef SSQ_LPR_FP32
+#define SSQ_LPR_FP32 16
+#endif
 template <int F>
 constexpr int lanes_per_row()
 {
-    return F == FP32 ? 16 : (Traits<F>::bits == 8 ? 8 : 4);
+    return F == FP32 ? SSQ_LPR_FP32 : (Traits<F>::bits == 8 ? SSQ_LPR_INT8 : SSQ_LPR_INT4);
 }
 
+// iterations per wave (straight-line code) and prefetch distance of the decode
+// step, per code width
+#ifndef SSQ_ITERS_INT4
+#define SSQ_ITERS_INT4 16
+#endif
+#ifndef SSQ_RING_INT4
+#define SSQ_RING_INT4 4
+#endif
+#ifndef SSQ_ITERS_INT8
+#define SSQ_ITERS_INT8 8
+#endif
+#ifndef SSQ_RING_INT8
+#define SSQ_RING_INT8 3
+#endif
+#ifndef SSQ_ITERS_FP32
+#define SSQ_ITERS_FP32 8
+#endif
+#ifndef SSQ_RING_FP32
+#define SSQ_RING_FP32 3
+#endif
+
 template <int F>
-static hipError_t launch_step_f(M2Args a, bool pre, int num_cus, hipStream_t st)
+constexpr int step_iters()
+{
+    return F == FP32 ? SSQ_ITERS_FP32 : (Traits<F>::bits == 8 ? SSQ_ITERS_INT8 : SSQ_ITERS_INT4);
+}
+template <int F>
+constexpr int step_ring()
+{
+    return F == FP32 ? SSQ_RING_FP32 : (Traits<F>::bits == 8 ? SSQ_RING_INT8 : SSQ_RING_INT4);
+}
+
+template <int F, bool PRE>
+static hipError_t launch_step_fp(M2Args a, hipStream_t st)
 {
     constexpr int LPR = lanes_per_row<F>();
     constexpr int RPW = 64 / LPR;
     a.total_iters = (int64_t)a.Bsz * a.H * a.P / RPW;
-    // enough waves to fill every CU several times over; each wave then walks a contiguous range
-    const int64_t target_waves = (int64_t)num_cus * 16;
-    int64_t ipw = (a.total_iters + target_waves - 1) / target_waves;
-    // a wave's rows span at most ipw*RPW/P + 1 heads; with ipw <= 32, RPW <= 16 <= P that is
-    // at most 33, so the per-head decay fits one lane per head
-    if (ipw < 1) ipw = 1;
-    if (ipw > 32) ipw = 32;
-    a.iters_per_wave = (int)ipw;
-    const int64_t waves = (a.total_iters + ipw - 1) / ipw;
-    const unsigned blocks = (unsigned)((waves + 3) / 4);
-    if (pre)
-        hipLaunchKernelGGL((k_m2_step<F, LPR, true>), dim3(blocks), dim3(256), 0, st, a);
-    else
-        hipLaunchKernelGGL((k_m2_step<F, LPR, false>), dim3(blocks), dim3(256), 0, st, a);
-    return hipGetLastError();
+    constexpr int kStepIters = step_iters<F>();
+    constexpr int kStepRing = step_ring<F>();
+    static_assert(kStepRing >= 1 && kStepRing <= kStepIters, "prefetch ring deeper than the iterations");
+    a.iters_per_wave = kStepIters;
+    // main launch: whole groups of K iterations per wave
+    const int64_t main_waves = a.total_iters / kStepIters;
+    if (main_waves > 0) {
+        const unsigned blocks = (unsigned)((main_waves + 3) / 4);
+        hipLaunchKernelGGL((k_m2_step<F, LPR, PRE, kStepIters, kStepRing>), dim3(blocks), dim3(256), 0, st, a,
+                           (int64_t)0);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    // leftover iterations, one per wave
+    const int64_t done = main_waves * kStepIters;
+    const int64_t rest = a.total_iters - done;
+    if (rest > 0) {
+        const unsigned blocks = (unsigned)((rest + 3) / 4);
+        hipLaunchKernelGGL((k_m2_step<F, LPR, PRE, 1, 1>), dim3(blocks), dim3(256), 0, st, a, done);
+        return hipGetLastError();
+    }
+    return hipSuccess;
+}
+
+template <int F>
+static hipError_t launch_step_f(M2Args a, bool pre, int /*num_cus*/, hipStream_t st)
+{
+    return pre ? launch_step_fp<F, true>(a, st) : launch_step_fp<F, false>(a, st);
 }
 
 hipError_t launch_m2_step(int fmt, M2Args a, bool pre, int num_cus, hipStream_t st)
