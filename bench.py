@@ -32,6 +32,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "state-update GB/s + % of HBM peak; decode steps/s at batch 256"
 HBM_PEAK_GBPS = 8000.0
+# fp32 vector issue without packed instructions: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 
 WORKLOADS = {
     # name: kind, layers, batch, heads, rows_per_head, format, init, tokens (scan), instances
@@ -330,8 +332,16 @@ def main():
         "device": torch.cuda.get_device_name(0),
     }
     if kind == "scan":
-        # VALU roofline: lane-operations are not counted by the bench; report element updates/s
-        rec["roofline"]["element_updates_per_s"] = rows * N * T / (kernel_ms_mean * 1e-3)
+        # the state stays on-chip for all T tokens: the scan is bound by VALU issue.  Algorithmic
+        # work per entry-step: convert, two fmas, min, max, round, and two for the readout of
+        # the new codes (asymmetric); one op fewer for the symmetric grid (|.| max); fp32: three
+        ops = 3 if fmt == "fp32" else (8 if fmt.endswith("asym") else 7)
+        achieved_ops = rows * N * T * ops / (kernel_ms_mean * 1e-3) / 1e12
+        rec["roofline"].update({
+            "bound": "alu", "achieved": round(achieved_ops, 3), "peak": VALU_PEAK_TOPS,
+            "unit": "T lane-ops/s", "frac": round(achieved_ops / VALU_PEAK_TOPS, 4),
+            "ops_per_entry_step": ops, "io_GBps": round(achieved, 2),
+        })
 
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(args, wl, bytes_per_launch, rows)

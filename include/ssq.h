@@ -28,13 +28,17 @@
  * are bit-reproducible and independent of the launch configuration):
  *   lambda = fl32(exp(fl(dt*A)))  (exp evaluated in double, rounded once)
  *   w      = fl(dt*x)
- *   h'_n   = fma(fl(lambda*s), fl(c_n - z), fl(w*B_n))   (quantized state)
- *   h'_n   = fma(lambda, h_n, fl(w*B_n))                  (fp32 state)
+ *   quantized state (scale s, zero point z, codes c), the decay acting on
+ *   the scale and the zero-point offset folded into the write term:
+ *     ls = fl(lambda*s),  h'_n = fma(ls, c_n, fma(w, B_n, -fl(ls*z)))
+ *   fp32 state:  h'_n = fma(lambda, h_n, fl(w*B_n))
  *   asymmetric refit: s' = fl(fl(max-min)/(2^b-1)), inv = fl(1/s'),
- *     z' = -rne(fl(min*inv)), c'_n = clamp(rne(fl(h'_n*inv) + z'), 0, 2^b-1)
- *     with the sum exact and ties to the even code
+ *     z' = -rne(min*inv), c'_n = clamp(rne(h'_n*inv + z'), 0, 2^b-1)
  *   symmetric refit: s' = fl(amax/(2^(b-1)-1)), inv = fl(1/s'),
- *     c'_n = clamp(rne(fl(h'_n*inv)), -(2^(b-1)-1), 2^(b-1)-1)
+ *     c'_n = clamp(rne(h'_n*inv), -(2^(b-1)-1), 2^(b-1)-1)
+ *   where rne() rounds the exact real value (the product is not rounded
+ *     first) to the nearest integer, a tie going to the even integer, and a
+ *     zero point of zero is stored as +0
  *   a zero or subnormal s' marks a degenerate row: asymmetric rows become the
  *     constant min (s' = |min|, z' = -sign(min), codes 0), symmetric rows zero
  *   y = sum_n C_n*r_n + D*x, r = the dequantized new row s'*(c'-z')
@@ -174,10 +178,11 @@ ssq_status ssq_scan(ssq_state *state, int32_t T, const float *x, const float *dt
  * ("Mamba state quantization for inference": the query reads the matrix,
  * decay and a delta-rule correction write the next version; the update
  * S_t = A_t S_(t-1) + W_t of "Quantization error returns on the next token"),
- * evaluated as u = k^T S (products and sum in double, rounded once),
- * w_j = fl(beta*fl(v_j - fl(alpha*u_j))), S'_ij = fma(fl(alpha*s_i), fl(c_ij - z_i),
- * fl(k_i*w_j)) (fp32 state: fma(alpha, S_ij, fl(k_i*w_j))), then each key row
- * refit and rounded as above.
+ * evaluated as u = k^T S (S_ij = s_i*(c_ij - z_i) taken as a real number,
+ * products and sum in double, rounded once), w_j = fl(beta*fl(v_j - fl(alpha*u_j))),
+ * S'_ij = fma(as_i, c_ij, fma(k_i, w_j, -fl(as_i*z_i))) with as_i = fl(alpha*s_i)
+ * (fp32 state: fma(alpha, S_ij, fl(k_i*w_j))), then each key row refit and
+ * rounded as above.
  *   q, k [batch][nheads][dk], v [batch][nheads][dv], alpha, beta
  *   [batch][nheads]; o [batch][nheads][dv] is written. */
 ssq_status ssq_delta_step(ssq_state *state, const float *q, const float *k, const float *v,
