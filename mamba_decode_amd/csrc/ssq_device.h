@@ -386,6 +386,67 @@ __device__ __forceinline__ void st_stream(T* p, T v)
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// ---------------------------------------------------------------------------
+// buffer (descriptor) addressing: a wave-uniform base and byte range in scalar
+// registers, a per-lane 32-bit offset and a uniform offset.  An access outside
+// the range reads 0 and writes nothing, so a wrong offset cannot fault.
+// ---------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr int kRsrcWord3 = 0x00020000; // gfx9 family: 32-bit data format, no swizzle, no stride
+constexpr int kAuxStream = SSQ_NT ? 2 : 0; // the non-temporal hint on state traffic
+
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+
+template <int NW, int AUX>
+__device__ __forceinline__ void buf_load_words(Rsrc r, uint32_t voff, uint32_t soff, uint32_t* w)
+{
+    if constexpr (NW % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < NW / 4; ++i) {
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16 * i, soff, AUX);
+            w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+        }
+    } else if constexpr (NW == 2) {
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, AUX);
+        w[0] = v.x; w[1] = v.y;
+    } else {
+        static_assert(NW == 1, "unsupported lane width");
+        w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, AUX);
+    }
+}
+
+template <int NW, int AUX>
+__device__ __forceinline__ void buf_store_words(Rsrc r, uint32_t voff, uint32_t soff, const uint32_t* w)
+{
+    if constexpr (NW % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < NW / 4; ++i) {
+            const u32x4 v = {w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+            __builtin_amdgcn_raw_buffer_store_b128(v, r, voff + 16 * i, soff, AUX);
+        }
+    } else if constexpr (NW == 2) {
+        const u32x2 v = {w[0], w[1]};
+        __builtin_amdgcn_raw_buffer_store_b64(v, r, voff, soff, AUX);
+    } else {
+        static_assert(NW == 1, "unsupported lane width");
+        __builtin_amdgcn_raw_buffer_store_b32(w[0], r, voff, soff, AUX);
+    }
+}
+
+template <int AUX>
+__device__ __forceinline__ float buf_load_f32(Rsrc r, uint32_t voff, uint32_t soff)
+{
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, AUX));
+}
+template <int AUX>
+__device__ __forceinline__ void buf_store_f32(float v, Rsrc r, uint32_t voff, uint32_t soff)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, AUX);
+}
+
 template <int NW>
 __device__ __forceinline__ void load_words(const void* p, uint32_t* w)
 {

@@ -9,17 +9,23 @@
 // Work mapping.  A wave64 handles 64/LPR rows at a time ("an iteration"),
 // LPR lanes per row and E = 128/LPR entries per lane, so each lane moves 16
 // contiguous bytes of int8 or int4 codes (32 for fp32) and a wave's access is
-// one contiguous run of rows.  The decode kernel gives each wave a contiguous
-// range of iterations; B and C of the current (sequence, group) stay in
-// registers while consecutive rows reuse them, and the per-head decay is
-// computed once for up to 64 heads in parallel lanes and broadcast with
-// v_readlane.  The next row's codes are loaded before the current row is
-// processed.  Nothing is shared between waves, so there is no LDS and no
-// barrier; the kernel is bound by HBM traffic (codes + metadata in and out).
+// one contiguous run of rows.  The decode kernel gives each wave a fixed run
+// of consecutive iterations; B and C of the current (sequence, group) are
+// staged once in the wave's own slice of LDS (quantized formats; registers for
+// fp32) and re-read by every row, and the per-head decay is computed once for
+// up to 64 heads in parallel lanes and broadcast with v_readlane.  The codes of
+// later iterations are in flight while the current one is processed.  Waves
+// share nothing, so there is no barrier; row reductions are DPP within the
+// row's lane group.
 #include "ssq_device.h"
 #include "ssq_internal.h"
 
 namespace ssq {
+
+// B and C of the decode step in LDS (quantized formats) rather than in registers
+#ifndef SSQ_BC_LDS
+#define SSQ_BC_LDS 1
+#endif
 
 template <int F>
 struct RowBytes {
@@ -41,7 +47,7 @@ struct RowStep {
     static constexpr int E = 128 / LPR;
     static constexpr int NW = Traits<F>::quant ? E * Traits<F>::bits / 32 : E;
 
-    // B and C of the current (sequence, group): E consecutive entries each
+    // B and C of the current (sequence, group): E consecutive entries each, in registers
     struct RowIn {
         float B[E];
         float C[E];
@@ -50,30 +56,43 @@ struct RowStep {
             load_f32<E>(Bp, B);
             load_f32<E>(Cp, C);
         }
+        __device__ __forceinline__ float b(int e) const { return B[e]; }
+        __device__ __forceinline__ float c(int e) const { return C[e]; }
+    };
+    // ... or in LDS: the wave's copy of B and C, E entries per lane group, rows of E + 4
+    // floats so that the LPR groups' 16-byte reads fall in different banks
+    static constexpr int LDS_PITCH = E + 4;
+    static constexpr int LDS_FLOATS = LPR * LDS_PITCH;
+    struct RowInLds {
+        const float* Bp; // this lane's E entries of B in LDS, 16-byte aligned
+        const float* Cp;
+        __device__ __forceinline__ float b(int e) const { return Bp[e]; }
+        __device__ __forceinline__ float c(int e) const { return Cp[e]; }
     };
 
     // quantized formats: the old codes as floats (h, overwritten) in -> the new packed codes
     // ow out; returns y (valid in every lane of the row).  ls = fl(lambda*s) and
     // lz = fl(ls*z) of the old row, w = fl(dt*x), dx = fl(D*x).
+    template <typename In>
     __device__ __forceinline__ static float run_q(float* h, float ls, float lz, float w, float dx,
-                                                  const RowIn& in, uint32_t* ow, RowGrid& g)
+                                                  const In& in, uint32_t* ow, RowGrid& g)
     {
         using Tr = Traits<F>;
         // lambda*s*(c - z) + w*B = fma(ls, c, fma(w, B, -ls*z)): the decay acts on the scale
         if constexpr (Tr::asym) {
 #pragma unroll
-            for (int e = 0; e < E; ++e) h[e] = __builtin_fmaf(ls, h[e], __builtin_fmaf(w, in.B[e], -lz));
+            for (int e = 0; e < E; ++e) h[e] = __builtin_fmaf(ls, h[e], __builtin_fmaf(w, in.b(e), -lz));
         } else {
 #pragma unroll
             for (int e = 0; e < E; ++e) {
-                const float wb = w * in.B[e];
+                const float wb = w * in.b(e);
                 h[e] = __builtin_fmaf(ls, h[e], wb);
             }
         }
         float acc = 0.0f;
         if constexpr (PRE) {
 #pragma unroll
-            for (int e = 0; e < E; ++e) acc = __builtin_fmaf(in.C[e], h[e], acc);
+            for (int e = 0; e < E; ++e) acc = __builtin_fmaf(in.c(e), h[e], acc);
         }
         float mn = 0.0f, mx = 0.0f, am = 0.0f;
         if constexpr (Tr::asym) {
@@ -107,31 +126,32 @@ struct RowStep {
         // y = s * sum_n C_n*(c_n - z) + dx, read from the new codes
         if (!slow_any) {
 #pragma unroll
-            for (int e = 0; e < E; ++e) acc = __builtin_fmaf(in.C[e], h[e] - g.Mz, acc);
+            for (int e = 0; e < E; ++e) acc = __builtin_fmaf(in.c(e), h[e] - g.Mz, acc);
         } else {
 #pragma unroll
-            for (int e = 0; e < E; ++e) acc = __builtin_fmaf(in.C[e], code_minus_z(h[e], g), acc);
+            for (int e = 0; e < E; ++e) acc = __builtin_fmaf(in.c(e), code_minus_z(h[e], g), acc);
         }
         acc = group_sum<LPR>(acc);
         if (__any(g.zadj != 0.0f)) {
             // a degenerate row codes everything as 0 around z = 0 but stands for the constant -z*s
             float cs = 0.0f;
 #pragma unroll
-            for (int e = 0; e < E; ++e) cs += in.C[e];
+            for (int e = 0; e < E; ++e) cs += in.c(e);
             acc = acc - g.zadj * group_sum<LPR>(cs);
         }
         return g.s * acc + dx;
     }
 
     // fp32 control: hv in/out, returns y
-    __device__ __forceinline__ static float run_f(float* hv, float lam, float w, float dx, const RowIn& in)
+    template <typename In>
+    __device__ __forceinline__ static float run_f(float* hv, float lam, float w, float dx, const In& in)
     {
         float acc = 0.0f;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-            const float wb = w * in.B[e];
+            const float wb = w * in.b(e);
             hv[e] = __builtin_fmaf(lam, hv[e], wb);
-            acc = __builtin_fmaf(in.C[e], hv[e], acc);
+            acc = __builtin_fmaf(in.c(e), hv[e], acc);
         }
         return group_sum<LPR>(acc) + dx;
     }
@@ -148,8 +168,8 @@ struct RowStep {
 // of a row stores the row's scale, zero point and y (the same value to the same
 // address), so no store sits behind a branch either.  Leftover iterations (fewer
 // than K) are run by a second launch with K = 1.
-template <int F, int LPR, bool PRE, int K, int D>
-__global__ __launch_bounds__(256) void k_m2_step(M2Args a, int64_t it_base)
+template <int F, int LPR, bool PRE, int K, int D, int W>
+__global__ __launch_bounds__(256, W) void k_m2_step(M2Args a, int64_t it_base)
 {
     using Tr = Traits<F>;
     using RS = RowStep<F, LPR, PRE>;
@@ -171,19 +191,33 @@ __global__ __launch_bounds__(256) void k_m2_step(M2Args a, int64_t it_base)
 
     uint32_t ring[DD][NS];
     float rs[DD], rz[DD], rx[DD];
-    auto issue = [&](int slot, int64_t it) {
-        const int64_t row = it * RPW + sub;
+    // The wave's K*RPW consecutive rows as buffer descriptors: a uniform base and range in
+    // scalar registers, one fixed 32-bit offset per lane and a constant offset per
+    // iteration, so that no per-iteration address occupies vector registers.
+    const int64_t row_first = it0 * RPW;
+    constexpr uint32_t SPAN = (uint32_t)(K * RPW);
+    constexpr uint32_t WB = Tr::quant ? (uint32_t)ROWB : 512u; // state bytes per row
+    const Rsrc r_w = make_rsrc(Tr::quant ? (const void*)(a.codes + row_first * ROWB)
+                                         : (const void*)(a.h32 + row_first * 128), SPAN * WB);
+    const Rsrc r_s = make_rsrc(a.scale + row_first, Tr::quant ? SPAN * 4 : 0);
+    const Rsrc r_z = make_rsrc(a.zero + row_first, Tr::asym ? SPAN * 4 : 0);
+    const Rsrc r_x = make_rsrc(a.x + row_first, SPAN * 4);
+    const Rsrc r_y = make_rsrc(a.y + row_first, SPAN * 4);
+    const uint32_t off_w = (uint32_t)(sub * WB + part * (Tr::quant ? NW * 4 : E * 4));
+    const uint32_t off_r = (uint32_t)(sub * 4);
+    auto issue = [&](int slot, int i) {
+        const uint32_t sw = (uint32_t)i * RPW * WB, sr = (uint32_t)i * RPW * 4;
         if constexpr (Tr::quant) {
-            load_words<NW>(a.codes + row * ROWB + part * (NW * 4), ring[slot]);
-            rs[slot] = ld_stream(a.scale + row);
-            if constexpr (Tr::asym) rz[slot] = ld_stream(a.zero + row);
+            buf_load_words<NW, kAuxStream>(r_w, off_w, sw, ring[slot]);
+            rs[slot] = buf_load_f32<kAuxStream>(r_s, off_r, sr);
+            if constexpr (Tr::asym) rz[slot] = buf_load_f32<kAuxStream>(r_z, off_r, sr);
             else rz[slot] = 0.0f;
         } else {
-            load_f32<E>(a.h32 + row * 128 + part * E, reinterpret_cast<float*>(ring[slot]));
+            buf_load_words<E, kAuxStream>(r_w, off_w, sw, ring[slot]);
             rs[slot] = 0.0f;
             rz[slot] = 0.0f;
         }
-        rx[slot] = a.x[row];
+        rx[slot] = buf_load_f32<0>(r_x, off_r, sr);
     };
     // decay, dt and D of the heads this wave covers (at most K*RPW/P + 1 <= 64), one per lane,
     // read by the iterations with v_readlane; and B, C of the first row.  Issued before the
@@ -199,17 +233,36 @@ __global__ __launch_bounds__(256) void k_m2_step(M2Args a, int64_t it_base)
         d_l = a.D[hq];
     }
     int64_t key = b * a.G + gi;
+    // B and C: in registers, or (quantized formats) in this wave's slice of LDS, each lane
+    // staging two entries of each
+    constexpr bool BCL = SSQ_BC_LDS != 0 && Tr::quant;
+    constexpr int PITCH = RS::LDS_PITCH, LDSF = RS::LDS_FLOATS;
+    __shared__ float4 bc_lds[BCL ? 4 * 2 * LDSF / 4 : 1];
+    float* const lds_b = reinterpret_cast<float*>(bc_lds) + (threadIdx.x >> 6) * (2 * LDSF);
+    float* const lds_c = lds_b + LDSF;
     typename RS::RowIn rin;
-    rin.load(a.Bm + key * 128 + part * E, a.Cm + key * 128 + part * E);
+    const typename RS::RowInLds rin_l{lds_b + part * PITCH, lds_c + part * PITCH};
+    float2 bv, cv;
+    auto bc_fetch = [&](int64_t k) {
+        bv = *reinterpret_cast<const float2*>(a.Bm + k * 128 + 2 * lane);
+        cv = *reinterpret_cast<const float2*>(a.Cm + k * 128 + 2 * lane);
+    };
+    auto bc_stage = [&]() {
+        const int n = 2 * lane, off = (n / E) * PITCH + n % E;
+        *reinterpret_cast<float2*>(lds_b + off) = bv;
+        *reinterpret_cast<float2*>(lds_c + off) = cv;
+    };
+    if constexpr (BCL) bc_fetch(key);
+    else rin.load(a.Bm + key * 128 + part * E, a.Cm + key * 128 + part * E);
 #pragma unroll
-    for (int j = 0; j < DD; ++j) issue(j, it0 + j);
+    for (int j = 0; j < DD; ++j) issue(j, j);
     const float lam_l = decay(dt_l, A_l);
+    if constexpr (BCL) bc_stage();
 
 #pragma unroll
     for (int i = 0; i < K; ++i) {
         const int j = i % DD;
-        const int64_t it = it0 + i;
-        const int64_t row = it * RPW + sub;
+        const uint32_t sw = (uint32_t)i * RPW * WB, sr = (uint32_t)i * RPW * 4;
         const int li = (int)(bh - bh0);
         const float lam = readlane_f(lam_l, li);
         const float dtv = readlane_f(dt_l, li);
@@ -224,27 +277,31 @@ __global__ __launch_bounds__(256) void k_m2_step(M2Args a, int64_t it_base)
         const float dx = Dh * rx[j];
         const float ls = lam * rs[j];
         const float lz = ls * rz[j];
-        if (i + DD < K) issue(j, it + DD);
+        if (i + DD < K) issue(j, i + DD);
 
         const int64_t k = b * a.G + gi;
         if (k != key) {
             // the wave crossed into another sequence or group: new B and C
             key = k;
-            rin.load(a.Bm + k * 128 + part * E, a.Cm + k * 128 + part * E);
+            if constexpr (BCL) bc_fetch(k);
+            else rin.load(a.Bm + k * 128 + part * E, a.Cm + k * 128 + part * E);
             wait_vmem_all();
+            if constexpr (BCL) bc_stage();
         }
         if constexpr (Tr::quant) {
             uint32_t ow[NW];
             RowGrid g;
-            const float yv = RS::run_q(cf, ls, lz, w, dx, rin, ow, g);
-            store_words<NW>(a.codes + row * ROWB + part * (NW * 4), ow);
-            st_stream(a.scale + row, g.s);
-            if constexpr (Tr::asym) st_stream(a.zero + row, g.z);
-            a.y[row] = yv;
+            float yv;
+            if constexpr (BCL) yv = RS::run_q(cf, ls, lz, w, dx, rin_l, ow, g);
+            else yv = RS::run_q(cf, ls, lz, w, dx, rin, ow, g);
+            buf_store_words<NW, kAuxStream>(r_w, off_w, sw, ow);
+            buf_store_f32<kAuxStream>(g.s, r_s, off_r, sr);
+            if constexpr (Tr::asym) buf_store_f32<kAuxStream>(g.z, r_z, off_r, sr);
+            buf_store_f32<0>(yv, r_y, off_r, sr);
         } else {
             const float yv = RS::run_f(cf, lam, w, dx, rin);
-            store_f32<E>(a.h32 + row * 128 + part * E, cf);
-            a.y[row] = yv;
+            buf_store_words<E, kAuxStream>(r_w, off_w, sw, reinterpret_cast<const uint32_t*>(cf));
+            buf_store_f32<0>(yv, r_y, off_r, sr);
         }
         if (++jh == ipH) {
             jh = 0;
@@ -465,13 +522,18 @@ constexpr int lanes_per_row()
     return F == FP32 ? SSQ_LPR_FP32 : (Traits<F>::bits == 8 ? SSQ_LPR_INT8 : SSQ_LPR_INT4);
 }
 
-// iterations per wave (straight-line code) and prefetch distance of the decode
-// step, per code width
+// iterations per wave (straight-line code), prefetch distance and the waves per
+// SIMD the register budget is sized for (launch bounds), per code width.  With B
+// and C in LDS and buffer addressing both quantized widths fit 128 registers
+// (4 waves per SIMD); K = 8 then makes one round of resident waves at 370m shape.
 #ifndef SSQ_ITERS_INT4
-#define SSQ_ITERS_INT4 16
+#define SSQ_ITERS_INT4 8
 #endif
 #ifndef SSQ_RING_INT4
 #define SSQ_RING_INT4 4
+#endif
+#ifndef SSQ_WAVES_INT4
+#define SSQ_WAVES_INT4 4
 #endif
 #ifndef SSQ_ITERS_INT8
 #define SSQ_ITERS_INT8 8
@@ -479,11 +541,17 @@ constexpr int lanes_per_row()
 #ifndef SSQ_RING_INT8
 #define SSQ_RING_INT8 3
 #endif
+#ifndef SSQ_WAVES_INT8
+#define SSQ_WAVES_INT8 4
+#endif
 #ifndef SSQ_ITERS_FP32
 #define SSQ_ITERS_FP32 8
 #endif
 #ifndef SSQ_RING_FP32
 #define SSQ_RING_FP32 3
+#endif
+#ifndef SSQ_WAVES_FP32
+#define SSQ_WAVES_FP32 1
 #endif
 
 template <int F>
@@ -495,6 +563,13 @@ template <int F>
 constexpr int step_ring()
 {
     return F == FP32 ? SSQ_RING_FP32 : (Traits<F>::bits == 8 ? SSQ_RING_INT8 : SSQ_RING_INT4);
+}
+// the pre-rounding readout keeps C live through the update: one wave less
+template <int F, bool PRE>
+constexpr int step_waves()
+{
+    constexpr int w = F == FP32 ? SSQ_WAVES_FP32 : (Traits<F>::bits == 8 ? SSQ_WAVES_INT8 : SSQ_WAVES_INT4);
+    return PRE && w > 2 ? w - 1 : w;
 }
 
 template <int F, bool PRE>
@@ -511,7 +586,8 @@ static hipError_t launch_step_fp(M2Args a, hipStream_t st)
     const int64_t main_waves = a.total_iters / kStepIters;
     if (main_waves > 0) {
         const unsigned blocks = (unsigned)((main_waves + 3) / 4);
-        hipLaunchKernelGGL((k_m2_step<F, LPR, PRE, kStepIters, kStepRing>), dim3(blocks), dim3(256), 0, st, a,
+        hipLaunchKernelGGL((k_m2_step<F, LPR, PRE, kStepIters, kStepRing, step_waves<F, PRE>()>), dim3(blocks),
+                           dim3(256), 0, st, a,
                            (int64_t)0);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -521,7 +597,7 @@ static hipError_t launch_step_fp(M2Args a, hipStream_t st)
     const int64_t rest = a.total_iters - done;
     if (rest > 0) {
         const unsigned blocks = (unsigned)((rest + 3) / 4);
-        hipLaunchKernelGGL((k_m2_step<F, LPR, PRE, 1, 1>), dim3(blocks), dim3(256), 0, st, a, done);
+        hipLaunchKernelGGL((k_m2_step<F, LPR, PRE, 1, 1, 1>), dim3(blocks), dim3(256), 0, st, a, done);
         return hipGetLastError();
     }
     return hipSuccess;
