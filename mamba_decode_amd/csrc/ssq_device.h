@@ -65,23 +65,51 @@ __device__ __forceinline__ float dppf(float v)
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
+// min / max of a lane and its DPP partner in one v_min_f32_dpp / v_max_f32_dpp.
+// Written out because the compiler, to keep fminf's NaN rules, would move the
+// partner with v_mov_b32_dpp and canonicalize it first (four instructions per
+// step); the values here are finite.  The s_nop gives the two wait states a DPP
+// read needs after a VALU write of its source.
+#define SSQ_DPP_MINMAX(NAME, OP)                                                                  \
+    template <int CTRL>                                                                           \
+    __device__ __forceinline__ float NAME(float v)                                                \
+    {                                                                                             \
+        float r;                                                                                  \
+        if constexpr (CTRL == 0xB1)                                                               \
+            asm("s_nop 1\n\t" OP " %0, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"   \
+                : "=v"(r) : "v"(v));                                                              \
+        else if constexpr (CTRL == 0x4E)                                                          \
+            asm("s_nop 1\n\t" OP " %0, %1, %1 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf"   \
+                : "=v"(r) : "v"(v));                                                              \
+        else if constexpr (CTRL == 0x141)                                                         \
+            asm("s_nop 1\n\t" OP " %0, %1, %1 row_half_mirror row_mask:0xf bank_mask:0xf"       \
+                : "=v"(r) : "v"(v));                                                              \
+        else                                                                                      \
+            asm("s_nop 1\n\t" OP " %0, %1, %1 row_mirror row_mask:0xf bank_mask:0xf"            \
+                : "=v"(r) : "v"(v));                                                              \
+        return r;                                                                                 \
+    }
+SSQ_DPP_MINMAX(dpp_min, "v_min_f32_dpp")
+SSQ_DPP_MINMAX(dpp_max, "v_max_f32_dpp")
+#undef SSQ_DPP_MINMAX
+
 // xor 1, xor 2 inside a quad; lane i <-> 7-i inside 8; lane i <-> 15-i inside 16
 template <int LPR>
 __device__ __forceinline__ float group_min(float v)
 {
-    if constexpr (LPR >= 2) v = fminf(v, dppf<0xB1>(v));
-    if constexpr (LPR >= 4) v = fminf(v, dppf<0x4E>(v));
-    if constexpr (LPR >= 8) v = fminf(v, dppf<0x141>(v));
-    if constexpr (LPR >= 16) v = fminf(v, dppf<0x140>(v));
+    if constexpr (LPR >= 2) v = dpp_min<0xB1>(v);
+    if constexpr (LPR >= 4) v = dpp_min<0x4E>(v);
+    if constexpr (LPR >= 8) v = dpp_min<0x141>(v);
+    if constexpr (LPR >= 16) v = dpp_min<0x140>(v);
     return v;
 }
 template <int LPR>
 __device__ __forceinline__ float group_max(float v)
 {
-    if constexpr (LPR >= 2) v = fmaxf(v, dppf<0xB1>(v));
-    if constexpr (LPR >= 4) v = fmaxf(v, dppf<0x4E>(v));
-    if constexpr (LPR >= 8) v = fmaxf(v, dppf<0x141>(v));
-    if constexpr (LPR >= 16) v = fmaxf(v, dppf<0x140>(v));
+    if constexpr (LPR >= 2) v = dpp_max<0xB1>(v);
+    if constexpr (LPR >= 4) v = dpp_max<0x4E>(v);
+    if constexpr (LPR >= 8) v = dpp_max<0x141>(v);
+    if constexpr (LPR >= 16) v = dpp_max<0x140>(v);
     return v;
 }
 // every lane of the group ends with the same sum (each step adds a value and its mirror)
