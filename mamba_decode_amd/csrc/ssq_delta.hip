@@ -17,18 +17,25 @@
 // rows in registers, then the 32 partial rows meet in LDS.  u is accumulated in
 // double and rounded once, so its reduction order only matters where the sum
 // lies within double rounding of an fp32 midpoint; o is an output only.  The whole matrix (16 KiB of int8
-// codes) is read once and written once: the kernel is bound by HBM traffic.
+// codes) is read once and written once.  The codes stay packed in registers between
+// the two phases (4 waves per SIMD, 4 matrices per CU in flight).
 #include "ssq_device.h"
 #include "ssq_internal.h"
 
 namespace ssq {
 
+// waves per SIMD the register budget is sized for
+#ifndef SSQ_DELTA_WAVES
+#define SSQ_DELTA_WAVES 4
+#endif
+
 template <int F, bool PRE>
-__global__ __launch_bounds__(256) void k_delta_step(DeltaArgs a)
+__global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_delta_step(DeltaArgs a)
 {
     using Tr = Traits<F>;
     constexpr int LPR = 8, E = 16, RG = 32, KR = 4; // lanes per row, columns per lane, row groups, rows per thread
     constexpr int NW = Tr::quant ? E * Tr::bits / 32 : E;
+    constexpr int NS = NW; // registers per row part (packed codes, or fp32 values)
     constexpr int ROWB = Tr::quant ? 128 * Tr::bits / 8 : 512;
     __shared__ double part_u[RG * 128]; // reused for the fp32 partials of o
     __shared__ float u_s[128];
@@ -40,7 +47,10 @@ __global__ __launch_bounds__(256) void k_delta_step(DeltaArgs a)
     const float alpha = a.alpha[mat], beta = a.beta[mat];
 
     float kk[KR], qq[KR], s_old[KR], z_old[KR];
-    float S[KR][E];
+    // the codes stay packed in registers (or the fp32 rows, for the fp32 state) and are
+    // unpacked where they are used, once for u and once for the update: fewer live
+    // registers, more waves per SIMD to overlap the matrix loads
+    uint32_t cw[KR][NW];
 #pragma unroll
     for (int r = 0; r < KR; ++r) {
         const int i = rg + RG * r;
@@ -48,17 +58,22 @@ __global__ __launch_bounds__(256) void k_delta_step(DeltaArgs a)
         qq[r] = a.q[mrow0 + i];
         const int64_t row = mrow0 + i;
         if constexpr (Tr::quant) {
-            uint32_t cw[NW];
-            load_words<NW>(a.codes + row * ROWB + part * (NW * 4), cw);
-            unpack_codes<F, E>(cw, S[r]); // the codes c_ij as floats
+            load_words<NW>(a.codes + row * ROWB + part * (NW * 4), cw[r]);
             s_old[r] = a.scale[row];
             z_old[r] = Tr::asym ? a.zero[row] : 0.0f;
         } else {
-            load_f32<E>(a.h32 + row * 128 + j0, S[r]);
+            load_f32<E>(a.h32 + row * 128 + j0, reinterpret_cast<float*>(cw[r]));
             s_old[r] = 1.0f;
             z_old[r] = 0.0f;
         }
     }
+    auto row_values = [&](int r, float* f) {
+        if constexpr (Tr::quant) unpack_codes<F, E>(cw[r], f); // the codes c_ij as floats
+        else {
+#pragma unroll
+            for (int e = 0; e < E; ++e) f[e] = __uint_as_float(cw[r][e]);
+        }
+    };
     float vv[E];
     load_f32<E>(a.v + mrow0 + j0, vv);
 
@@ -76,8 +91,10 @@ __global__ __launch_bounds__(256) void k_delta_step(DeltaArgs a)
 #pragma unroll
         for (int r = 0; r < KR; ++r) {
             const double kap = Tr::quant ? (double)kk[r] * (double)s_old[r] : (double)kk[r];
+            float f[E];
+            row_values(r, f);
 #pragma unroll
-            for (int e = 0; e < E; ++e) up[e] = __builtin_fma(kap, (double)S[r][e], up[e]);
+            for (int e = 0; e < E; ++e) up[e] = __builtin_fma(kap, (double)f[e], up[e]);
         }
 #pragma unroll
         for (int e = 0; e < E; ++e) part_u[rg * 128 + j0 + e] = up[e];
@@ -107,49 +124,54 @@ __global__ __launch_bounds__(256) void k_delta_step(DeltaArgs a)
 #pragma unroll
     for (int r = 0; r < KR; ++r) {
         const int64_t row = mrow0 + rg + RG * r;
+        // unpack again rather than keep the first unpacking alive across the u reduction
+#pragma unroll
+        for (int q = 0; q < NS; ++q) asm volatile("" : "+v"(cw[r][q]));
+        float S[E];
+        row_values(r, S);
         if constexpr (Tr::quant) {
             // alpha*s*(c - z) + k*w = fma(as, c, fma(k, w, -as*z)): the decay acts on the scale
             const float as = alpha * s_old[r];
             const float az = as * z_old[r];
 #pragma unroll
-            for (int e = 0; e < E; ++e) S[r][e] = __builtin_fmaf(as, S[r][e], __builtin_fmaf(kk[r], ww[e], -az));
+            for (int e = 0; e < E; ++e) S[e] = __builtin_fmaf(as, S[e], __builtin_fmaf(kk[r], ww[e], -az));
         } else {
 #pragma unroll
             for (int e = 0; e < E; ++e) {
                 const float kw = kk[r] * ww[e];
-                S[r][e] = __builtin_fmaf(alpha, S[r][e], kw);
+                S[e] = __builtin_fmaf(alpha, S[e], kw);
             }
         }
         if constexpr (!Tr::quant || PRE) {
 #pragma unroll
-            for (int e = 0; e < E; ++e) op[e] = __builtin_fmaf(qq[r], S[r][e], op[e]);
+            for (int e = 0; e < E; ++e) op[e] = __builtin_fmaf(qq[r], S[e], op[e]);
         }
         if constexpr (Tr::quant) {
             float mn = 0.0f, mx = 0.0f, am = 0.0f;
             if constexpr (Tr::asym) {
-                mn = S[r][0];
-                mx = S[r][0];
+                mn = S[0];
+                mx = S[0];
 #pragma unroll
                 for (int e = 1; e < E; ++e) {
-                    mn = fminf(mn, S[r][e]);
-                    mx = fmaxf(mx, S[r][e]);
+                    mn = fminf(mn, S[e]);
+                    mx = fmaxf(mx, S[e]);
                 }
                 mn = group_min<LPR>(mn);
                 mx = group_max<LPR>(mx);
             } else {
 #pragma unroll
-                for (int e = 0; e < E; ++e) am = fmaxf(am, fabsf(S[r][e]));
+                for (int e = 0; e < E; ++e) am = fmaxf(am, fabsf(S[e]));
                 am = group_max<LPR>(am);
             }
             RowGrid g;
             float f[E];
             if (__all(refit_fast<F>(mn, mx, am, g))) {
 #pragma unroll
-                for (int e = 0; e < E; ++e) f[e] = __builtin_fmaf(S[r][e], g.inv, g.Mz);
+                for (int e = 0; e < E; ++e) f[e] = __builtin_fmaf(S[e], g.inv, g.Mz);
             } else {
                 g = refit<F>(mn, mx, am);
                 const bool slow_any = Tr::asym && __any(g.slow);
-                round_codes<F, E>(S[r], g, slow_any, f);
+                round_codes<F, E>(S, g, slow_any, f);
             }
             uint32_t ow[NW];
             pack_codes<F, E>(f, ow);
@@ -167,7 +189,7 @@ __global__ __launch_bounds__(256) void k_delta_step(DeltaArgs a)
                 }
             }
         } else {
-            store_f32<E>(a.h32 + row * 128 + j0, S[r]);
+            store_f32<E>(a.h32 + row * 128 + j0, S);
         }
     }
 
