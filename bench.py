@@ -333,9 +333,11 @@ def main():
     }
     if kind == "scan":
         # the state stays on-chip for all T tokens: the scan is bound by VALU issue.  Algorithmic
-        # work per entry-step: convert, two fmas, min, max, round, and two for the readout of
-        # the new codes (asymmetric); one op fewer for the symmetric grid (|.| max); fp32: three
-        ops = 3 if fmt == "fp32" else (8 if fmt.endswith("asym") else 7)
+        # work per entry-step, in VALU lane-instructions: the two fmas of the update, the
+        # row's extremes (min3 and max3 each take two new entries: one per entry; the
+        # symmetric grid's |.| max3: one half), the rounding fma, and (c - z) plus one fma
+        # for the readout of the new codes; fp32: the product, the fma and the readout fma
+        ops = 3 if fmt == "fp32" else (6 if fmt.endswith("asym") else 5.5)
         achieved_ops = rows * N * T * ops / (kernel_ms_mean * 1e-3) / 1e12
         rec["roofline"].update({
             "bound": "alu", "achieved": round(achieved_ops, 3), "peak": VALU_PEAK_TOPS,

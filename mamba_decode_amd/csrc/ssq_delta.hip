@@ -184,7 +184,7 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_delta_step(DeltaArgs a
                 const float qs = qq[r] * g.s;
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
-                    const float cz = code_minus_z(f[e], g) - g.zadj;
+                    const float cz = f[e] - g.Mr; // c - z (the readout is an output)
                     op[e] = __builtin_fmaf(qs, cz, op[e]);
                 }
             }

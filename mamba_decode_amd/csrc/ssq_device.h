@@ -241,8 +241,8 @@ struct RowGrid {
     float z;     // stored zero point (0 for symmetric)
     float inv;   // 1/s, or 0 for a degenerate row (all codes 0)
     float Mz;    // 1.5*2^23 + z on the fast path
+    float Mr;    // 1.5*2^23 + the z the readout subtracts: f - Mr = c - z
     float zc;    // z used for coding (0 for a degenerate row)
-    float zadj;  // z for readout of a degenerate asymmetric row, else 0
     bool slow;   // |z| >= 2^21
 };
 
@@ -251,7 +251,6 @@ __device__ __forceinline__ RowGrid refit(float mn, float mx, float amax)
 {
     RowGrid g;
     g.slow = false;
-    g.zadj = 0.0f;
     if constexpr (Traits<F>::asym) {
         constexpr float qmax = (float)Traits<F>::hi;
         const float range = mx - mn;
@@ -262,8 +261,8 @@ __device__ __forceinline__ RowGrid refit(float mn, float mx, float amax)
             g.z = -(mn > 0.0f ? 1.0f : (mn < 0.0f ? -1.0f : 0.0f)) + 0.0f; // a zero zero point is +0
             g.inv = 0.0f;
             g.zc = 0.0f;
-            g.zadj = g.z;
-            g.Mz = kMagic;
+            g.Mz = kMagic;      // every code 0 ...
+            g.Mr = kMagic + g.z; // ... standing for s*(0 - z) = mn
         } else {
             const float inv = 1.0f / s;
             // the product of two floats is exact in double; rint rounds half to even
@@ -274,6 +273,7 @@ __device__ __forceinline__ RowGrid refit(float mn, float mx, float amax)
             g.zc = z;
             g.slow = fabsf(z) >= kSlowZero;
             g.Mz = kMagic + z;
+            g.Mr = g.Mz; // inexact only when |z| >= 2^22, where f - Mr is within 2^-21 relative of c - z
         }
     } else {
         constexpr float qmax = (float)Traits<F>::hi;
@@ -281,6 +281,7 @@ __device__ __forceinline__ RowGrid refit(float mn, float mx, float amax)
         g.z = 0.0f;
         g.zc = 0.0f;
         g.Mz = kMagic;
+        g.Mr = kMagic;
         if (!(s >= kFltMin)) {
             g.s = 0.0f;
             g.inv = 0.0f;
@@ -350,7 +351,6 @@ __device__ __forceinline__ bool refit_fast(float mn, float mx, float amax, RowGr
     constexpr float lo_ok = 7.88860905e-31f; // 2^-100
     constexpr float hi_ok = 1.26765060e+30f; // 2^100
     g.slow = false;
-    g.zadj = 0.0f;
     if constexpr (Traits<F>::asym) {
         const float range = mx - mn;
         const float s = div_by_const<Traits<F>::hi>(range);
@@ -361,6 +361,7 @@ __device__ __forceinline__ bool refit_fast(float mn, float mx, float amax, RowGr
         g.inv = inv;
         g.zc = z;
         g.Mz = kMagic + z;
+        g.Mr = g.Mz;
         const float top = __builtin_fmaf(mx, inv, g.Mz);
         return range >= lo_ok && range <= hi_ok && fabsf(z) < kSlowZero &&
                top <= kMagic + (float)Traits<F>::hi;
@@ -372,16 +373,12 @@ __device__ __forceinline__ bool refit_fast(float mn, float mx, float amax, RowGr
         g.inv = inv;
         g.zc = 0.0f;
         g.Mz = kMagic;
+        g.Mr = kMagic;
         const float top = __builtin_fmaf(amax, inv, kMagic);
         return amax >= lo_ok && amax <= hi_ok && top <= kMagic + (float)Traits<F>::hi;
     }
 }
 
-// (code - z) as float from f, exact on the fast path
-__device__ __forceinline__ float code_minus_z(float f, const RowGrid& g)
-{
-    return g.slow ? (f - kMagic) - g.zc : f - g.Mz;
-}
 
 // ---------------------------------------------------------------------------
 // vector memory helpers: NW consecutive 32-bit words at a 4*NW-byte aligned address

@@ -73,7 +73,9 @@ struct RowStep {
     // quantized formats: the old codes as floats (h, overwritten) in -> the new packed codes
     // ow out; returns y (valid in every lane of the row).  ls = fl(lambda*s) and
     // lz = fl(ls*z) of the old row, w = fl(dt*x), dx = fl(D*x).
-    template <typename In>
+    // PACK: pack the new codes into ow; otherwise h ends holding the new codes as floats
+    // (what the next token of a scan starts from)
+    template <bool PACK = true, typename In>
     __device__ __forceinline__ static float run_q(float* h, float ls, float lz, float w, float dx,
                                                   const In& in, uint32_t* ow, RowGrid& g)
     {
@@ -111,33 +113,31 @@ struct RowStep {
             am = group_max<LPR>(am);
         }
         // h becomes f = 1.5*2^23 + code in place
-        bool slow_any = false;
         if (__all(refit_fast<F>(mn, mx, am, g))) {
             // every row of the wave is inside the verified ranges and needs no clamp
 #pragma unroll
             for (int e = 0; e < E; ++e) h[e] = __builtin_fmaf(h[e], g.inv, g.Mz);
         } else {
             g = refit<F>(mn, mx, am);
-            slow_any = Tr::asym && __any(g.slow);
+            const bool slow_any = Tr::asym && __any(g.slow);
             round_codes<F, E>(h, g, slow_any, h);
         }
-        pack_codes<F, E>(h, ow);
-        if constexpr (PRE) return group_sum<LPR>(acc) + dx;
-        // y = s * sum_n C_n*(c_n - z) + dx, read from the new codes
-        if (!slow_any) {
+        if constexpr (PACK) pack_codes<F, E>(h, ow);
+        if constexpr (PRE) {
+            if constexpr (!PACK) {
 #pragma unroll
-            for (int e = 0; e < E; ++e) acc = __builtin_fmaf(in.c(e), h[e] - g.Mz, acc);
-        } else {
-#pragma unroll
-            for (int e = 0; e < E; ++e) acc = __builtin_fmaf(in.c(e), code_minus_z(h[e], g), acc);
+                for (int e = 0; e < E; ++e) h[e] -= kMagic; // exact: the code
+            }
+            return group_sum<LPR>(acc) + dx;
         }
-        acc = group_sum<LPR>(acc);
-        if (__any(g.zadj != 0.0f)) {
-            // a degenerate row codes everything as 0 around z = 0 but stands for the constant -z*s
-            float cs = 0.0f;
+        // y = s * sum_n C_n*(c_n - z) + dx, read from the new codes: f - Mr is c - z exactly
+        // (within 2^-21 relative for a zero point beyond 2^22; y is an output)
 #pragma unroll
-            for (int e = 0; e < E; ++e) cs += in.c(e);
-            acc = acc - g.zadj * group_sum<LPR>(cs);
+        for (int e = 0; e < E; ++e) acc = __builtin_fmaf(in.c(e), h[e] - g.Mr, acc);
+        acc = group_sum<LPR>(acc);
+        if constexpr (!PACK) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) h[e] -= kMagic; // exact: the code
         }
         return g.s * acc + dx;
     }
@@ -233,9 +233,9 @@ __global__ __launch_bounds__(256, W) void k_m2_step(M2Args a, int64_t it_base)
         d_l = a.D[hq];
     }
     int64_t key = b * a.G + gi;
-    // B and C: in registers, or (quantized formats) in this wave's slice of LDS, each lane
-    // staging two entries of each
-    constexpr bool BCL = SSQ_BC_LDS != 0 && Tr::quant;
+    // B and C: in this wave's slice of LDS (each lane staging two entries of each), or in
+    // registers when built with SSQ_BC_LDS=0
+    constexpr bool BCL = SSQ_BC_LDS != 0;
     constexpr int PITCH = RS::LDS_PITCH, LDSF = RS::LDS_FLOATS;
     __shared__ float4 bc_lds[BCL ? 4 * 2 * LDSF / 4 : 1];
     float* const lds_b = reinterpret_cast<float*>(bc_lds) + (threadIdx.x >> 6) * (2 * LDSF);
@@ -299,7 +299,9 @@ __global__ __launch_bounds__(256, W) void k_m2_step(M2Args a, int64_t it_base)
             if constexpr (Tr::asym) buf_store_f32<kAuxStream>(g.z, r_z, off_r, sr);
             buf_store_f32<0>(yv, r_y, off_r, sr);
         } else {
-            const float yv = RS::run_f(cf, lam, w, dx, rin);
+            float yv;
+            if constexpr (BCL) yv = RS::run_f(cf, lam, w, dx, rin_l);
+            else yv = RS::run_f(cf, lam, w, dx, rin);
             buf_store_words<E, kAuxStream>(r_w, off_w, sw, reinterpret_cast<const uint32_t*>(cf));
             buf_store_f32<0>(yv, r_y, off_r, sr);
         }
@@ -322,12 +324,24 @@ __global__ __launch_bounds__(256, W) void k_m2_step(M2Args a, int64_t it_base)
 // ---------------------------------------------------------------------------
 // fused scan: each wave keeps one iteration's rows in registers for T tokens
 // ---------------------------------------------------------------------------
+// The rows stay on-chip as codes in float form (no packing between tokens) with
+// their scale and zero point.  B and C of each token go through two LDS buffers
+// per wave: token t reads buffer t&1 while token t+1's B and C, loaded during
+// token t-1, are written to the other one and token t+2's are being loaded, so
+// every global load has a full token of work to arrive.  All loads are
+// unconditional (the token index is clamped at the end), and every lane of a
+// row stores that row's y.
+#ifndef SSQ_SCAN_WAVES
+#define SSQ_SCAN_WAVES 4
+#endif
 template <int F, int LPR, bool PRE>
-__global__ __launch_bounds__(256) void k_m2_scan(M2Args a)
+__global__ __launch_bounds__(256, PRE ? SSQ_SCAN_WAVES - 1 : SSQ_SCAN_WAVES) void k_m2_scan(M2Args a)
 {
     using Tr = Traits<F>;
     using RS = RowStep<F, LPR, PRE>;
     constexpr int E = RS::E, NW = RS::NW, RPW = 64 / LPR, ROWB = RowBytes<F>::value;
+    constexpr int PITCH = RS::LDS_PITCH, LDSF = RS::LDS_FLOATS;
+    __shared__ float4 bc_lds[4 * 2 * 2 * LDSF / 4]; // [wave][buffer][B, C][LDSF]
     const int lane = threadIdx.x & 63, sub = lane / LPR, part = lane % LPR;
     const int64_t it = wave_id();
     if (it >= a.total_iters) return;
@@ -340,24 +354,34 @@ __global__ __launch_bounds__(256) void k_m2_scan(M2Args a)
     const int T = a.T, H = a.H, P = a.P, G = a.G;
     const float Ah = a.A[h], Dh = a.D[h];
 
-    uint32_t cw[NW];
-    float hv[Tr::quant ? 1 : E];
+    float cf[E]; // the row's codes as floats (quantized) or its fp32 values
     float s = 0.0f, z = 0.0f;
     if constexpr (Tr::quant) {
+        uint32_t cw[NW];
         load_words<NW>(a.codes + row * ROWB + part * (NW * 4), cw);
         s = a.scale[row];
         if constexpr (Tr::asym) z = a.zero[row];
+        unpack_codes<F, E>(cw, cf);
     } else {
-        load_f32<E>(a.h32 + row * 128 + part * E, hv);
+        load_f32<E>(a.h32 + row * 128 + part * E, cf);
     }
 
-    auto bc_ptr = [&](const float* base, int t) { return base + (((int64_t)b * T + t) * G + g) * 128 + part * E; };
+    float* const wl = reinterpret_cast<float*>(bc_lds) + (threadIdx.x >> 6) * (4 * LDSF);
+    const int n2 = 2 * lane, st_off = (n2 / E) * PITCH + n2 % E; // this lane's two entries
+    auto bc_at = [&](const float* base, int t) {
+        return *reinterpret_cast<const float2*>(base + (((int64_t)b * T + t) * G + g) * 128 + n2);
+    };
+    auto stage = [&](int buf, float2 bv, float2 cv) {
+        *reinterpret_cast<float2*>(wl + buf * (2 * LDSF) + st_off) = bv;
+        *reinterpret_cast<float2*>(wl + buf * (2 * LDSF) + LDSF + st_off) = cv;
+    };
     auto x_idx = [&](int t) { return (((int64_t)b * T + t) * H + h) * P + p; };
 
-    // B/C of the current token; the next token's raw B/C are prefetched
-    typename RS::RowIn rin;
-    rin.load(bc_ptr(a.Bm, 0), bc_ptr(a.Cm, 0));
-    float xv = a.x[x_idx(0)];
+    // token 0 into buffer 0; token 1 in registers
+    stage(0, bc_at(a.Bm, 0), bc_at(a.Cm, 0));
+    const int t1 = T > 1 ? 1 : 0;
+    float2 bn = bc_at(a.Bm, t1), cn = bc_at(a.Cm, t1);
+    float xv = a.x[x_idx(0)], xn = a.x[x_idx(t1)];
     float dt_l = 0.0f, lam_l = 0.0f;
 
     for (int t = 0; t < T; ++t) {
@@ -371,57 +395,52 @@ __global__ __launch_bounds__(256) void k_m2_scan(M2Args a)
         const float lam = readlane_f(lam_l, t & 63);
         const float dtv = readlane_f(dt_l, t & 63);
 
-        // prefetch the next token's inputs
-        float nB[E], nC[E], nx = 0.0f;
-        if (t + 1 < T) {
-            load_f32<E>(bc_ptr(a.Bm, t + 1), nB);
-            load_f32<E>(bc_ptr(a.Cm, t + 1), nC);
-            nx = a.x[x_idx(t + 1)];
-        }
+        // token t+2's inputs (clamped to the last token)
+        const int t2 = t + 2 < T ? t + 2 : T - 1;
+        const float2 bf = bc_at(a.Bm, t2), cf2 = bc_at(a.Cm, t2);
+        const float xf = a.x[x_idx(t2)];
 
+        const float* const cur = wl + (t & 1) * (2 * LDSF);
+        const typename RS::RowInLds in{cur + part * PITCH, cur + LDSF + part * PITCH};
         const float w = dtv * xv;
         const float dx = Dh * xv;
         float yv;
         if constexpr (Tr::quant) {
-            uint32_t ow[NW];
             RowGrid gr;
-            float cf[E];
-            unpack_codes<F, E>(cw, cf);
             const float ls = lam * s;
             const float lz = ls * z;
-            yv = RS::run_q(cf, ls, lz, w, dx, rin, ow, gr);
-#pragma unroll
-            for (int i = 0; i < NW; ++i) cw[i] = ow[i];
+            yv = RS::template run_q<false>(cf, ls, lz, w, dx, in, nullptr, gr);
             s = gr.s;
             z = gr.z;
         } else {
-            yv = RS::run_f(hv, lam, w, dx, rin);
+            yv = RS::run_f(cf, lam, w, dx, in);
         }
-        if (part == 0) a.y[x_idx(t)] = yv;
+        a.y[x_idx(t)] = yv;
 
-        if (t + 1 < T) {
-#pragma unroll
-            for (int e = 0; e < E; ++e) rin.B[e] = nB[e];
-#pragma unroll
-            for (int e = 0; e < E; ++e) rin.C[e] = nC[e];
-            xv = nx;
-        }
+        // token t+1's B and C into the other buffer
+        stage((t + 1) & 1, bn, cn);
+        bn = bf;
+        cn = cf2;
+        xv = xn;
+        xn = xf;
     }
 
     if constexpr (Tr::quant) {
+        float f[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) f[e] = cf[e] + kMagic; // the codes in the form pack_codes takes
+        uint32_t cw[NW];
+        pack_codes<F, E>(f, cw);
         store_words<NW>(a.codes + row * ROWB + part * (NW * 4), cw);
         if (part == 0) {
             a.scale[row] = s;
             if constexpr (Tr::asym) a.zero[row] = z;
         }
     } else {
-        store_f32<E>(a.h32 + row * 128 + part * E, hv);
+        store_f32<E>(a.h32 + row * 128 + part * E, cf);
     }
 }
 
-// ---------------------------------------------------------------------------
-// quantize fp32 rows into a state (state initialisation), and dequantize
-// ---------------------------------------------------------------------------
 template <int F, int LPR>
 __global__ __launch_bounds__(256) void k_quantize_rows(QArgs a)
 {
@@ -514,7 +533,7 @@ __global__ __launch_bounds__(256) void k_zero_fill(uint4* p, int64_t n16)
 #define SSQ_LPR_INT8 4
 #endif
 #ifndef SSQ_LPR_FP32
-#define SSQ_LPR_FP32 16
+#define SSQ_LPR_FP32 4
 #endif
 template <int F>
 constexpr int lanes_per_row()
@@ -548,10 +567,10 @@ constexpr int lanes_per_row()
 #define SSQ_ITERS_FP32 8
 #endif
 #ifndef SSQ_RING_FP32
-#define SSQ_RING_FP32 3
+#define SSQ_RING_FP32 2
 #endif
 #ifndef SSQ_WAVES_FP32
-#define SSQ_WAVES_FP32 1
+#define SSQ_WAVES_FP32 3
 #endif
 
 template <int F>
