@@ -74,6 +74,24 @@ def bind(path: str):
     L.orc_delta_step.argtypes = [ci, ci, ci, ci, ci, ci, i32p, f32p, f32p, f32p, f32p, f32p,
                                  f32p, f32p, f32p, f32p, ci, f32p, f32p]
     L.orc_delta_step.restype = ci
+    u64 = ctypes.c_uint64
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    L.orc_splitmix64.argtypes = [u64, u64]
+    L.orc_splitmix64.restype = u64
+    L.orc_sr_uniform.argtypes = [u64, u64, cl, cl, ci, ci]
+    L.orc_sr_uniform.restype = ctypes.c_float
+    L.orc_sr_row_uniforms.argtypes = [u64, u64, cl, cl, ci, f32p]
+    L.orc_sr_row_uniforms.restype = None
+    L.orc_quantize_row_sr.argtypes = [f32p, ci, ci, ci, i32p, f32p, f32p, f32p, f32p]
+    L.orc_quantize_row_sr.restype = None
+    L.orc_mamba2_step_sr.argtypes = L.orc_mamba2_step.argtypes + [ci, u64, u64]
+    L.orc_mamba2_step_sr.restype = ci
+    L.orc_mamba2_scan_sr.argtypes = L.orc_mamba2_scan.argtypes + [ci, u64, u64]
+    L.orc_mamba2_scan_sr.restype = ci
+    L.orc_mamba2_rows_scan_sr.argtypes = L.orc_mamba2_rows_scan.argtypes + [ci, u64, u64, cl, i64p]
+    L.orc_mamba2_rows_scan_sr.restype = ci
+    L.orc_delta_step_sr.argtypes = L.orc_delta_step.argtypes + [ci, u64, u64]
+    L.orc_delta_step_sr.restype = ci
     return L
 
 
@@ -177,16 +195,57 @@ def decay(dt: float, A: float) -> float:
     return lib().orc_decay(ctypes.c_float(dt), ctypes.c_float(A))
 
 
+def splitmix64(seed: int, i: int) -> int:
+    """Output number ``i`` (>= 1) of SplitMix64 started at ``seed``."""
+    return int(lib().orc_splitmix64(seed, i))
+
+
+def sr_uniform(seed: int, step: int, rows: int, r: int, n_len: int, n: int) -> float:
+    """The uniform entry ``n`` of state row ``r`` draws at token ``step``."""
+    return float(lib().orc_sr_uniform(seed, step, rows, r, n_len, n))
+
+
+def sr_row_uniforms(seed: int, step: int, rows: int, r: int, n_len: int) -> np.ndarray:
+    """The ``n_len`` uniforms of state row ``r`` at token ``step``."""
+    U = np.empty(n_len, np.float32)
+    lib().orc_sr_row_uniforms(seed, step, rows, r, n_len, _f(U))
+    return U
+
+
+def quantize_row_sr(h: np.ndarray, fmt: str, U: np.ndarray | None):
+    """One row refit and rounded; stochastically with uniforms ``U`` (same length), or to
+    nearest when ``U`` is None.  Returns (code, scale, zero)."""
+    h = _c32(h)
+    n = h.shape[0]
+    bits, asym = FORMATS[fmt]
+    code = np.empty(n, np.int32)
+    s = np.empty(1, np.float32)
+    z = np.empty(1, np.float32)
+    lib().orc_quantize_row_sr(_f(h), n, bits, asym, _i(code), _f(s), _f(z), None,
+                              None if U is None else _f(_c32(U)))
+    return code, float(s[0]), float(z[0])
+
+
+def _sr_args(sr):
+    """``sr``: None (round to nearest) or (seed, step) of stochastic rounding."""
+    if sr is None:
+        return 0, 0, 0
+    seed, step = sr
+    return 1, seed, step
+
+
 def _ro(readout: str) -> int:
     if readout not in ("post", "pre"):
         raise ValueError("readout must be 'post' or 'pre'")
     return 1 if readout == "pre" else 0
 
 
-def mamba2_step(st: State, x, dt, A, Bm, Cm, D, readout: str = "post", diag: bool = False):
+def mamba2_step(st: State, x, dt, A, Bm, Cm, D, readout: str = "post", diag: bool = False,
+                sr=None):
     """One decode token of one layer.  ``x`` [B][H][P], ``dt`` [B][H], ``A``/``D`` [H],
     ``Bm``/``Cm`` [B][G][N]; updates ``st`` in place and returns ``y`` [B][H][P]
-    (plus the pre-rounding row and the rounded fp32 values when ``diag``)."""
+    (plus the pre-rounding row and the rounded fp32 values when ``diag``).  ``sr``:
+    (seed, step) for stochastic rounding."""
     x, dt, A, Bm, Cm, D = map(_c32, (x, dt, A, Bm, Cm, D))
     Bsz, H, P = x.shape
     G, N = Bm.shape[1], Bm.shape[2]
@@ -194,45 +253,53 @@ def mamba2_step(st: State, x, dt, A, Bm, Cm, D, readout: str = "post", diag: boo
     y = np.empty((Bsz, H, P), np.float32)
     hpre = np.empty((st.rows, N), np.float32) if diag else None
     vq = np.empty((st.rows, N), np.float32) if diag and st.fmt != "fp32" else None
-    rc = lib().orc_mamba2_step(Bsz, H, G, P, N, st.bits, st.asym, _i(st.code), _f(st.scale),
-                               _f(st.zero), _f(st.h), _f(x), _f(dt), _f(A), _f(Bm), _f(Cm), _f(D),
-                               _f(y), _ro(readout), _f(hpre), _f(vq))
+    rc = lib().orc_mamba2_step_sr(Bsz, H, G, P, N, st.bits, st.asym, _i(st.code), _f(st.scale),
+                                  _f(st.zero), _f(st.h), _f(x), _f(dt), _f(A), _f(Bm), _f(Cm),
+                                  _f(D), _f(y), _ro(readout), _f(hpre), _f(vq), *_sr_args(sr))
     assert rc == 0
     return (y, hpre, vq) if diag else y
 
 
-def mamba2_scan(st: State, x, dt, A, Bm, Cm, D, readout: str = "post"):
+def mamba2_scan(st: State, x, dt, A, Bm, Cm, D, readout: str = "post", sr=None):
     """``T`` tokens, the state rounded after each.  ``x`` [B][T][H][P], ``dt`` [B][T][H],
-    ``Bm``/``Cm`` [B][T][G][N]; returns ``y`` [B][T][H][P]."""
+    ``Bm``/``Cm`` [B][T][G][N]; returns ``y`` [B][T][H][P].  ``sr``: (seed, first step)."""
     x, dt, A, Bm, Cm, D = map(_c32, (x, dt, A, Bm, Cm, D))
     Bsz, T, H, P = x.shape
     G, N = Bm.shape[2], Bm.shape[3]
     assert st.rows == Bsz * H * P and st.n == N
     y = np.empty((Bsz, T, H, P), np.float32)
-    rc = lib().orc_mamba2_scan(Bsz, T, H, G, P, N, st.bits, st.asym, _i(st.code), _f(st.scale),
-                               _f(st.zero), _f(st.h), _f(x), _f(dt), _f(A), _f(Bm), _f(Cm), _f(D),
-                               _f(y), _ro(readout))
+    rc = lib().orc_mamba2_scan_sr(Bsz, T, H, G, P, N, st.bits, st.asym, _i(st.code),
+                                  _f(st.scale), _f(st.zero), _f(st.h), _f(x), _f(dt), _f(A), _f(Bm),
+                                  _f(Cm), _f(D), _f(y), _ro(readout), *_sr_args(sr))
     assert rc == 0
     return y
 
 
-def mamba2_rows_scan(st: State, x, dt, A, Bm, Cm, D, readout: str = "post"):
+def mamba2_rows_scan(st: State, x, dt, A, Bm, Cm, D, readout: str = "post", sr=None,
+                     rows: int = 0, row_id=None):
     """``T`` tokens for independent rows with per-row inputs: ``x``/``dt`` [R][T], ``A``/``D`` [R],
-    ``Bm``/``Cm`` [R][T][N]; returns ``y`` [R][T]."""
+    ``Bm``/``Cm`` [R][T][N]; returns ``y`` [R][T].  With ``sr`` = (seed, first step), row i draws
+    the uniforms of state row ``row_id[i]`` of a state of ``rows`` rows."""
     x, dt, A, Bm, Cm, D = map(_c32, (x, dt, A, Bm, Cm, D))
     R, T = x.shape
     N = Bm.shape[2]
     assert st.rows == R and st.n == N
     y = np.empty((R, T), np.float32)
-    rc = lib().orc_mamba2_rows_scan(R, T, N, st.bits, st.asym, _i(st.code), _f(st.scale),
-                                    _f(st.zero), _f(st.h), _f(x), _f(dt), _f(A), _f(Bm), _f(Cm),
-                                    _f(D), _f(y), _ro(readout))
+    ids = None
+    if sr is not None:
+        ids = np.ascontiguousarray(row_id, np.int64)
+        assert ids.shape == (R,) and rows > 0
+    rc = lib().orc_mamba2_rows_scan_sr(R, T, N, st.bits, st.asym, _i(st.code), _f(st.scale),
+                                       _f(st.zero), _f(st.h), _f(x), _f(dt), _f(A), _f(Bm), _f(Cm),
+                                       _f(D), _f(y), _ro(readout), *_sr_args(sr), rows,
+                                       None if ids is None else
+                                       ids.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)))
     assert rc == 0
     return y
 
 
 def delta_step(st: State, q, k, v, alpha, beta, Bsz: int, H: int, readout: str = "post",
-               diag: bool = False):
+               diag: bool = False, sr=None):
     """One delta-rule step for ``Bsz*H`` matrices of ``dk`` rows by ``dv``: ``q``/``k`` [B][H][dk],
     ``v`` [B][H][dv], ``alpha``/``beta`` [B][H]; returns ``o`` [B][H][dv]."""
     q, k, v, alpha, beta = map(_c32, (q, k, v, alpha, beta))
@@ -241,8 +308,8 @@ def delta_step(st: State, q, k, v, alpha, beta, Bsz: int, H: int, readout: str =
     o = np.empty((Bsz, H, dv), np.float32)
     Spre = np.empty((st.rows, dv), np.float32) if diag else None
     vq = np.empty((st.rows, dv), np.float32) if diag and st.fmt != "fp32" else None
-    rc = lib().orc_delta_step(Bsz, H, dk, dv, st.bits, st.asym, _i(st.code), _f(st.scale),
-                              _f(st.zero), _f(st.h), _f(q), _f(k), _f(v), _f(alpha), _f(beta),
-                              _f(o), _ro(readout), _f(Spre), _f(vq))
+    rc = lib().orc_delta_step_sr(Bsz, H, dk, dv, st.bits, st.asym, _i(st.code), _f(st.scale),
+                                 _f(st.zero), _f(st.h), _f(q), _f(k), _f(v), _f(alpha), _f(beta),
+                                 _f(o), _ro(readout), _f(Spre), _f(vq), *_sr_args(sr))
     assert rc == 0
     return (o, Spre, vq) if diag else o

@@ -25,6 +25,10 @@
  *               codes in [0, 2^b-1]
  *  refit every step from the new fp32 row.
  *
+ *  Rounding is to nearest, or stochastic (README, Findings 9): the code is
+ *  floor(v + U) for the exact v = h*inv + z and U uniform in [0, 1) drawn from
+ *  SplitMix64 by (seed, token, state row, entry); the grid is the same.
+ *
  *  Delta rule (GDN/KDA-style), one dk x dv matrix S per (sequence, head) --
  *  "Mamba state quantization for inference", sections "Mamba state
  *  quantization changes persistent state" and "Quantization error returns on
@@ -105,6 +109,47 @@ static double rne_sum(double p, double z)
     return k + z;
 }
 
+/* Stochastic rounding ("ssm-state-quantization" README, Findings 9: the state
+ * rounded stochastically instead of to nearest).  The code is floor(v + U)
+ * for the exact real v = h*inv + z and a uniform U in [0, 1): it rounds up
+ * with probability equal to the fractional part of v.  floor(p) and p - floor(p)
+ * are exact in double, and so is 1 - U (U has 24 bits), so the decision
+ * frac >= 1 - U is exact. */
+static double sr_sum(double p, double z, float u)
+{
+    double f = floor(p);
+    double r = p - f;
+    return f + z + (r >= 1.0 - (double)u ? 1.0 : 0.0);
+}
+
+/* SplitMix64 (Steele, Lea and Flood, "Fast splittable pseudorandom number
+ * generators", OOPSLA 2014): output number i >= 1 of the generator whose state
+ * starts at `seed`, i.e. the state advanced i times by the golden gamma and
+ * passed through the finalizer. */
+uint64_t orc_splitmix64(uint64_t seed, uint64_t i)
+{
+    uint64_t x = seed + i * 0x9E3779B97F4A7C15ull;
+    x = (x ^ (x >> 30)) * 0xBF58476D1CE4E5B9ull;
+    x = (x ^ (x >> 27)) * 0x94D049BB133111EBull;
+    return x ^ (x >> 31);
+}
+
+/* The uniform that entry n of state row r draws at token `step`: the top 24
+ * bits of output number ctr + 1, ctr = (step*rows + r)*N + n, scaled by 2^-24. */
+float orc_sr_uniform(uint64_t seed, uint64_t step, int64_t rows, int64_t r, int N, int n)
+{
+    uint64_t ctr = (step * (uint64_t)rows + (uint64_t)r) * (uint64_t)N + (uint64_t)n;
+    return (float)(orc_splitmix64(seed, ctr + 1) >> 40) * (1.0f / 16777216.0f);
+}
+
+/* the N uniforms of state row r at token `step` */
+void orc_sr_row_uniforms(uint64_t seed, uint64_t step, int64_t rows, int64_t r, int N, float *U)
+{
+    int n;
+    for (n = 0; n < N; ++n)
+        U[n] = orc_sr_uniform(seed, step, rows, r, N, n);
+}
+
 static float sign_of(float c)
 {
     if (c > 0.0f)
@@ -117,9 +162,11 @@ static float sign_of(float c)
 /* Quantize the n entries of h with a b-bit grid (bits in 2..8).  Writes the
  * integer codes, the scale and the zero point (0 for the symmetric grid).
  * v_out, if not NULL, receives fl(h_n*inv), the value that is rounded (to
- * within half an ulp: the rounding itself uses the exact product). */
-void orc_quantize_row(const float *h, int n, int bits, int asym, int32_t *code, float *s_out,
-                      float *z_out, float *v_out)
+ * within half an ulp: the rounding itself uses the exact product).  U NULL:
+ * round to nearest; else U[i] in [0, 1) rounds entry i stochastically.  The
+ * grid (scale, zero point) does not depend on the rounding. */
+void orc_quantize_row_sr(const float *h, int n, int bits, int asym, int32_t *code, float *s_out,
+                         float *z_out, float *v_out, const float *U)
 {
     int i;
     if (asym) {
@@ -148,7 +195,8 @@ void orc_quantize_row(const float *h, int n, int bits, int asym, int32_t *code, 
         float z = (float)(-rne_sum((double)mn * (double)inv, 0.0)) + 0.0f; /* +0, never -0 */
         for (i = 0; i < n; ++i) {
             float v = h[i] * inv;
-            double t = rne_sum((double)h[i] * (double)inv, (double)z);
+            double p = (double)h[i] * (double)inv;
+            double t = U ? sr_sum(p, (double)z, U[i]) : rne_sum(p, (double)z);
             if (t < 0.0)
                 t = 0.0;
             if (t > (double)cmax)
@@ -181,7 +229,8 @@ void orc_quantize_row(const float *h, int n, int bits, int asym, int32_t *code, 
         float inv = 1.0f / s;
         for (i = 0; i < n; ++i) {
             float v = h[i] * inv;
-            double t = rne_sum((double)h[i] * (double)inv, 0.0);
+            double p = (double)h[i] * (double)inv;
+            double t = U ? sr_sum(p, 0.0, U[i]) : rne_sum(p, 0.0);
             if (t < -(double)cmax)
                 t = -(double)cmax;
             if (t > (double)cmax)
@@ -193,6 +242,12 @@ void orc_quantize_row(const float *h, int n, int bits, int asym, int32_t *code, 
         *s_out = s;
         *z_out = 0.0f;
     }
+}
+
+void orc_quantize_row(const float *h, int n, int bits, int asym, int32_t *code, float *s_out,
+                      float *z_out, float *v_out)
+{
+    orc_quantize_row_sr(h, n, bits, asym, code, s_out, z_out, v_out, NULL);
 }
 
 void orc_dequantize_row(const int32_t *code, int n, float s, float z, float *out)
@@ -232,7 +287,7 @@ void orc_dequantize_rows(int64_t rows, int n, const int32_t *code, const float *
 static float mamba2_row_step(int N, int bits, int asym, int32_t *code, float *s, float *z,
                              float *h, float x, float dt, float A, const float *Bn,
                              const float *Cn, float D, int readout_pre, float *hpre, float *vq,
-                             float *work)
+                             float *work, const float *U)
 {
     int n;
     float lam = orc_decay(dt, A);
@@ -265,7 +320,7 @@ static float mamba2_row_step(int N, int bits, int asym, int32_t *code, float *s,
         for (n = 0; n < N; ++n)
             acc += (double)Cn[n] * (double)work[n];
     }
-    orc_quantize_row(work, N, bits, asym, code, s, z, vq);
+    orc_quantize_row_sr(work, N, bits, asym, code, s, z, vq, U);
     if (!readout_pre) {
         orc_dequantize_row(code, N, *s, *z, work);
         for (n = 0; n < N; ++n)
@@ -280,18 +335,23 @@ static float mamba2_row_step(int N, int bits, int asym, int32_t *code, float *s,
  *   x [Bsz][H][P], dt [Bsz][H], A [H], Bm/Cm [Bsz][G][N], D [H], y [Bsz][H][P]
  *   hpre, vq: optional [Bsz][H][P][N] diagnostics.
  * Returns 0, or -1 on bad sizes. */
-int orc_mamba2_step(int Bsz, int H, int G, int P, int N, int bits, int asym, int32_t *code,
-                    float *s, float *z, float *h, const float *x, const float *dt, const float *A,
-                    const float *Bm, const float *Cm, const float *D, float *y, int readout_pre,
-                    float *hpre, float *vq)
+int orc_mamba2_step_sr(int Bsz, int H, int G, int P, int N, int bits, int asym, int32_t *code,
+                       float *s, float *z, float *h, const float *x, const float *dt, const float *A,
+                       const float *Bm, const float *Cm, const float *D, float *y, int readout_pre,
+                       float *hpre, float *vq, int sr, uint64_t seed, uint64_t step)
 {
     int b, hh, p;
-    float *work;
+    float *work, *U;
+    int64_t rows = (int64_t)Bsz * H * P;
     if (Bsz <= 0 || H <= 0 || G <= 0 || P <= 0 || N <= 0 || H % G != 0)
         return -1;
     work = (float *)malloc(sizeof(float) * (size_t)N);
-    if (!work)
+    U = (float *)malloc(sizeof(float) * (size_t)N);
+    if (!work || !U) {
+        free(work);
+        free(U);
         return -1;
+    }
     for (b = 0; b < Bsz; ++b)
         for (hh = 0; hh < H; ++hh) {
             int g = hh / (H / G);
@@ -300,22 +360,35 @@ int orc_mamba2_step(int Bsz, int H, int G, int P, int N, int bits, int asym, int
             float dtv = dt[(int64_t)b * H + hh];
             for (p = 0; p < P; ++p) {
                 int64_t r = ((int64_t)b * H + hh) * P + p;
+                if (sr)
+                    orc_sr_row_uniforms(seed, step, rows, r, N, U);
                 y[r] = mamba2_row_step(N, bits, asym, code ? code + r * N : NULL, s ? s + r : NULL,
                                        z ? z + r : NULL, h ? h + r * N : NULL, x[r], dtv, A[hh],
                                        Bn, Cn, D[hh], readout_pre, hpre ? hpre + r * N : NULL,
-                                       vq ? vq + r * N : NULL, work);
+                                       vq ? vq + r * N : NULL, work, sr ? U : NULL);
             }
         }
     free(work);
+    free(U);
     return 0;
+}
+
+int orc_mamba2_step(int Bsz, int H, int G, int P, int N, int bits, int asym, int32_t *code,
+                    float *s, float *z, float *h, const float *x, const float *dt, const float *A,
+                    const float *Bm, const float *Cm, const float *D, float *y, int readout_pre,
+                    float *hpre, float *vq)
+{
+    return orc_mamba2_step_sr(Bsz, H, G, P, N, bits, asym, code, s, z, h, x, dt, A, Bm, Cm, D, y,
+                              readout_pre, hpre, vq, 0, 0, 0);
 }
 
 /* T tokens of one layer, the state rounded after every token: plain repetition
  * of orc_mamba2_step on token-t slices.
  *   x [Bsz][T][H][P], dt [Bsz][T][H], Bm/Cm [Bsz][T][G][N], y [Bsz][T][H][P] */
-int orc_mamba2_scan(int Bsz, int T, int H, int G, int P, int N, int bits, int asym, int32_t *code,
-                    float *s, float *z, float *h, const float *x, const float *dt, const float *A,
-                    const float *Bm, const float *Cm, const float *D, float *y, int readout_pre)
+int orc_mamba2_scan_sr(int Bsz, int T, int H, int G, int P, int N, int bits, int asym,
+                       int32_t *code, float *s, float *z, float *h, const float *x, const float *dt,
+                       const float *A, const float *Bm, const float *Cm, const float *D, float *y,
+                       int readout_pre, int sr, uint64_t seed, uint64_t step)
 {
     int t, b;
     int rc = 0;
@@ -339,8 +412,9 @@ int orc_mamba2_scan(int Bsz, int T, int H, int G, int P, int N, int bits, int as
             memcpy(Bs + (size_t)b * G * N, Bm + ((size_t)b * T + t) * G * N, sizeof(float) * G * N);
             memcpy(Cs + (size_t)b * G * N, Cm + ((size_t)b * T + t) * G * N, sizeof(float) * G * N);
         }
-        rc = orc_mamba2_step(Bsz, H, G, P, N, bits, asym, code, s, z, h, xs, dts, A, Bs, Cs, D, ys,
-                             readout_pre, NULL, NULL);
+        /* token t draws the uniforms of step + t */
+        rc = orc_mamba2_step_sr(Bsz, H, G, P, N, bits, asym, code, s, z, h, xs, dts, A, Bs, Cs, D,
+                                ys, readout_pre, NULL, NULL, sr, seed, step + (uint64_t)t);
         if (rc)
             goto done;
         for (b = 0; b < Bsz; ++b)
@@ -355,28 +429,54 @@ done:
     return rc;
 }
 
+int orc_mamba2_scan(int Bsz, int T, int H, int G, int P, int N, int bits, int asym, int32_t *code,
+                    float *s, float *z, float *h, const float *x, const float *dt, const float *A,
+                    const float *Bm, const float *Cm, const float *D, float *y, int readout_pre)
+{
+    return orc_mamba2_scan_sr(Bsz, T, H, G, P, N, bits, asym, code, s, z, h, x, dt, A, Bm, Cm, D, y,
+                              readout_pre, 0, 0, 0);
+}
+
 /* T tokens for R independent rows, each with its own inputs (for checking
  * sampled rows of a large state):
  *   code/h [R][N], s/z [R], x/dt/y [R][T], A/D [R], Bm/Cm [R][T][N] */
+int orc_mamba2_rows_scan_sr(int64_t R, int T, int N, int bits, int asym, int32_t *code, float *s,
+                            float *z, float *h, const float *x, const float *dt, const float *A,
+                            const float *Bm, const float *Cm, const float *D, float *y,
+                            int readout_pre, int sr, uint64_t seed, uint64_t step, int64_t rows,
+                            const int64_t *row_id)
+{
+    int64_t r;
+    int t;
+    float *work = (float *)malloc(sizeof(float) * (size_t)N);
+    float *U = (float *)malloc(sizeof(float) * (size_t)N);
+    if (!work || !U) {
+        free(work);
+        free(U);
+        return -1;
+    }
+    for (r = 0; r < R; ++r)
+        for (t = 0; t < T; ++t) {
+            int64_t rt = r * T + t;
+            if (sr)
+                orc_sr_row_uniforms(seed, step + (uint64_t)t, rows, row_id[r], N, U);
+            y[rt] = mamba2_row_step(N, bits, asym, code ? code + r * N : NULL, s ? s + r : NULL,
+                                    z ? z + r : NULL, h ? h + r * N : NULL, x[rt], dt[rt], A[r],
+                                    Bm + rt * N, Cm + rt * N, D[r], readout_pre, NULL, NULL, work,
+                                    sr ? U : NULL);
+        }
+    free(work);
+    free(U);
+    return 0;
+}
+
 int orc_mamba2_rows_scan(int64_t R, int T, int N, int bits, int asym, int32_t *code, float *s,
                          float *z, float *h, const float *x, const float *dt, const float *A,
                          const float *Bm, const float *Cm, const float *D, float *y,
                          int readout_pre)
 {
-    int64_t r;
-    int t;
-    float *work = (float *)malloc(sizeof(float) * (size_t)N);
-    if (!work)
-        return -1;
-    for (r = 0; r < R; ++r)
-        for (t = 0; t < T; ++t) {
-            int64_t rt = r * T + t;
-            y[rt] = mamba2_row_step(N, bits, asym, code ? code + r * N : NULL, s ? s + r : NULL,
-                                    z ? z + r : NULL, h ? h + r * N : NULL, x[rt], dt[rt], A[r],
-                                    Bm + rt * N, Cm + rt * N, D[r], readout_pre, NULL, NULL, work);
-        }
-    free(work);
-    return 0;
+    return orc_mamba2_rows_scan_sr(R, T, N, bits, asym, code, s, z, h, x, dt, A, Bm, Cm, D, y,
+                                   readout_pre, 0, 0, 0, 0, NULL);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -387,7 +487,8 @@ int orc_mamba2_rows_scan(int64_t R, int T, int N, int bits, int asym, int32_t *c
  * v [dv]; o [dv].  Spre, vq: optional [dk][dv] diagnostics. */
 static int delta_matrix_step(int dk, int dv, int bits, int asym, int32_t *code, float *s, float *z,
                              float *S, const float *q, const float *k, const float *v, float alpha,
-                             float beta, float *o, int readout_pre, float *Spre, float *vq)
+                             float beta, float *o, int readout_pre, float *Spre, float *vq,
+                             const float *U)
 {
     int i, j;
     float *u = (float *)malloc(sizeof(float) * (size_t)dv);
@@ -451,8 +552,9 @@ static int delta_matrix_step(int dk, int dv, int bits, int asym, int32_t *code, 
         memcpy(S, Sn, sizeof(float) * (size_t)dk * dv);
     } else {
         for (i = 0; i < dk; ++i)
-            orc_quantize_row(Sn + (int64_t)i * dv, dv, bits, asym, code + (int64_t)i * dv, s + i,
-                             z + i, vq ? vq + (int64_t)i * dv : NULL);
+            orc_quantize_row_sr(Sn + (int64_t)i * dv, dv, bits, asym, code + (int64_t)i * dv, s + i,
+                                z + i, vq ? vq + (int64_t)i * dv : NULL,
+                                U ? U + (int64_t)i * dv : NULL);
         if (!readout_pre) {
             for (i = 0; i < dk; ++i) {
                 orc_dequantize_row(code + (int64_t)i * dv, dv, s[i], z[i], Sn + (int64_t)i * dv);
@@ -475,23 +577,45 @@ static int delta_matrix_step(int dk, int dv, int bits, int asym, int32_t *code, 
  *   code [Bsz][H][dk][dv], s/z [Bsz][H][dk] or S [Bsz][H][dk][dv]
  *   q, k [Bsz][H][dk], v [Bsz][H][dv], alpha/beta [Bsz][H], o [Bsz][H][dv]
  *   Spre, vq: optional [Bsz][H][dk][dv] */
+int orc_delta_step_sr(int Bsz, int H, int dk, int dv, int bits, int asym, int32_t *code, float *s,
+                      float *z, float *S, const float *q, const float *k, const float *v,
+                      const float *alpha, const float *beta, float *o, int readout_pre, float *Spre,
+                      float *vq, int sr, uint64_t seed, uint64_t step)
+{
+    int64_t m, nm = (int64_t)Bsz * H, i;
+    float *U = NULL;
+    if (Bsz <= 0 || H <= 0 || dk <= 0 || dv <= 0)
+        return -1;
+    if (sr) {
+        U = (float *)malloc(sizeof(float) * (size_t)dk * dv);
+        if (!U)
+            return -1;
+    }
+    for (m = 0; m < nm; ++m) {
+        int64_t mat = m * dk * dv;
+        int rc;
+        if (sr) /* key row i of matrix m is state row m*dk + i */
+            for (i = 0; i < dk; ++i)
+                orc_sr_row_uniforms(seed, step, nm * dk, m * dk + i, dv, U + i * dv);
+        rc = delta_matrix_step(dk, dv, bits, asym, code ? code + mat : NULL,
+                               s ? s + m * dk : NULL, z ? z + m * dk : NULL,
+                               S ? S + mat : NULL, q + m * dk, k + m * dk, v + m * dv,
+                               alpha[m], beta[m], o + m * dv, readout_pre,
+                               Spre ? Spre + mat : NULL, vq ? vq + mat : NULL, U);
+        if (rc) {
+            free(U);
+            return rc;
+        }
+    }
+    free(U);
+    return 0;
+}
+
 int orc_delta_step(int Bsz, int H, int dk, int dv, int bits, int asym, int32_t *code, float *s,
                    float *z, float *S, const float *q, const float *k, const float *v,
                    const float *alpha, const float *beta, float *o, int readout_pre, float *Spre,
                    float *vq)
 {
-    int64_t m, nm = (int64_t)Bsz * H;
-    if (Bsz <= 0 || H <= 0 || dk <= 0 || dv <= 0)
-        return -1;
-    for (m = 0; m < nm; ++m) {
-        int64_t mat = m * dk * dv;
-        int rc = delta_matrix_step(dk, dv, bits, asym, code ? code + mat : NULL,
-                                   s ? s + m * dk : NULL, z ? z + m * dk : NULL,
-                                   S ? S + mat : NULL, q + m * dk, k + m * dk, v + m * dv,
-                                   alpha[m], beta[m], o + m * dv, readout_pre,
-                                   Spre ? Spre + mat : NULL, vq ? vq + mat : NULL);
-        if (rc)
-            return rc;
-    }
-    return 0;
+    return orc_delta_step_sr(Bsz, H, dk, dv, bits, asym, code, s, z, S, q, k, v, alpha, beta, o,
+                             readout_pre, Spre, vq, 0, 0, 0);
 }

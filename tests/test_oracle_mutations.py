@@ -14,6 +14,7 @@ import pytest
 
 import oracle
 from tests import test_oracle_pins as pins
+from tests import test_oracle_sr as sr_pins
 
 SRC = open(os.path.join(os.path.dirname(oracle.__file__), "ssq_oracle.c")).read()
 
@@ -52,12 +53,27 @@ MUTATIONS = [
     ("delta u uses the wrong key index", "a += (double)k[i] * (double)S[(int64_t)i * dv + j];",
      "a += (double)k[j % dk] * (double)S[(int64_t)i * dv + j];"),
     ("dequantization scale dropped", "        out[i] = s * d;", "        out[i] = d;"),
+    ("stochastic rounding compares with U, not 1 - U",
+     "return f + z + (r >= 1.0 - (double)u ? 1.0 : 0.0);", "return f + z + (r > (double)u ? 1.0 : 0.0);"),
+    ("stochastic rounding drops the zero point",
+     "return f + z + (r >= 1.0 - (double)u ? 1.0 : 0.0);", "return f + (r >= 1.0 - (double)u ? 1.0 : 0.0);"),
+    ("uniform counter ignores the token",
+     "uint64_t ctr = (step * (uint64_t)rows + (uint64_t)r) * (uint64_t)N + (uint64_t)n;",
+     "uint64_t ctr = ((uint64_t)r) * (uint64_t)N + (uint64_t)n;"),
+    ("uniform keeps 24 low bits", "return (float)(orc_splitmix64(seed, ctr + 1) >> 40) * (1.0f / 16777216.0f);",
+     "return (float)(orc_splitmix64(seed, ctr + 1) & 0xFFFFFF) * (1.0f / 16777216.0f);"),
+    ("scan reuses the first token's uniforms", "ys, readout_pre, NULL, NULL, sr, seed, step + (uint64_t)t);",
+     "ys, readout_pre, NULL, NULL, sr, seed, step);"),
+    ("delta draws the uniforms of the matrix's first row",
+     "sr_row_uniforms(seed, step, nm * dk, m * dk + i, dv, U + i * dv);",
+     "sr_row_uniforms(seed, step, nm * dk, m * dk, dv, U + i * dv);"),
 ]
 
 
 def _pin_cases():
     cases = []
-    for name, fn in inspect.getmembers(pins, inspect.isfunction):
+    members = inspect.getmembers(pins, inspect.isfunction) + inspect.getmembers(sr_pins, inspect.isfunction)
+    for name, fn in members:
         if not name.startswith("test_"):
             continue
         marks = getattr(fn, "pytestmark", [])
