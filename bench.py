@@ -41,6 +41,10 @@ WORKLOADS = {
                          desc="Mamba-2 370m-shaped decode step: 48 layers x 32 heads x 64 x 128, batch 256, "
                               "int4 asymmetric state (per-row fp32 scale + zero point), seeded random state "
                               "with 5% x20 outlier rows"),
+    "m2_370m_int4_sr": dict(kind="m2", layers=48, B=256, H=32, P=64, fmt="int4_asym", init="random",
+                            rounding="stochastic",
+                            desc="as m2_370m_int4 with stochastic rounding of the codes (SplitMix64 "
+                                 "uniforms per entry); graph replays reuse the captured token"),
     "delta_int8": dict(kind="delta", layers=30, B=256, H=32, P=128, fmt="int8_asym", init="random",
                        desc="Delta-rule (GDN/KDA-style) decode step: 30 layers x 32 heads x 128 x 128, batch 256, "
                             "int8 asymmetric per-row state, seeded random state with 5% x20 outlier rows"),
@@ -139,6 +143,8 @@ def main():
             del h, out
         else:
             st = ssq.ssq_alloc_state(desc, storage=storage)
+        if wl.get("rounding") == "stochastic":
+            ssq.ssq_set_rounding(st, ssq.SSQ_ROUND_STOCHASTIC, args.seed * 1000 + layer, 0)
         states.append(st)
         storages.append(storage)
     torch.cuda.synchronize()

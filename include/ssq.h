@@ -93,6 +93,8 @@ typedef enum { SSQ_MAMBA2 = 0, SSQ_DELTA = 1 } ssq_kind;
 
 typedef enum { SSQ_READ_POST_QUANT = 0, SSQ_READ_PRE_QUANT = 1 } ssq_readout;
 
+typedef enum { SSQ_ROUND_NEAREST = 0, SSQ_ROUND_STOCHASTIC = 1 } ssq_rounding;
+
 /* Shape and format of one layer's state for all sequences of a batch. */
 typedef struct {
     int32_t kind;          /* ssq_kind */
@@ -153,6 +155,27 @@ ssq_status ssq_free_state(ssq_state *state);
 /* The description, storage pointer and layout of a state (any out pointer
  * may be NULL). */
 ssq_status ssq_state_info(const ssq_state *state, ssq_desc *desc, void **storage, ssq_layout *layout);
+
+/* How the state's codes are rounded by the calls below ("ssm-state-quantization"
+ * README, Findings 9: stochastic rounding of the state as the alternative to
+ * round to nearest).  SSQ_ROUND_NEAREST (the default) is the rule above.
+ * SSQ_ROUND_STOCHASTIC keeps the same grid (scale, zero point) and sets each
+ * code to floor(v + U) for the exact real v = h'*inv + z', clamped to the
+ * code range, so a row rounds up with probability equal to the fractional
+ * part of v.  Entry n of state row r at token t draws U = (top 24 bits of
+ * SplitMix64 output number ctr + 1 for `seed`) * 2^-24 with
+ * ctr = (t*rows + r)*row_len + n (Steele, Lea and Flood, "Fast splittable
+ * pseudorandom number generators", OOPSLA 2014), rows = the state's rows.
+ * `step` is the token the next call starts at: ssq_decode_step and
+ * ssq_delta_step use it and advance it by one, ssq_scan uses step .. step+T-1
+ * and advances it by T, at enqueue time.  A captured graph replays the tokens
+ * it was captured with.  The fp32 state is never rounded:
+ * SSQ_ROUND_STOCHASTIC on it gives SSQ_ERR_UNSUPPORTED.  Host-side only:
+ * changes nothing already enqueued. */
+ssq_status ssq_set_rounding(ssq_state *state, int32_t mode, uint64_t seed, uint64_t step);
+
+/* The state's rounding mode, seed and next token (any out pointer may be NULL). */
+ssq_status ssq_get_rounding(const ssq_state *state, int32_t *mode, uint64_t *seed, uint64_t *step);
 
 /* One Mamba-2 decode token for every row of the layer (README, Setup: decay
  * lambda = exp(dt*A) per head, write dt*B*x, per-row refit every step, round

@@ -27,6 +27,8 @@ SSQ_FP32, SSQ_INT8_SYM, SSQ_INT8_ASYM, SSQ_INT4_SYM, SSQ_INT4_ASYM = range(5)
 SSQ_MAMBA2, SSQ_DELTA = 0, 1
 # ssq_readout
 SSQ_READ_POST_QUANT, SSQ_READ_PRE_QUANT = 0, 1
+# ssq_rounding
+SSQ_ROUND_NEAREST, SSQ_ROUND_STOCHASTIC = 0, 1
 
 FORMAT_NAMES = {"fp32": SSQ_FP32, "int8_sym": SSQ_INT8_SYM, "int8_asym": SSQ_INT8_ASYM,
                 "int4_sym": SSQ_INT4_SYM, "int4_asym": SSQ_INT4_ASYM}
@@ -80,6 +82,11 @@ def _load():
     L.ssq_status_string.restype = ctypes.c_char_p
     L.ssq_last_error.argtypes = []
     L.ssq_last_error.restype = ctypes.c_char_p
+    u64 = ctypes.c_uint64
+    L.ssq_set_rounding.argtypes = [vp, ctypes.c_int32, u64, u64]
+    L.ssq_set_rounding.restype = st
+    L.ssq_get_rounding.argtypes = [vp, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(u64), ctypes.POINTER(u64)]
+    L.ssq_get_rounding.restype = st
     return L
 
 
@@ -206,6 +213,19 @@ def ssq_state_info(state: State):
     _check(lib.ssq_state_info(state.handle, ctypes.byref(d), ctypes.byref(ptr), ctypes.byref(lay)),
            "ssq_state_info")
     return d, ptr.value, lay
+
+
+def ssq_set_rounding(state: State, mode: int, seed: int = 0, step: int = 0):
+    """Round the state's codes to nearest or stochastically (seed, next token)."""
+    _check(lib.ssq_set_rounding(state.handle, mode, seed, step), "ssq_set_rounding")
+
+
+def ssq_get_rounding(state: State):
+    """(mode, seed, next token) of a state."""
+    m, sd, sp = ctypes.c_int32(), ctypes.c_uint64(), ctypes.c_uint64()
+    _check(lib.ssq_get_rounding(state.handle, ctypes.byref(m), ctypes.byref(sd), ctypes.byref(sp)),
+           "ssq_get_rounding")
+    return m.value, sd.value, sp.value
 
 
 def _sizes(state: State, kind: int, *sizes):

@@ -1,6 +1,7 @@
 """Build ``libssq.so`` (the HIP kernels and the C ABI of ``include/ssq.h``) for gfx950.
 
-Usage: ``python -m mamba_decode_amd.build`` (or ``__graft_entry__.build()``).
+Usage: ``python mamba_decode_amd/build.py`` (or ``__graft_entry__.build()``); it
+does not import the package, which loads the library it builds.
 Cross-compiles on a machine without a GPU; the library is written next to
 this file so that it travels with the source tree.
 """

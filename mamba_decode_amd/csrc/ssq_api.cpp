@@ -21,6 +21,9 @@ struct ssq_state {
     void* storage;
     bool owned;
     int device;
+    int32_t rounding; // ssq_rounding
+    uint64_t sr_seed; // stochastic rounding: generator seed
+    uint64_t sr_step; // stochastic rounding: the token the next call starts at
 };
 
 namespace {
@@ -181,6 +184,9 @@ ssq_status ssq_alloc_state(const ssq_desc* desc, void* storage, const float* ini
     st->device = dev;
     st->owned = false;
     st->storage = storage;
+    st->rounding = SSQ_ROUND_NEAREST;
+    st->sr_seed = 0;
+    st->sr_step = 0;
     if (!storage) {
         void* p = nullptr;
         e = hipMalloc(&p, lay.total_bytes);
@@ -232,6 +238,45 @@ ssq_status ssq_state_info(const ssq_state* st, ssq_desc* desc, void** storage, s
     return ok();
 }
 
+// the stochastic-rounding arguments of the next call on a state
+static ssq::SrArgs sr_args(const ssq_state* st)
+{
+    ssq::SrArgs r{};
+    r.on = st->rounding == SSQ_ROUND_STOCHASTIC;
+    r.seed = st->sr_seed;
+    r.step = st->sr_step;
+    r.rows = (int64_t)st->lay.rows;
+    return r;
+}
+
+// a call that was enqueued consumed `tokens` tokens of the state's random stream
+static void advance(ssq_state* st, uint64_t tokens)
+{
+    if (st->rounding == SSQ_ROUND_STOCHASTIC) st->sr_step += tokens;
+}
+
+ssq_status ssq_set_rounding(ssq_state* st, int32_t mode, uint64_t seed, uint64_t step)
+{
+    SSQ_REQUIRE(st, SSQ_ERR_INVALID_ARG, "state is NULL");
+    SSQ_REQUIRE(mode == SSQ_ROUND_NEAREST || mode == SSQ_ROUND_STOCHASTIC, SSQ_ERR_INVALID_ARG,
+                "unknown rounding mode");
+    SSQ_REQUIRE(mode == SSQ_ROUND_NEAREST || fmt_quant(st->desc.format), SSQ_ERR_UNSUPPORTED,
+                "the fp32 state is not rounded");
+    st->rounding = mode;
+    st->sr_seed = seed;
+    st->sr_step = step;
+    return ok();
+}
+
+ssq_status ssq_get_rounding(const ssq_state* st, int32_t* mode, uint64_t* seed, uint64_t* step)
+{
+    SSQ_REQUIRE(st, SSQ_ERR_INVALID_ARG, "state is NULL");
+    if (mode) *mode = st->rounding;
+    if (seed) *seed = st->sr_seed;
+    if (step) *step = st->sr_step;
+    return ok();
+}
+
 static ssq_status fill_m2(ssq_state* st, const float* x, const float* dt, const float* A, const float* B,
                           const float* C, const float* D, float* y, int32_t readout, ssq::M2Args* a)
 {
@@ -271,9 +316,12 @@ ssq_status ssq_decode_step(ssq_state* st, const float* x, const float* dt, const
     ssq::M2Args a;
     ssq_status s = fill_m2(st, x, dt, A, B, C, D, y, readout, &a);
     if (s != SSQ_OK) return s;
-    return from_hip(ssq::launch_m2_step(st->desc.format, a, readout == SSQ_READ_PRE_QUANT, num_cus(st->device),
-                                        (hipStream_t)stream),
-                    "decode step launch");
+    a.sr = sr_args(st);
+    s = from_hip(ssq::launch_m2_step(st->desc.format, a, readout == SSQ_READ_PRE_QUANT, num_cus(st->device),
+                                     (hipStream_t)stream),
+                 "decode step launch");
+    if (s == SSQ_OK) advance(st, 1);
+    return s;
 }
 
 ssq_status ssq_scan(ssq_state* st, int32_t T, const float* x, const float* dt, const float* A, const float* B,
@@ -284,8 +332,11 @@ ssq_status ssq_scan(ssq_state* st, int32_t T, const float* x, const float* dt, c
     if (s != SSQ_OK) return s;
     SSQ_REQUIRE(T > 0, SSQ_ERR_INVALID_ARG, "T must be positive");
     a.T = T;
-    return from_hip(ssq::launch_m2_scan(st->desc.format, a, readout == SSQ_READ_PRE_QUANT, (hipStream_t)stream),
-                    "scan launch");
+    a.sr = sr_args(st);
+    s = from_hip(ssq::launch_m2_scan(st->desc.format, a, readout == SSQ_READ_PRE_QUANT, (hipStream_t)stream),
+                 "scan launch");
+    if (s == SSQ_OK) advance(st, (uint64_t)T);
+    return s;
 }
 
 ssq_status ssq_delta_step(ssq_state* st, const float* q, const float* k, const float* v, const float* alpha,
@@ -313,8 +364,11 @@ ssq_status ssq_delta_step(ssq_state* st, const float* q, const float* k, const f
     a.beta = beta;
     a.o = o;
     a.nmat = (int64_t)st->desc.batch * st->desc.nheads;
-    return from_hip(ssq::launch_delta_step(st->desc.format, a, readout == SSQ_READ_PRE_QUANT, (hipStream_t)stream),
-                    "delta step launch");
+    a.sr = sr_args(st);
+    s = from_hip(ssq::launch_delta_step(st->desc.format, a, readout == SSQ_READ_PRE_QUANT, (hipStream_t)stream),
+                 "delta step launch");
+    if (s == SSQ_OK) advance(st, 1);
+    return s;
 }
 
 ssq_status ssq_dequant(const ssq_state* st, float* out, void* stream)

@@ -29,7 +29,7 @@ namespace ssq {
 #define SSQ_DELTA_WAVES 4
 #endif
 
-template <int F, bool PRE>
+template <int F, bool PRE, bool SR>
 __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_delta_step(DeltaArgs a)
 {
     using Tr = Traits<F>;
@@ -165,13 +165,23 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_delta_step(DeltaArgs a
             }
             RowGrid g;
             float f[E];
+            // stochastic rounding: this lane's first counter, (step*rows + row)*128 + j0
+            const uint64_t ctr0 = SR ? ((a.sr.step * (uint64_t)a.sr.rows + (uint64_t)row) * 128u + (uint64_t)j0) : 0;
             if (__all(refit_fast<F>(mn, mx, am, g))) {
+                if constexpr (SR) {
+                    round_codes_sr<F, E>(S, g, a.sr.seed, ctr0, f);
+                } else {
 #pragma unroll
-                for (int e = 0; e < E; ++e) f[e] = __builtin_fmaf(S[e], g.inv, g.Mz);
+                    for (int e = 0; e < E; ++e) f[e] = __builtin_fmaf(S[e], g.inv, g.Mz);
+                }
             } else {
                 g = refit<F>(mn, mx, am);
-                const bool slow_any = Tr::asym && __any(g.slow);
-                round_codes<F, E>(S, g, slow_any, f);
+                if constexpr (SR) {
+                    round_codes_sr<F, E>(S, g, a.sr.seed, ctr0, f);
+                } else {
+                    const bool slow_any = Tr::asym && __any(g.slow);
+                    round_codes<F, E>(S, g, slow_any, f);
+                }
             }
             uint32_t ow[NW];
             pack_codes<F, E>(f, ow);
@@ -210,10 +220,19 @@ template <int F>
 static hipError_t launch_delta_f(DeltaArgs a, bool pre, hipStream_t st)
 {
     const unsigned blocks = (unsigned)a.nmat;
+    if constexpr (Traits<F>::quant) {
+        if (a.sr.on) {
+            if (pre)
+                hipLaunchKernelGGL((k_delta_step<F, true, true>), dim3(blocks), dim3(256), 0, st, a);
+            else
+                hipLaunchKernelGGL((k_delta_step<F, false, true>), dim3(blocks), dim3(256), 0, st, a);
+            return hipGetLastError();
+        }
+    }
     if (pre)
-        hipLaunchKernelGGL((k_delta_step<F, true>), dim3(blocks), dim3(256), 0, st, a);
+        hipLaunchKernelGGL((k_delta_step<F, true, false>), dim3(blocks), dim3(256), 0, st, a);
     else
-        hipLaunchKernelGGL((k_delta_step<F, false>), dim3(blocks), dim3(256), 0, st, a);
+        hipLaunchKernelGGL((k_delta_step<F, false, false>), dim3(blocks), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 

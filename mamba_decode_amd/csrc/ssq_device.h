@@ -319,6 +319,43 @@ __device__ __forceinline__ void round_codes(const float* h, const RowGrid& g, bo
 }
 
 // ---------------------------------------------------------------------------
+// stochastic rounding ("ssm-state-quantization" README, Findings 9): the code
+// is floor(v + U) for the exact real v = h*inv + z and U uniform in [0, 1), on
+// the grid round-to-nearest refits.  U is the top 24 bits of SplitMix64
+// (Steele, Lea and Flood, OOPSLA 2014) output number ctr + 1 for the state's
+// seed: the state advanced ctr + 1 times by the golden gamma, then mixed.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float sr_uniform(uint64_t seed, uint64_t ctr)
+{
+    uint64_t x = seed + (ctr + 1) * 0x9E3779B97F4A7C15ull;
+    x = (x ^ (x >> 30)) * 0xBF58476D1CE4E5B9ull;
+    x = (x ^ (x >> 27)) * 0x94D049BB133111EBull;
+    // the finalizer's last step, x ^= x >> 31, leaves bits 40..63 as they are
+    return (float)(uint32_t)(x >> 40) * (1.0f / 16777216.0f);
+}
+
+// f = 1.5*2^23 + clamp(floor(h*inv + z + U)) for E entries whose uniforms are
+// counters ctr0 .. ctr0 + E - 1.  h*inv is exact in double, floor(p) and
+// p - floor(p) are exact, and 1 - U is exact (24 bits), so the decision to round
+// up, frac >= 1 - U, is exact.
+template <int F, int E>
+__device__ __forceinline__ void round_codes_sr(const float* h, const RowGrid& g, uint64_t seed, uint64_t ctr0,
+                                               float* f)
+{
+    constexpr double lo = (double)Traits<F>::lo;
+    constexpr double hi = (double)Traits<F>::hi;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const double p = (double)h[e] * (double)g.inv;
+        const double fl = floor(p);
+        const float u = sr_uniform(seed, ctr0 + (uint64_t)e);
+        double c = fl + (double)g.zc + ((p - fl) >= 1.0 - (double)u ? 1.0 : 0.0);
+        c = fmin(fmax(c, lo), hi);
+        f[e] = kMagic + (float)c;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // fast refit: the same s, inv and z as refit(), with fewer instructions, for
 // rows inside the ranges where the shortcuts were verified exhaustively
 // (every fp32 mantissa, against IEEE division):

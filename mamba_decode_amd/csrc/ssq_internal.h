@@ -7,6 +7,15 @@
 
 namespace ssq {
 
+// stochastic rounding of the codes: off, or entry n of state row r at token t
+// draws the uniform of SplitMix64 output number ((step + t)*rows + r)*128 + n + 1
+struct SrArgs {
+    int on;
+    uint64_t seed;
+    uint64_t step;
+    int64_t rows;
+};
+
 // Mamba-2 decode step / scan of one layer
 struct M2Args {
     uint8_t* codes; // quantized formats: [rows][128*bits/8]
@@ -23,6 +32,7 @@ struct M2Args {
     int Bsz, H, G, P, T;
     int64_t total_iters;
     int iters_per_wave;
+    SrArgs sr;
 };
 
 // row quantization (state initialisation) and dequantization
@@ -49,6 +59,7 @@ struct DeltaArgs {
     const float* beta;
     float* o;
     int64_t nmat;
+    SrArgs sr;
 };
 
 hipError_t launch_m2_step(int fmt, M2Args a, bool pre, int num_cus, hipStream_t st);

@@ -74,10 +74,12 @@ struct RowStep {
     // ow out; returns y (valid in every lane of the row).  ls = fl(lambda*s) and
     // lz = fl(ls*z) of the old row, w = fl(dt*x), dx = fl(D*x).
     // PACK: pack the new codes into ow; otherwise h ends holding the new codes as floats
-    // (what the next token of a scan starts from)
-    template <bool PACK = true, typename In>
+    // (what the next token of a scan starts from).  SR: round stochastically with the
+    // uniforms of counters ctr0 .. ctr0 + E - 1.
+    template <bool PACK = true, bool SR = false, typename In>
     __device__ __forceinline__ static float run_q(float* h, float ls, float lz, float w, float dx,
-                                                  const In& in, uint32_t* ow, RowGrid& g)
+                                                  const In& in, uint32_t* ow, RowGrid& g, uint64_t sr_seed = 0,
+                                                  uint64_t ctr0 = 0)
     {
         using Tr = Traits<F>;
         // lambda*s*(c - z) + w*B = fma(ls, c, fma(w, B, -ls*z)): the decay acts on the scale
@@ -115,12 +117,20 @@ struct RowStep {
         // h becomes f = 1.5*2^23 + code in place
         if (__all(refit_fast<F>(mn, mx, am, g))) {
             // every row of the wave is inside the verified ranges and needs no clamp
+            if constexpr (SR) {
+                round_codes_sr<F, E>(h, g, sr_seed, ctr0, h);
+            } else {
 #pragma unroll
-            for (int e = 0; e < E; ++e) h[e] = __builtin_fmaf(h[e], g.inv, g.Mz);
+                for (int e = 0; e < E; ++e) h[e] = __builtin_fmaf(h[e], g.inv, g.Mz);
+            }
         } else {
             g = refit<F>(mn, mx, am);
-            const bool slow_any = Tr::asym && __any(g.slow);
-            round_codes<F, E>(h, g, slow_any, h);
+            if constexpr (SR) {
+                round_codes_sr<F, E>(h, g, sr_seed, ctr0, h);
+            } else {
+                const bool slow_any = Tr::asym && __any(g.slow);
+                round_codes<F, E>(h, g, slow_any, h);
+            }
         }
         if constexpr (PACK) pack_codes<F, E>(h, ow);
         if constexpr (PRE) {
@@ -168,7 +178,7 @@ struct RowStep {
 // of a row stores the row's scale, zero point and y (the same value to the same
 // address), so no store sits behind a branch either.  Leftover iterations (fewer
 // than K) are run by a second launch with K = 1.
-template <int F, int LPR, bool PRE, int K, int D, int W>
+template <int F, int LPR, bool PRE, int K, int D, int W, bool SR>
 __global__ __launch_bounds__(256, W) void k_m2_step(M2Args a, int64_t it_base)
 {
     using Tr = Traits<F>;
@@ -291,9 +301,14 @@ __global__ __launch_bounds__(256, W) void k_m2_step(M2Args a, int64_t it_base)
         if constexpr (Tr::quant) {
             uint32_t ow[NW];
             RowGrid g;
+            // this lane's first counter of stochastic rounding: (step*rows + row)*128 + part*E
+            const uint64_t ctr0 =
+                SR ? ((a.sr.step * (uint64_t)a.sr.rows + (uint64_t)(row_first + (int64_t)i * RPW + sub)) * 128u +
+                      (uint64_t)(part * E))
+                   : 0;
             float yv;
-            if constexpr (BCL) yv = RS::run_q(cf, ls, lz, w, dx, rin_l, ow, g);
-            else yv = RS::run_q(cf, ls, lz, w, dx, rin, ow, g);
+            if constexpr (BCL) yv = RS::template run_q<true, SR>(cf, ls, lz, w, dx, rin_l, ow, g, a.sr.seed, ctr0);
+            else yv = RS::template run_q<true, SR>(cf, ls, lz, w, dx, rin, ow, g, a.sr.seed, ctr0);
             buf_store_words<NW, kAuxStream>(r_w, off_w, sw, ow);
             buf_store_f32<kAuxStream>(g.s, r_s, off_r, sr);
             if constexpr (Tr::asym) buf_store_f32<kAuxStream>(g.z, r_z, off_r, sr);
@@ -334,7 +349,7 @@ __global__ __launch_bounds__(256, W) void k_m2_step(M2Args a, int64_t it_base)
 #ifndef SSQ_SCAN_WAVES
 #define SSQ_SCAN_WAVES 4
 #endif
-template <int F, int LPR, bool PRE>
+template <int F, int LPR, bool PRE, bool SR>
 __global__ __launch_bounds__(256, PRE ? SSQ_SCAN_WAVES - 1 : SSQ_SCAN_WAVES) void k_m2_scan(M2Args a)
 {
     using Tr = Traits<F>;
@@ -409,7 +424,10 @@ __global__ __launch_bounds__(256, PRE ? SSQ_SCAN_WAVES - 1 : SSQ_SCAN_WAVES) voi
             RowGrid gr;
             const float ls = lam * s;
             const float lz = ls * z;
-            yv = RS::template run_q<false>(cf, ls, lz, w, dx, in, nullptr, gr);
+            const uint64_t ctr0 =
+                SR ? (((a.sr.step + (uint64_t)t) * (uint64_t)a.sr.rows + (uint64_t)row) * 128u + (uint64_t)(part * E))
+                   : 0;
+            yv = RS::template run_q<false, SR>(cf, ls, lz, w, dx, in, nullptr, gr, a.sr.seed, ctr0);
             s = gr.s;
             z = gr.z;
         } else {
@@ -591,7 +609,7 @@ constexpr int step_waves()
     return PRE && w > 2 ? w - 1 : w;
 }
 
-template <int F, bool PRE>
+template <int F, bool PRE, bool SR>
 static hipError_t launch_step_fp(M2Args a, hipStream_t st)
 {
     constexpr int LPR = lanes_per_row<F>();
@@ -605,7 +623,7 @@ static hipError_t launch_step_fp(M2Args a, hipStream_t st)
     const int64_t main_waves = a.total_iters / kStepIters;
     if (main_waves > 0) {
         const unsigned blocks = (unsigned)((main_waves + 3) / 4);
-        hipLaunchKernelGGL((k_m2_step<F, LPR, PRE, kStepIters, kStepRing, step_waves<F, PRE>()>), dim3(blocks),
+        hipLaunchKernelGGL((k_m2_step<F, LPR, PRE, kStepIters, kStepRing, step_waves<F, PRE>(), SR>), dim3(blocks),
                            dim3(256), 0, st, a,
                            (int64_t)0);
         hipError_t e = hipGetLastError();
@@ -616,7 +634,7 @@ static hipError_t launch_step_fp(M2Args a, hipStream_t st)
     const int64_t rest = a.total_iters - done;
     if (rest > 0) {
         const unsigned blocks = (unsigned)((rest + 3) / 4);
-        hipLaunchKernelGGL((k_m2_step<F, LPR, PRE, 1, 1, 1>), dim3(blocks), dim3(256), 0, st, a, done);
+        hipLaunchKernelGGL((k_m2_step<F, LPR, PRE, 1, 1, 1, SR>), dim3(blocks), dim3(256), 0, st, a, done);
         return hipGetLastError();
     }
     return hipSuccess;
@@ -625,7 +643,10 @@ static hipError_t launch_step_fp(M2Args a, hipStream_t st)
 template <int F>
 static hipError_t launch_step_f(M2Args a, bool pre, int /*num_cus*/, hipStream_t st)
 {
-    return pre ? launch_step_fp<F, true>(a, st) : launch_step_fp<F, false>(a, st);
+    if constexpr (Traits<F>::quant) {
+        if (a.sr.on) return pre ? launch_step_fp<F, true, true>(a, st) : launch_step_fp<F, false, true>(a, st);
+    }
+    return pre ? launch_step_fp<F, true, false>(a, st) : launch_step_fp<F, false, false>(a, st);
 }
 
 hipError_t launch_m2_step(int fmt, M2Args a, bool pre, int num_cus, hipStream_t st)
@@ -648,10 +669,19 @@ static hipError_t launch_scan_f(M2Args a, bool pre, hipStream_t st)
     a.total_iters = (int64_t)a.Bsz * a.H * a.P / RPW;
     a.iters_per_wave = 1;
     const unsigned blocks = (unsigned)((a.total_iters + 3) / 4);
+    if constexpr (Traits<F>::quant) {
+        if (a.sr.on) {
+            if (pre)
+                hipLaunchKernelGGL((k_m2_scan<F, LPR, true, true>), dim3(blocks), dim3(256), 0, st, a);
+            else
+                hipLaunchKernelGGL((k_m2_scan<F, LPR, false, true>), dim3(blocks), dim3(256), 0, st, a);
+            return hipGetLastError();
+        }
+    }
     if (pre)
-        hipLaunchKernelGGL((k_m2_scan<F, LPR, true>), dim3(blocks), dim3(256), 0, st, a);
+        hipLaunchKernelGGL((k_m2_scan<F, LPR, true, false>), dim3(blocks), dim3(256), 0, st, a);
     else
-        hipLaunchKernelGGL((k_m2_scan<F, LPR, false>), dim3(blocks), dim3(256), 0, st, a);
+        hipLaunchKernelGGL((k_m2_scan<F, LPR, false, false>), dim3(blocks), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
