@@ -92,6 +92,8 @@ def bind(path: str):
     L.orc_mamba2_rows_scan_sr.restype = ci
     L.orc_delta_step_sr.argtypes = L.orc_delta_step.argtypes + [ci, u64, u64]
     L.orc_delta_step_sr.restype = ci
+    L.orc_kda_step_sr.argtypes = L.orc_delta_step_sr.argtypes
+    L.orc_kda_step_sr.restype = ci
     return L
 
 
@@ -311,5 +313,22 @@ def delta_step(st: State, q, k, v, alpha, beta, Bsz: int, H: int, readout: str =
     rc = lib().orc_delta_step_sr(Bsz, H, dk, dv, st.bits, st.asym, _i(st.code), _f(st.scale),
                                  _f(st.zero), _f(st.h), _f(q), _f(k), _f(v), _f(alpha), _f(beta),
                                  _f(o), _ro(readout), _f(Spre), _f(vq), *_sr_args(sr))
+    assert rc == 0
+    return (o, Spre, vq) if diag else o
+
+
+def kda_step(st: State, q, k, v, alpha, beta, Bsz: int, H: int, readout: str = "post",
+             diag: bool = False, sr=None):
+    """One KDA-style step (a decay per key channel): ``alpha`` [B][H][dk], the rest as
+    ``delta_step``; returns ``o`` [B][H][dv]."""
+    q, k, v, alpha, beta = map(_c32, (q, k, v, alpha, beta))
+    dk, dv = k.shape[-1], v.shape[-1]
+    assert st.rows == Bsz * H * dk and st.n == dv and alpha.size == Bsz * H * dk
+    o = np.empty((Bsz, H, dv), np.float32)
+    Spre = np.empty((st.rows, dv), np.float32) if diag else None
+    vq = np.empty((st.rows, dv), np.float32) if diag and st.fmt != "fp32" else None
+    rc = lib().orc_kda_step_sr(Bsz, H, dk, dv, st.bits, st.asym, _i(st.code), _f(st.scale),
+                               _f(st.zero), _f(st.h), _f(q), _f(k), _f(v), _f(alpha), _f(beta),
+                               _f(o), _ro(readout), _f(Spre), _f(vq), *_sr_args(sr))
     assert rc == 0
     return (o, Spre, vq) if diag else o

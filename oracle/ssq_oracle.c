@@ -484,11 +484,16 @@ int orc_mamba2_rows_scan(int64_t R, int T, int N, int bits, int asym, int32_t *c
 /* ------------------------------------------------------------------------ */
 
 /* code [dk][dv], s/z [dk] (quantized) or S [dk][dv] fp32 (bits == 0); q, k [dk];
- * v [dv]; o [dv].  Spre, vq: optional [dk][dv] diagnostics. */
+ * v [dv]; o [dv].  Spre, vq: optional [dk][dv] diagnostics.
+ * avec NULL: one decay alpha for the matrix (Gated DeltaNet):
+ *   u = k^T S, w = beta*(v - alpha*u), S' = alpha*S + k w^T.
+ * avec [dk]: a decay per key channel (Kimi Delta Attention's channel-wise gate):
+ *   S' = (I - beta k k^T) Diag(avec) S + beta k v^T, i.e.
+ *   u = k^T Diag(avec) S, w = beta*(v - u), S'_ij = avec_i*S_ij + k_i*w_j. */
 static int delta_matrix_step(int dk, int dv, int bits, int asym, int32_t *code, float *s, float *z,
                              float *S, const float *q, const float *k, const float *v, float alpha,
                              float beta, float *o, int readout_pre, float *Spre, float *vq,
-                             const float *U)
+                             const float *U, const float *avec)
 {
     int i, j;
     float *u = (float *)malloc(sizeof(float) * (size_t)dv);
@@ -503,34 +508,41 @@ static int delta_matrix_step(int dk, int dv, int bits, int asym, int32_t *code, 
         return -1;
     }
 
-    /* u = k^T S (the state before the step) */
+    /* u = k^T S, or k^T Diag(avec) S (the state before the step) */
     for (j = 0; j < dv; ++j) {
         double a = 0.0;
         for (i = 0; i < dk; ++i) {
+            double kd = avec ? (double)k[i] * (double)avec[i] : (double)k[i];
             if (bits == 0) {
-                a += (double)k[i] * (double)S[(int64_t)i * dv + j];
+                a += kd * (double)S[(int64_t)i * dv + j];
             } else {
                 float d = (float)code[(int64_t)i * dv + j] - z[i];
-                a += ((double)k[i] * (double)s[i]) * (double)d;
+                a += (kd * (double)s[i]) * (double)d;
             }
         }
         u[j] = (float)a;
     }
-    /* w = beta*(v - alpha*u) */
+    /* w = beta*(v - alpha*u), or beta*(v - u) when the decay is already in u */
     for (j = 0; j < dv; ++j) {
-        float au = alpha * u[j];
-        float vm = v[j] - au;
+        float vm;
+        if (avec) {
+            vm = v[j] - u[j];
+        } else {
+            float au = alpha * u[j];
+            vm = v[j] - au;
+        }
         w[j] = beta * vm;
     }
-    /* S' = alpha*S + k w^T */
+    /* S' = alpha*S + k w^T, alpha the key channel's own decay with avec */
     for (i = 0; i < dk; ++i) {
+        float al = avec ? avec[i] : alpha;
         if (bits == 0) {
             for (j = 0; j < dv; ++j) {
                 float kw = k[i] * w[j];
-                Sn[(int64_t)i * dv + j] = fmaf(alpha, S[(int64_t)i * dv + j], kw);
+                Sn[(int64_t)i * dv + j] = fmaf(al, S[(int64_t)i * dv + j], kw);
             }
         } else {
-            float as = alpha * s[i];
+            float as = al * s[i];
             float az = as * z[i];
             for (j = 0; j < dv; ++j) {
                 float kw = fmaf(k[i], w[j], -az);
@@ -601,7 +613,7 @@ int orc_delta_step_sr(int Bsz, int H, int dk, int dv, int bits, int asym, int32_
                                s ? s + m * dk : NULL, z ? z + m * dk : NULL,
                                S ? S + mat : NULL, q + m * dk, k + m * dk, v + m * dv,
                                alpha[m], beta[m], o + m * dv, readout_pre,
-                               Spre ? Spre + mat : NULL, vq ? vq + mat : NULL, U);
+                               Spre ? Spre + mat : NULL, vq ? vq + mat : NULL, U, NULL);
         if (rc) {
             free(U);
             return rc;
@@ -618,4 +630,43 @@ int orc_delta_step(int Bsz, int H, int dk, int dv, int bits, int asym, int32_t *
 {
     return orc_delta_step_sr(Bsz, H, dk, dv, bits, asym, code, s, z, S, q, k, v, alpha, beta, o,
                              readout_pre, Spre, vq, 0, 0, 0);
+}
+
+/* One Kimi-Delta-Attention-style step of one layer: the delta rule with a decay
+ * per key channel ("Mamba state quantization for inference": KDA keeps one
+ * dk x dv matrix per head, and DAMP finds persistence differing per key
+ * channel), S' = (I - beta k k^T) Diag(alpha) S + beta k v^T, o = S'^T q.
+ *   alpha [Bsz][H][dk]; everything else as orc_delta_step_sr. */
+int orc_kda_step_sr(int Bsz, int H, int dk, int dv, int bits, int asym, int32_t *code, float *s,
+                    float *z, float *S, const float *q, const float *k, const float *v,
+                    const float *alpha, const float *beta, float *o, int readout_pre, float *Spre,
+                    float *vq, int sr, uint64_t seed, uint64_t step)
+{
+    int64_t m, nm = (int64_t)Bsz * H, i;
+    float *U = NULL;
+    if (Bsz <= 0 || H <= 0 || dk <= 0 || dv <= 0)
+        return -1;
+    if (sr) {
+        U = (float *)malloc(sizeof(float) * (size_t)dk * dv);
+        if (!U)
+            return -1;
+    }
+    for (m = 0; m < nm; ++m) {
+        int64_t mat = m * dk * dv;
+        int rc;
+        if (sr)
+            for (i = 0; i < dk; ++i)
+                orc_sr_row_uniforms(seed, step, nm * dk, m * dk + i, dv, U + i * dv);
+        rc = delta_matrix_step(dk, dv, bits, asym, code ? code + mat : NULL,
+                               s ? s + m * dk : NULL, z ? z + m * dk : NULL,
+                               S ? S + mat : NULL, q + m * dk, k + m * dk, v + m * dv,
+                               0.0f, beta[m], o + m * dv, readout_pre,
+                               Spre ? Spre + mat : NULL, vq ? vq + mat : NULL, U, alpha + m * dk);
+        if (rc) {
+            free(U);
+            return rc;
+        }
+    }
+    free(U);
+    return 0;
 }

@@ -27,7 +27,8 @@ pages and of the benchmark configurations built on them):
 * Initial states: ``N(0,1)`` rows, each row independently an outlier with
   probability 0.05 and then scaled by 20.
 * Delta rule: ``k, q`` are ``N(0,1)`` vectors normalised to unit L2 norm,
-  ``v ~ N(0,1)``, ``alpha = sigmoid(N(3,1))``, ``beta = sigmoid(N(0,1))``.
+  ``v ~ N(0,1)``, ``alpha = sigmoid(N(3,1))``, ``beta = sigmoid(N(0,1))``; the
+  KDA-style step draws ``alpha`` per key channel from the same distribution.
 """
 from __future__ import annotations
 
@@ -38,7 +39,7 @@ import numpy as np
 __all__ = [
     "STREAMS", "uniform", "normal", "band_of_head", "BAND_MEDIAN_NEG_LOG_LAMBDA",
     "mamba2_head_params", "mamba2_step_inputs", "mamba2_scan_inputs", "mamba2_rows_scan_inputs",
-    "init_state", "init_state_rows", "delta_inputs",
+    "init_state", "init_state_rows", "delta_inputs", "kda_alpha",
 ]
 
 _GOLD = np.uint64(0x9E3779B97F4A7C15)
@@ -49,7 +50,7 @@ _MASK64 = (1 << 64) - 1
 # one independent stream per tensor
 STREAMS = {
     "A": 1, "dt": 2, "x": 3, "B": 4, "C": 5, "D": 6, "init": 7, "outlier": 8,
-    "k": 9, "q": 10, "v": 11, "alpha": 12, "beta": 13,
+    "k": 9, "q": 10, "v": 11, "alpha": 12, "beta": 13, "alpha_k": 14,
 }
 
 # median of -ln(lambda) for decay bands 0 (lambda <= 0.9), 1 (0.9..0.99], 2 (> 0.99)
@@ -227,3 +228,10 @@ def delta_inputs(seed: int, layer: int, Bsz: int, H: int, dk: int, dv: int, t: i
     alpha = _f32(1.0 / (1.0 + np.exp(-(3.0 + normal(seed, STREAMS["alpha"], layer, bh)))))
     beta = _f32(1.0 / (1.0 + np.exp(-normal(seed, STREAMS["beta"], layer, bh))))
     return q, k, v, alpha, beta
+
+
+def kda_alpha(seed: int, layer: int, Bsz: int, H: int, dk: int, t: int = 0):
+    """A decay per key channel for the KDA-style step: ``sigmoid(N(3,1))`` per (sequence, head,
+    key channel), [Bsz][H][dk] float32 (the scalar gate's distribution, drawn per channel)."""
+    idx = (np.uint64(t) * np.uint64(Bsz * H * dk) + np.arange(Bsz * H * dk, dtype=np.uint64))
+    return _f32(1.0 / (1.0 + np.exp(-(3.0 + normal(seed, STREAMS["alpha_k"], layer, idx))))).reshape(Bsz, H, dk)

@@ -15,6 +15,7 @@ import pytest
 import oracle
 from tests import test_oracle_pins as pins
 from tests import test_oracle_sr as sr_pins
+from tests import test_oracle_kda as kda_pins
 
 SRC = open(os.path.join(os.path.dirname(oracle.__file__), "ssq_oracle.c")).read()
 
@@ -45,13 +46,14 @@ MUTATIONS = [
     ("scan reads token 0 every step", "memcpy(xs + (size_t)b * H * P, x + ((size_t)b * T + t) * H * P",
      "memcpy(xs + (size_t)b * H * P, x + ((size_t)b * T + 0) * H * P"),
     ("group index wrong", "int g = hh / (H / G);", "int g = hh % G;"),
-    ("delta correction sign", "float vm = v[j] - au;", "float vm = v[j] + au;"),
-    ("delta decay not applied to the state", "float as = alpha * s[i];", "float as = s[i];"),
+    ("delta correction sign", "            vm = v[j] - au;", "            vm = v[j] + au;"),
+    ("delta decay not applied to the state", "float as = al * s[i];", "float as = s[i];"),
     ("delta readout with k instead of q",
      "                for (j = 0; j < dv; ++j)\n                    acc[j] += (double)q[i] * (double)Sn[(int64_t)i * dv + j];\n            }\n        }",
      "                for (j = 0; j < dv; ++j)\n                    acc[j] += (double)k[i] * (double)Sn[(int64_t)i * dv + j];\n            }\n        }"),
-    ("delta u uses the wrong key index", "a += (double)k[i] * (double)S[(int64_t)i * dv + j];",
-     "a += (double)k[j % dk] * (double)S[(int64_t)i * dv + j];"),
+    ("delta u uses the wrong key index",
+     "double kd = avec ? (double)k[i] * (double)avec[i] : (double)k[i];",
+     "double kd = avec ? (double)k[i] * (double)avec[i] : (double)k[j % dk];"),
     ("dequantization scale dropped", "        out[i] = s * d;", "        out[i] = d;"),
     ("stochastic rounding compares with U, not 1 - U",
      "return f + z + (r >= 1.0 - (double)u ? 1.0 : 0.0);", "return f + z + (r > (double)u ? 1.0 : 0.0);"),
@@ -65,14 +67,24 @@ MUTATIONS = [
     ("scan reuses the first token's uniforms", "ys, readout_pre, NULL, NULL, sr, seed, step + (uint64_t)t);",
      "ys, readout_pre, NULL, NULL, sr, seed, step);"),
     ("delta draws the uniforms of the matrix's first row",
-     "sr_row_uniforms(seed, step, nm * dk, m * dk + i, dv, U + i * dv);",
-     "sr_row_uniforms(seed, step, nm * dk, m * dk, dv, U + i * dv);"),
+     "/* key row i of matrix m is state row m*dk + i */\n            for (i = 0; i < dk; ++i)\n"
+     "                orc_sr_row_uniforms(seed, step, nm * dk, m * dk + i, dv, U + i * dv);",
+     "/* key row i of matrix m is state row m*dk + i */\n            for (i = 0; i < dk; ++i)\n"
+     "                orc_sr_row_uniforms(seed, step, nm * dk, m * dk, dv, U + i * dv);"),
+    ("KDA decay missing from u", "double kd = avec ? (double)k[i] * (double)avec[i] : (double)k[i];",
+     "double kd = (double)k[i];"),
+    ("KDA decays every row with the first channel's gate", "float al = avec ? avec[i] : alpha;",
+     "float al = avec ? avec[0] : alpha;"),
+    ("KDA applies the decay to u twice", "            vm = v[j] - u[j];",
+     "            vm = v[j] - avec[0] * u[j];"),
 ]
 
 
 def _pin_cases():
     cases = []
-    members = inspect.getmembers(pins, inspect.isfunction) + inspect.getmembers(sr_pins, inspect.isfunction)
+    members = []
+    for mod in (pins, sr_pins, kda_pins):
+        members += inspect.getmembers(mod, inspect.isfunction)
     for name, fn in members:
         if not name.startswith("test_"):
             continue
