@@ -48,6 +48,9 @@ WORKLOADS = {
     "delta_int8": dict(kind="delta", layers=30, B=256, H=32, P=128, fmt="int8_asym", init="random",
                        desc="Delta-rule (GDN/KDA-style) decode step: 30 layers x 32 heads x 128 x 128, batch 256, "
                             "int8 asymmetric per-row state, seeded random state with 5% x20 outlier rows"),
+    "kda_int8": dict(kind="kda", layers=30, B=256, H=32, P=128, fmt="int8_asym", init="random",
+                     desc="KDA-style decode step (a decay per key channel): 30 layers x 32 heads x 128 x 128, "
+                          "batch 256, int8 asymmetric per-row state, seeded random state with 5% x20 outlier rows"),
     "m2_8b_int8sym": dict(kind="m2", layers=8, B=256, H=128, P=64, fmt="int8_sym", init="zero", rotate=True,
                           desc="Mamba-2 8B-shaped decode layer: 128 heads x 64 x 128, batch 256, int8 symmetric; "
                                "8 state instances in rotation so that the state is not cache resident"),
@@ -68,7 +71,7 @@ WORKLOADS = {
                             desc="Mamba-2 8B-shaped layer: batch 8, 8192-token scan, int4 asymmetric"),
 }
 
-KERNEL_NAMES = {"m2": "k_m2_step", "delta": "k_delta_step", "scan": "k_m2_scan"}
+KERNEL_NAMES = {"m2": "k_m2_step", "delta": "k_delta_step", "kda": "k_delta_step", "scan": "k_m2_scan"}
 
 
 def parse():
@@ -120,7 +123,7 @@ def main():
     T = wl.get("T", 1)
     rows = B * H * P
     fmt_id = ssq.FORMAT_NAMES[fmt]
-    skind = ssq.SSQ_DELTA if kind == "delta" else ssq.SSQ_MAMBA2
+    skind = ssq.SSQ_DELTA if kind in ("delta", "kda") else ssq.SSQ_MAMBA2
     desc = ssq.make_desc(skind, fmt, B, H, P, N)
     lay = ssq.ssq_state_layout(desc)
     meta = 0 if fmt == "fp32" else (8 if fmt.endswith("asym") else 4)
@@ -166,19 +169,21 @@ def main():
             return ssq.lib.ssq_decode_step(states[layer].handle, vp(x.data_ptr()), vp(dt.data_ptr()),
                                            vp(A.data_ptr()), vp(Bm.data_ptr()), vp(Cm.data_ptr()),
                                            vp(D.data_ptr()), vp(y.data_ptr()), 0, stream)
-    elif kind == "delta":
+    elif kind in ("delta", "kda"):
         for layer in range(L):
             q, k, v, al, be = synth.delta_inputs(args.seed, layer, B, H, P, N)
+            if kind == "kda":
+                al = synth.kda_alpha(args.seed, layer, B, H, P)
             t = [torch.from_numpy(a).to(dev) for a in (q, k, v, al, be)]
             o = torch.empty(B * H * N, device=dev)
             ins.append((t, o))
-        io_bytes = 4 * (B * H * (2 * P + 2 * N) + 2 * B * H)
+        io_bytes = 4 * (B * H * (2 * P + 2 * N) + 2 * B * H) + (4 * B * H * (P - 1) if kind == "kda" else 0)
+        step_fn = ssq.lib.ssq_kda_step if kind == "kda" else ssq.lib.ssq_delta_step
 
         def launch(layer, stream):
             (q, k, v, al, be), o = ins[layer]
-            return ssq.lib.ssq_delta_step(states[layer].handle, vp(q.data_ptr()), vp(k.data_ptr()),
-                                          vp(v.data_ptr()), vp(al.data_ptr()), vp(be.data_ptr()),
-                                          vp(o.data_ptr()), 0, stream)
+            return step_fn(states[layer].handle, vp(q.data_ptr()), vp(k.data_ptr()), vp(v.data_ptr()),
+                           vp(al.data_ptr()), vp(be.data_ptr()), vp(o.data_ptr()), 0, stream)
     else:  # scan: one layer's inputs drawn on the device, shared by every layer
         g2 = torch.Generator(device=dev)
         g2.manual_seed(args.seed + 1)
@@ -364,14 +369,18 @@ def cpu_baseline(args, wl, bytes_per_launch, rows_per_layer):
     import synth
 
     kind, fmt, B, H, P, N = wl["kind"], wl["fmt"], wl["B"], wl["H"], wl["P"], 128
-    if kind == "delta":
+    if kind in ("delta", "kda"):
         nmat = 64
         init = synth.init_state(args.seed, 0, nmat * P, N)
         st = oracle.make_state(fmt, nmat * P, N, init)
         q, k, v, al, be = synth.delta_inputs(args.seed, 0, 1, nmat, P, N)
+        step = oracle.delta_step
+        if kind == "kda":
+            al = synth.kda_alpha(args.seed, 0, 1, nmat, P)
+            step = oracle.kda_step
         done, t0 = 0, time.perf_counter()
         while time.perf_counter() - t0 < args.cpu_seconds:
-            oracle.delta_step(st, q, k, v, al, be, 1, nmat)
+            step(st, q, k, v, al, be, 1, nmat)
             done += nmat * P
         sample = f"{nmat} matrices (128 x 128, {fmt}) of the delta layer, one step per call"
     else:

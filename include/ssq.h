@@ -212,6 +212,21 @@ ssq_status ssq_delta_step(ssq_state *state, const float *q, const float *k, cons
                           const float *alpha, const float *beta, float *o, int32_t readout,
                           void *stream);
 
+/* One Kimi-Delta-Attention-style step: the delta rule with a decay per key
+ * channel ("Mamba state quantization for inference" names KDA beside Gated
+ * DeltaNet and reports persistence differing across KDA key channels):
+ *   S' = (I - beta*k*k^T) * Diag(alpha) * S + beta*k*v^T,  o = S'^T q
+ * evaluated as u = k^T Diag(alpha) S (S_ij = s_i*(c_ij - z_i) as a real
+ * number, products and sum in double, rounded once), w_j = fl(beta*fl(v_j - u_j)),
+ * S'_ij = fma(as_i, c_ij, fma(k_i, w_j, -fl(as_i*z_i))) with as_i =
+ * fl(alpha_i*s_i) (fp32 state: fma(alpha_i, S_ij, fl(k_i*w_j))), then each key
+ * row refit and rounded as above.
+ *   alpha [batch][nheads][dk] (each in (0, 1]); q, k, v, beta, o as in
+ *   ssq_delta_step.  Errors as ssq_delta_step. */
+ssq_status ssq_kda_step(ssq_state *state, const float *q, const float *k, const float *v,
+                        const float *alpha, const float *beta, float *o, int32_t readout,
+                        void *stream);
+
 /* The fp32 value the state stands for, fl(s*fl(c - z)) per entry (the stored
  * fp32 for SSQ_FP32): out [batch][nheads][rows_per_head][row_len]. */
 ssq_status ssq_dequant(const ssq_state *state, float *out, void *stream);

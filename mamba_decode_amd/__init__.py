@@ -82,6 +82,8 @@ def _load():
     L.ssq_status_string.restype = ctypes.c_char_p
     L.ssq_last_error.argtypes = []
     L.ssq_last_error.restype = ctypes.c_char_p
+    L.ssq_kda_step.argtypes = [vp, f32p, f32p, f32p, f32p, f32p, f32p, ctypes.c_int32, vp]
+    L.ssq_kda_step.restype = st
     u64 = ctypes.c_uint64
     L.ssq_set_rounding.argtypes = [vp, ctypes.c_int32, u64, u64]
     L.ssq_set_rounding.restype = st
@@ -258,6 +260,15 @@ def ssq_delta_step(state: State, q, k, v, alpha, beta, o, readout: int = SSQ_REA
     _check(lib.ssq_delta_step(state.handle, _dev(q, "q", nk), _dev(k, "k", nk), _dev(v, "v", nv),
                               _dev(alpha, "alpha", nb), _dev(beta, "beta", nb), _dev(o, "o", nv), readout,
                               _stream(stream)), "ssq_delta_step")
+
+
+def ssq_kda_step(state: State, q, k, v, alpha, beta, o, readout: int = SSQ_READ_POST_QUANT, stream=None):
+    d = state.desc
+    bh = d.batch * d.nheads
+    nk, nv, nb = _sizes(state, SSQ_DELTA, bh * d.rows_per_head, bh * d.row_len, bh)
+    _check(lib.ssq_kda_step(state.handle, _dev(q, "q", nk), _dev(k, "k", nk), _dev(v, "v", nv),
+                            _dev(alpha, "alpha", nk), _dev(beta, "beta", nb), _dev(o, "o", nv), readout,
+                            _stream(stream)), "ssq_kda_step")
 
 
 def ssq_dequant(state: State, out, stream=None):

@@ -339,8 +339,8 @@ ssq_status ssq_scan(ssq_state* st, int32_t T, const float* x, const float* dt, c
     return s;
 }
 
-ssq_status ssq_delta_step(ssq_state* st, const float* q, const float* k, const float* v, const float* alpha,
-                          const float* beta, float* o, int32_t readout, void* stream)
+static ssq_status delta_common(ssq_state* st, const float* q, const float* k, const float* v, const float* alpha,
+                               const float* beta, float* o, int32_t readout, void* stream, bool kda)
 {
     SSQ_REQUIRE(st, SSQ_ERR_INVALID_ARG, "state is NULL");
     SSQ_REQUIRE(st->desc.kind == SSQ_DELTA, SSQ_ERR_KIND_MISMATCH, "a delta-rule call on a Mamba-2 state");
@@ -364,11 +364,24 @@ ssq_status ssq_delta_step(ssq_state* st, const float* q, const float* k, const f
     a.beta = beta;
     a.o = o;
     a.nmat = (int64_t)st->desc.batch * st->desc.nheads;
+    a.kda = kda ? 1 : 0;
     a.sr = sr_args(st);
     s = from_hip(ssq::launch_delta_step(st->desc.format, a, readout == SSQ_READ_PRE_QUANT, (hipStream_t)stream),
-                 "delta step launch");
+                 kda ? "KDA step launch" : "delta step launch");
     if (s == SSQ_OK) advance(st, 1);
     return s;
+}
+
+ssq_status ssq_delta_step(ssq_state* st, const float* q, const float* k, const float* v, const float* alpha,
+                          const float* beta, float* o, int32_t readout, void* stream)
+{
+    return delta_common(st, q, k, v, alpha, beta, o, readout, stream, false);
+}
+
+ssq_status ssq_kda_step(ssq_state* st, const float* q, const float* k, const float* v, const float* alpha,
+                        const float* beta, float* o, int32_t readout, void* stream)
+{
+    return delta_common(st, q, k, v, alpha, beta, o, readout, stream, true);
 }
 
 ssq_status ssq_dequant(const ssq_state* st, float* out, void* stream)

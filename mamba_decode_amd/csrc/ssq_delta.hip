@@ -29,7 +29,9 @@ namespace ssq {
 #define SSQ_DELTA_WAVES 4
 #endif
 
-template <int F, bool PRE, bool SR>
+// KDA: a decay per key channel (alpha [matrices][128]), S' = (I - beta k k^T) Diag(alpha) S
+// + beta k v^T, evaluated as u = k^T Diag(alpha) S, w = beta*(v - u), S' = alpha_i*S + k w^T
+template <int F, bool PRE, bool SR, bool KDA>
 __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_delta_step(DeltaArgs a)
 {
     using Tr = Traits<F>;
@@ -44,9 +46,9 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_delta_step(DeltaArgs a
     const int rg = t >> 3, part = t & 7, j0 = part * E;
     const int64_t mat = blockIdx.x;
     const int64_t mrow0 = mat * 128; // first state row of the matrix
-    const float alpha = a.alpha[mat], beta = a.beta[mat];
+    const float alpha = KDA ? 0.0f : a.alpha[mat], beta = a.beta[mat];
 
-    float kk[KR], qq[KR], s_old[KR], z_old[KR];
+    float kk[KR], qq[KR], s_old[KR], z_old[KR], al[KR];
     // the codes stay packed in registers (or the fp32 rows, for the fp32 state) and are
     // unpacked where they are used, once for u and once for the update: fewer live
     // registers, more waves per SIMD to overlap the matrix loads
@@ -56,6 +58,7 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_delta_step(DeltaArgs a
         const int i = rg + RG * r;
         kk[r] = a.k[mrow0 + i];
         qq[r] = a.q[mrow0 + i];
+        al[r] = KDA ? a.alpha[mrow0 + i] : alpha; // the key row's decay
         const int64_t row = mrow0 + i;
         if constexpr (Tr::quant) {
             load_words<NW>(a.codes + row * ROWB + part * (NW * 4), cw[r]);
@@ -78,19 +81,26 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_delta_step(DeltaArgs a
     load_f32<E>(a.v + mrow0 + j0, vv);
 
     // u = k^T S in double: sum_i kap_i*c_ij - sum_i kap_i*z_i with kap_i = k_i*s_i exact
-    // (quantized), or sum_i k_i*S_ij (fp32); the z term is the same for every column
+    // (quantized), or sum_i k_i*S_ij (fp32); the z term is the same for every column.
+    // KDA folds the row's decay in: kap_i = (k_i*alpha_i)*s_i.
     {
+        double kaps[KR];
+#pragma unroll
+        for (int r = 0; r < KR; ++r) {
+            const double kd = KDA ? (double)kk[r] * (double)al[r] : (double)kk[r];
+            kaps[r] = Tr::quant ? kd * (double)s_old[r] : kd;
+        }
         double up[E];
         double zt = 0.0;
         if constexpr (Tr::asym) {
 #pragma unroll
-            for (int r = 0; r < KR; ++r) zt = __builtin_fma((double)kk[r] * (double)s_old[r], (double)z_old[r], zt);
+            for (int r = 0; r < KR; ++r) zt = __builtin_fma(kaps[r], (double)z_old[r], zt);
         }
 #pragma unroll
         for (int e = 0; e < E; ++e) up[e] = -zt;
 #pragma unroll
         for (int r = 0; r < KR; ++r) {
-            const double kap = Tr::quant ? (double)kk[r] * (double)s_old[r] : (double)kk[r];
+            const double kap = kaps[r];
             float f[E];
             row_values(r, f);
 #pragma unroll
@@ -108,11 +118,11 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_delta_step(DeltaArgs a
     }
     __syncthreads();
 
-    // w = beta*(v - alpha*u)
+    // w = beta*(v - alpha*u), or beta*(v - u) for KDA (the decay is already in u)
     float ww[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-        const float au = alpha * u_s[j0 + e];
+        const float au = KDA ? u_s[j0 + e] : alpha * u_s[j0 + e];
         const float vm = vv[e] - au;
         ww[e] = beta * vm;
     }
@@ -131,7 +141,7 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_delta_step(DeltaArgs a
         row_values(r, S);
         if constexpr (Tr::quant) {
             // alpha*s*(c - z) + k*w = fma(as, c, fma(k, w, -as*z)): the decay acts on the scale
-            const float as = alpha * s_old[r];
+            const float as = al[r] * s_old[r];
             const float az = as * z_old[r];
 #pragma unroll
             for (int e = 0; e < E; ++e) S[e] = __builtin_fmaf(as, S[e], __builtin_fmaf(kk[r], ww[e], -az));
@@ -139,7 +149,7 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_delta_step(DeltaArgs a
 #pragma unroll
             for (int e = 0; e < E; ++e) {
                 const float kw = kk[r] * ww[e];
-                S[e] = __builtin_fmaf(alpha, S[e], kw);
+                S[e] = __builtin_fmaf(al[r], S[e], kw);
             }
         }
         if constexpr (!Tr::quant || PRE) {
@@ -216,24 +226,30 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_delta_step(DeltaArgs a
     }
 }
 
-template <int F>
-static hipError_t launch_delta_f(DeltaArgs a, bool pre, hipStream_t st)
+template <int F, bool KDA>
+static hipError_t launch_delta_fk(DeltaArgs a, bool pre, hipStream_t st)
 {
     const unsigned blocks = (unsigned)a.nmat;
     if constexpr (Traits<F>::quant) {
         if (a.sr.on) {
             if (pre)
-                hipLaunchKernelGGL((k_delta_step<F, true, true>), dim3(blocks), dim3(256), 0, st, a);
+                hipLaunchKernelGGL((k_delta_step<F, true, true, KDA>), dim3(blocks), dim3(256), 0, st, a);
             else
-                hipLaunchKernelGGL((k_delta_step<F, false, true>), dim3(blocks), dim3(256), 0, st, a);
+                hipLaunchKernelGGL((k_delta_step<F, false, true, KDA>), dim3(blocks), dim3(256), 0, st, a);
             return hipGetLastError();
         }
     }
     if (pre)
-        hipLaunchKernelGGL((k_delta_step<F, true, false>), dim3(blocks), dim3(256), 0, st, a);
+        hipLaunchKernelGGL((k_delta_step<F, true, false, KDA>), dim3(blocks), dim3(256), 0, st, a);
     else
-        hipLaunchKernelGGL((k_delta_step<F, false, false>), dim3(blocks), dim3(256), 0, st, a);
+        hipLaunchKernelGGL((k_delta_step<F, false, false, KDA>), dim3(blocks), dim3(256), 0, st, a);
     return hipGetLastError();
+}
+
+template <int F>
+static hipError_t launch_delta_f(DeltaArgs a, bool pre, hipStream_t st)
+{
+    return a.kda ? launch_delta_fk<F, true>(a, pre, st) : launch_delta_fk<F, false>(a, pre, st);
 }
 
 hipError_t launch_delta_step(int fmt, DeltaArgs a, bool pre, hipStream_t st)

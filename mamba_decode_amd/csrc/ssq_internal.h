@@ -55,10 +55,11 @@ struct DeltaArgs {
     const float* q;
     const float* k;
     const float* v;
-    const float* alpha;
+    const float* alpha; // [nmat], or [nmat][128] with kda (a decay per key channel)
     const float* beta;
     float* o;
     int64_t nmat;
+    int kda;
     SrArgs sr;
 };
 

@@ -118,6 +118,7 @@ def test_null_arguments_are_rejected_before_any_device_call():
     assert L.ssq_decode_step(None, None, None, None, None, None, None, None, 0, None) == ssq.SSQ_ERR_INVALID_ARG
     assert L.ssq_scan(None, 4, None, None, None, None, None, None, None, 0, None) == ssq.SSQ_ERR_INVALID_ARG
     assert L.ssq_delta_step(None, None, None, None, None, None, None, 0, None) == ssq.SSQ_ERR_INVALID_ARG
+    assert L.ssq_kda_step(None, None, None, None, None, None, None, 0, None) == ssq.SSQ_ERR_INVALID_ARG
     assert L.ssq_dequant(None, None, None) == ssq.SSQ_ERR_INVALID_ARG
     assert L.ssq_state_info(None, None, None, None) == ssq.SSQ_ERR_INVALID_ARG
     assert L.ssq_set_rounding(None, ssq.SSQ_ROUND_STOCHASTIC, 1, 0) == ssq.SSQ_ERR_INVALID_ARG

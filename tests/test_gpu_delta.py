@@ -124,3 +124,99 @@ def test_delta_layer_full_size_sampled():
     sub = {"code": g["code"][srows], "scale": g["scale"][srows], "zero": g["zero"][srows]}
     par.check_codes(sub, ost.code, ost.scale, ost.zero, vq, fmt, "full layer")
     assert par.block_rel(og[mats], oo[0], axis=1) <= 1e-5
+
+
+# ---------------------------------------------------------------------------
+# KDA-style step: a decay per key channel (ssq_kda_step)
+# ---------------------------------------------------------------------------
+def run_kda(gst, q, k, v, al, be, readout):
+    o = torch.empty(v.shape, dtype=torch.float32, device="cuda")
+    ssq.ssq_kda_step(gst, par.dev(q), par.dev(k), par.dev(v), par.dev(al), par.dev(be), o, readout)
+    return o.cpu().numpy()
+
+
+@pytest.mark.parametrize("readout", ["post", "pre"])
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_kda_step_teacher_forced(fmt, readout):
+    B, H, T = 2, 3, 3
+    rows = B * H * 128
+    ro = ssq.SSQ_READ_PRE_QUANT if readout == "pre" else ssq.SSQ_READ_POST_QUANT
+    init = synth.init_state(95, 0, rows, 128)
+    init[7] = 0.0
+    init[300] = -1.5
+    ost = oracle.make_state(fmt, rows, 128, init)
+    gst = par.new_gpu_state(ddesc(fmt, B, H))
+    for t in range(T):
+        say(f"kda teacher-forced fmt={fmt} readout={readout} t={t}")
+        q, k, v, _, be = synth.delta_inputs(95, 0, B, H, 128, 128, t=t)
+        al = synth.kda_alpha(95, 0, B, H, 128, t=t)
+        par.write_gpu_state(gst, ost)
+        before = ost.copy()
+        og = run_kda(gst, q, k, v, al, be, ro)
+        oo, _, vq = oracle.kda_step(ost, q, k, v, al, be, B, H, readout=readout, diag=True)
+        g = par.read_gpu_state(gst, fmt)
+        if fmt == "fp32":
+            tie = u_tie_rows(before, k * al, B, H)  # u = (k*alpha)^T S
+            if not np.array_equal(g["h"], ost.h):
+                bad = np.unique(np.nonzero((g["h"] != ost.h).any(axis=1))[0] // 128)
+                assert np.all(tie[bad]), t
+        else:
+            par.check_codes(g, ost.code, ost.scale, ost.zero, vq, fmt, f"t={t}")
+        assert par.block_rel(og, oo, axis=2) <= 1e-5, t
+
+
+def test_kda_layer_full_size_sampled_with_stochastic_rounding():
+    """KDA-style layer at the profiled footprint (batch 256 x 32 heads x 128 x 128, int8
+    asymmetric), one round-to-nearest step then one stochastic step; 32 sampled matrices."""
+    B, H, fmt = 256, 32, "int8_asym"
+    rows = B * H * 128
+    say("kda full layer: generating init")
+    init = synth.init_state(6, 0, rows, 128, threads=8)
+    gst = par.new_gpu_state(ddesc(fmt, B, H), init)
+    mats = np.unique(np.linspace(0, B * H - 1, 32).astype(np.int64))
+    srows = (mats[:, None] * 128 + np.arange(128)).reshape(-1)
+    # the sampled matrices' rows, indexed as their own small state, with their state row ids
+    ost = oracle.make_state(fmt, len(srows), 128, init[srows])
+    del init
+    sel = lambda a: a.reshape(B * H, *a.shape[2:])[mats][None]  # noqa: E731
+    for t, sr in enumerate([None, (77, 12)]):
+        say(f"kda full layer: step {t}")
+        if sr is not None:
+            ssq.ssq_set_rounding(gst, ssq.SSQ_ROUND_STOCHASTIC, *sr)
+        q, k, v, _, be = synth.delta_inputs(6, 0, B, H, 128, 128, t=t)
+        al = synth.kda_alpha(6, 0, B, H, 128, t=t)
+        og = run_kda(gst, q, k, v, al, be, ssq.SSQ_READ_POST_QUANT).reshape(B * H, 128)
+        if sr is None:
+            oo, _, vq = oracle.kda_step(ost, sel(q), sel(k), sel(v), sel(al), be.reshape(-1)[mats][None],
+                                        1, len(mats), diag=True)
+        else:
+            # the oracle draws per state row: run each sampled matrix as matrix m of the full layer
+            oo = np.empty((1, len(mats), 128), np.float32)
+            for i, m in enumerate(mats):
+                one = oracle.make_state(fmt, 128, 128)
+                one.code, one.scale, one.zero = (ost.code[i * 128:(i + 1) * 128].copy(),
+                                                 ost.scale[i * 128:(i + 1) * 128].copy(),
+                                                 ost.zero[i * 128:(i + 1) * 128].copy())
+                # a full-layer state row index enters only through the uniforms' counter
+                U = np.stack([oracle.sr_row_uniforms(sr[0], sr[1], rows, m * 128 + r, 128) for r in range(128)])
+                _, Spre, _ = oracle.kda_step(one.copy(), sel(q)[:, i:i + 1], sel(k)[:, i:i + 1],
+                                             sel(v)[:, i:i + 1], sel(al)[:, i:i + 1],
+                                             be.reshape(-1)[[m]][None], 1, 1, diag=True)
+                for r in range(128):
+                    c, s_, z_ = oracle.quantize_row_sr(Spre[r], fmt, U[r])
+                    one.code[r], one.scale[r], one.zero[r] = c, s_, z_
+                deq = one.dequant().astype(np.float64)
+                oo[0, i] = (deq * sel(q)[0, i].astype(np.float64)[:, None]).sum(axis=0)
+                ost.code[i * 128:(i + 1) * 128] = one.code
+                ost.scale[i * 128:(i + 1) * 128] = one.scale
+                ost.zero[i * 128:(i + 1) * 128] = one.zero
+        g = par.read_gpu_state(gst, fmt)
+        sub = {"code": g["code"][srows], "scale": g["scale"][srows], "zero": g["zero"][srows]}
+        if sr is None:
+            par.check_codes(sub, ost.code, ost.scale, ost.zero, vq, fmt, "kda full layer")
+            # continue from the GPU's state so that the stochastic step starts from the same codes
+            ost.code, ost.scale, ost.zero = sub["code"].copy(), sub["scale"].copy(), sub["zero"].copy()
+        else:
+            assert np.array_equal(sub["code"], ost.code)
+            assert np.array_equal(sub["scale"], ost.scale) and np.array_equal(sub["zero"], ost.zero)
+        assert par.block_rel(og[mats], oo[0], axis=1) <= 1e-5
