@@ -94,6 +94,9 @@ def bind(path: str):
     L.orc_delta_step_sr.restype = ci
     L.orc_kda_step_sr.argtypes = L.orc_delta_step_sr.argtypes
     L.orc_kda_step_sr.restype = ci
+    L.orc_mamba2_prefill_sr.argtypes = [ci, ci, ci, ci, ci, ci, ci, ci, ci, i32p, f32p, f32p, f32p,
+                                        f32p, f32p, f32p, f32p, f32p, f32p, f32p, ci, ci, u64, u64]
+    L.orc_mamba2_prefill_sr.restype = ci
     return L
 
 
@@ -332,3 +335,18 @@ def kda_step(st: State, q, k, v, alpha, beta, Bsz: int, H: int, readout: str = "
                                _f(o), _ro(readout), _f(Spre), _f(vq), *_sr_args(sr))
     assert rc == 0
     return (o, Spre, vq) if diag else o
+
+
+def mamba2_prefill(st: State, x, dt, A, Bm, Cm, D, chunk: int, readout: str = "post", sr=None):
+    """``T`` prompt tokens with the state quantized only at chunk ends (and after the last
+    token); shapes as ``mamba2_scan``; returns ``y`` [B][T][H][P]."""
+    x, dt, A, Bm, Cm, D = map(_c32, (x, dt, A, Bm, Cm, D))
+    Bsz, T, H, P = x.shape
+    G, N = Bm.shape[2], Bm.shape[3]
+    assert st.rows == Bsz * H * P and st.n == N
+    y = np.empty((Bsz, T, H, P), np.float32)
+    rc = lib().orc_mamba2_prefill_sr(Bsz, T, chunk, H, G, P, N, st.bits, st.asym, _i(st.code),
+                                     _f(st.scale), _f(st.zero), _f(st.h), _f(x), _f(dt), _f(A), _f(Bm),
+                                     _f(Cm), _f(D), _f(y), _ro(readout), *_sr_args(sr))
+    assert rc == 0
+    return y

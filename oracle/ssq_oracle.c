@@ -670,3 +670,84 @@ int orc_kda_step_sr(int Bsz, int H, int dk, int dv, int bits, int asym, int32_t 
     free(U);
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Mamba-2 prefill with chunk-final quantization                              */
+/* ------------------------------------------------------------------------ */
+
+/* T prompt tokens of one layer, the state quantized only at the end of each
+ * chunk of `chunk` tokens and after the last token ("Mamba state quantization
+ * for inference", "Mamba state quantization needs phase-aware benchmarks":
+ * DAMP runs the recurrence in FP32 inside each chunk and writes the
+ * chunk-final state into the packed cache).  Per row: the stored state is
+ * dequantized once, then every token applies the fp32 update
+ * h'_n = fma(lambda, h_n, fl(w*B_n)); inside a chunk y is read from that fp32
+ * state; at a chunk end the row is refit and rounded (to nearest, or
+ * stochastically with the uniforms of token step + t), y is read from the
+ * state the readout flag names, and the next chunk starts from the
+ * dequantized new codes.  bits == 0 (fp32 state): the plain fp32 scan.
+ * Shapes as orc_mamba2_scan. */
+int orc_mamba2_prefill_sr(int Bsz, int T, int chunk, int H, int G, int P, int N, int bits, int asym,
+                          int32_t *code, float *s, float *z, float *h, const float *x,
+                          const float *dt, const float *A, const float *Bm, const float *Cm,
+                          const float *D, float *y, int readout_pre, int sr, uint64_t seed,
+                          uint64_t step)
+{
+    int b, hh, p, t, n;
+    int64_t rows = (int64_t)Bsz * H * P;
+    float *r, *U;
+    if (Bsz <= 0 || T <= 0 || chunk <= 0 || H <= 0 || G <= 0 || P <= 0 || N <= 0 || H % G != 0)
+        return -1;
+    if (bits == 0)
+        return orc_mamba2_scan(Bsz, T, H, G, P, N, 0, 0, NULL, NULL, NULL, h, x, dt, A, Bm, Cm, D, y,
+                               readout_pre);
+    r = (float *)malloc(sizeof(float) * (size_t)N);
+    U = (float *)malloc(sizeof(float) * (size_t)N);
+    if (!r || !U) {
+        free(r);
+        free(U);
+        return -1;
+    }
+    for (b = 0; b < Bsz; ++b)
+        for (hh = 0; hh < H; ++hh) {
+            int g = hh / (H / G);
+            for (p = 0; p < P; ++p) {
+                int64_t row = ((int64_t)b * H + hh) * P + p;
+                int32_t *c = code + row * N;
+                orc_dequantize_row(c, N, s[row], z[row], r);
+                for (t = 0; t < T; ++t) {
+                    int64_t bt = (int64_t)b * T + t;
+                    const float *Bn = Bm + (bt * G + g) * N;
+                    const float *Cn = Cm + (bt * G + g) * N;
+                    float xv = x[(bt * H + hh) * P + p];
+                    float dtv = dt[bt * H + hh];
+                    float lam = orc_decay(dtv, A[hh]);
+                    float w = dtv * xv;
+                    float dx = D[hh] * xv;
+                    int end = ((t + 1) % chunk == 0) || t == T - 1;
+                    double acc = 0.0;
+                    for (n = 0; n < N; ++n) {
+                        float wb = w * Bn[n];
+                        r[n] = fmaf(lam, r[n], wb);
+                    }
+                    if (!end || readout_pre)
+                        for (n = 0; n < N; ++n)
+                            acc += (double)Cn[n] * (double)r[n];
+                    if (end) {
+                        if (sr)
+                            orc_sr_row_uniforms(seed, step + (uint64_t)t, rows, row, N, U);
+                        orc_quantize_row_sr(r, N, bits, asym, c, s + row, z + row, NULL,
+                                            sr ? U : NULL);
+                        orc_dequantize_row(c, N, s[row], z[row], r);
+                        if (!readout_pre)
+                            for (n = 0; n < N; ++n)
+                                acc += (double)Cn[n] * (double)r[n];
+                    }
+                    y[(bt * H + hh) * P + p] = (float)(acc + (double)dx);
+                }
+            }
+        }
+    free(r);
+    free(U);
+    return 0;
+}

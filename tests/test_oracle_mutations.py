@@ -16,6 +16,7 @@ import oracle
 from tests import test_oracle_pins as pins
 from tests import test_oracle_sr as sr_pins
 from tests import test_oracle_kda as kda_pins
+from tests import test_oracle_prefill as prefill_pins
 
 SRC = open(os.path.join(os.path.dirname(oracle.__file__), "ssq_oracle.c")).read()
 
@@ -45,7 +46,10 @@ MUTATIONS = [
      "            code[i] = (int32_t)t;\n            if (v_out)\n                v_out[i] = v;\n        }\n        *s_out = s;\n        *z_out = z;"),
     ("scan reads token 0 every step", "memcpy(xs + (size_t)b * H * P, x + ((size_t)b * T + t) * H * P",
      "memcpy(xs + (size_t)b * H * P, x + ((size_t)b * T + 0) * H * P"),
-    ("group index wrong", "int g = hh / (H / G);", "int g = hh % G;"),
+    ("group index wrong", "            int g = hh / (H / G);\n            const float *Bn = Bm + ((int64_t)b * G + g) * N;",
+     "            int g = hh % G;\n            const float *Bn = Bm + ((int64_t)b * G + g) * N;"),
+    ("prefill group index wrong", "            int g = hh / (H / G);\n            for (p = 0; p < P; ++p) {",
+     "            int g = hh % G;\n            for (p = 0; p < P; ++p) {"),
     ("delta correction sign", "            vm = v[j] - au;", "            vm = v[j] + au;"),
     ("delta decay not applied to the state", "float as = al * s[i];", "float as = s[i];"),
     ("delta readout with k instead of q",
@@ -77,13 +81,22 @@ MUTATIONS = [
      "float al = avec ? avec[0] : alpha;"),
     ("KDA applies the decay to u twice", "            vm = v[j] - u[j];",
      "            vm = v[j] - avec[0] * u[j];"),
+    ("prefill quantizes every token", "int end = ((t + 1) % chunk == 0) || t == T - 1;", "int end = 1;"),
+    ("prefill ignores the chunk length", "int end = ((t + 1) % chunk == 0) || t == T - 1;",
+     "int end = t == T - 1;"),
+    ("prefill reads the fp32 state at a chunk end", "if (!end || readout_pre)", "if (1)"),
+    ("prefill continues from the unrounded row",
+     "sr ? U : NULL);\n                        orc_dequantize_row(c, N, s[row], z[row], r);",
+     "sr ? U : NULL);"),
+    ("chunk-end uniforms of the first token", "orc_sr_row_uniforms(seed, step + (uint64_t)t, rows, row, N, U);",
+     "orc_sr_row_uniforms(seed, step, rows, row, N, U);"),
 ]
 
 
 def _pin_cases():
     cases = []
     members = []
-    for mod in (pins, sr_pins, kda_pins):
+    for mod in (pins, sr_pins, kda_pins, prefill_pins):
         members += inspect.getmembers(mod, inspect.isfunction)
     for name, fn in members:
         if not name.startswith("test_"):
