@@ -64,6 +64,11 @@ WORKLOADS = {
                                  desc="as m2_130m_scan_int8asym with the int8 symmetric grid"),
     "m2_130m_scan_fp32": dict(kind="scan", layers=24, B=32, H=24, P=64, fmt="fp32", init="zero", T=2048,
                               desc="as m2_130m_scan_int8asym with the fp32 control state"),
+    "m2_130m_prefill_int8asym": dict(kind="prefill", layers=24, B=32, H=24, P=64, fmt="int8_asym", init="zero",
+                                     T=2048, chunk=64,
+                                     desc="Mamba-2 130m-shaped stack: 24 layers x 24 heads x 64 x 128, batch 32, "
+                                          "2048-token prompt per layer, fp32 recurrence inside chunks of 64 tokens, "
+                                          "int8 asymmetric state written at each chunk end"),
     "m2_8b_scan_int8sym": dict(kind="scan", layers=1, B=8, H=128, P=64, fmt="int8_sym", init="zero", T=8192,
                                desc="Mamba-2 8B-shaped layer: batch 8, 8192-token scan, int8 symmetric, state "
                                     "rounded every token"),
@@ -71,7 +76,8 @@ WORKLOADS = {
                             desc="Mamba-2 8B-shaped layer: batch 8, 8192-token scan, int4 asymmetric"),
 }
 
-KERNEL_NAMES = {"m2": "k_m2_step", "delta": "k_delta_step", "kda": "k_delta_step", "scan": "k_m2_scan"}
+KERNEL_NAMES = {"m2": "k_m2_step", "delta": "k_delta_step", "kda": "k_delta_step", "scan": "k_m2_scan",
+                "prefill": "k_m2_prefill"}
 
 
 def parse():
@@ -114,8 +120,9 @@ def main():
 
     wl = WORKLOADS[args.workload]
     kind = wl["kind"]
-    steps = args.steps if args.steps is not None else (3 if kind == "scan" else 100)
-    warmup = args.warmup if args.warmup is not None else (1 if kind == "scan" else 10)
+    seq = kind in ("scan", "prefill")  # T tokens per launch, the state on-chip
+    steps = args.steps if args.steps is not None else (3 if seq else 100)
+    warmup = args.warmup if args.warmup is not None else (1 if seq else 10)
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
     L, B, H, P, fmt = wl["layers"], wl["B"], wl["H"], wl["P"], wl["fmt"]
@@ -184,7 +191,7 @@ def main():
             (q, k, v, al, be), o = ins[layer]
             return step_fn(states[layer].handle, vp(q.data_ptr()), vp(k.data_ptr()), vp(v.data_ptr()),
                            vp(al.data_ptr()), vp(be.data_ptr()), vp(o.data_ptr()), 0, stream)
-    else:  # scan: one layer's inputs drawn on the device, shared by every layer
+    else:  # scan / prefill: one layer's inputs drawn on the device, shared by every layer
         g2 = torch.Generator(device=dev)
         g2.manual_seed(args.seed + 1)
         A_np, D_np, bias = synth.mamba2_head_params(args.seed, 0, H)
@@ -201,11 +208,12 @@ def main():
 
         def launch(layer, stream):
             (x, dt, A, Bm, Cm, D), y = ins[0]
-            return ssq.lib.ssq_scan(states[layer].handle, T, vp(x.data_ptr()), vp(dt.data_ptr()),
-                                    vp(A.data_ptr()), vp(Bm.data_ptr()), vp(Cm.data_ptr()),
-                                    vp(D.data_ptr()), vp(y.data_ptr()), 0, stream)
+            ptrs = [vp(t.data_ptr()) for t in (x, dt, A, Bm, Cm, D, y)]
+            if kind == "prefill":
+                return ssq.lib.ssq_prefill(states[layer].handle, T, wl["chunk"], *ptrs, 0, stream)
+            return ssq.lib.ssq_scan(states[layer].handle, T, *ptrs, 0, stream)
     torch.cuda.synchronize()
-    bytes_per_launch = (state_bytes_layer if kind != "scan" else 0) + io_bytes
+    bytes_per_launch = (state_bytes_layer if not seq else 0) + io_bytes
 
     def run_step():
         s = vp(torch.cuda.current_stream().cuda_stream)
@@ -215,7 +223,7 @@ def main():
                 raise RuntimeError(f"launch failed: {ssq.ssq_last_error()}")
 
     # ---------------- graph capture of one step ----------------
-    use_graph = not args.eager and kind != "scan"
+    use_graph = not args.eager and not seq
     graph = None
     if use_graph:
         run_step()  # warm the launch path before capture
@@ -250,7 +258,7 @@ def main():
     ms_per_step = ms_total / steps
 
     # ---------------- eager per-launch time (events around each launch, same stream): context ----------------
-    kreps = max(1, min(steps, 20 if kind != "scan" else 2))
+    kreps = max(1, min(steps, 20 if not seq else 2))
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(kreps * L)]
     s = vp(torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
@@ -286,7 +294,7 @@ def main():
 
     total_bytes_step = bytes_per_launch * L
     value = total_bytes_step / (ms_per_step * 1e-3) / 1e9
-    state_gbps = state_bytes_layer * L / (ms_per_step * 1e-3) / 1e9 if kind != "scan" else None
+    state_gbps = state_bytes_layer * L / (ms_per_step * 1e-3) / 1e9 if not seq else None
     achieved = bytes_per_launch / (kernel_ms_mean * 1e-3) / 1e9
 
     # traffic from the committed rocprofv3 counter runs, only while the kernels are unchanged
@@ -314,7 +322,7 @@ def main():
             "workload": wl["desc"],
             "name": args.workload,
             "layers": L, "batch": B, "heads": H, "rows_per_head": P, "row_len": N, "format": fmt,
-            "tokens": T if kind == "scan" else 1,
+            "tokens": T if seq else 1,
             "launch": ("hipGraph replay of " if graph is not None else "back-to-back launches of ")
                       + f"{L} per-layer kernels per step",
             "parallelism": "single GPU",
@@ -322,13 +330,13 @@ def main():
         "hbm_frac": round(value / HBM_PEAK_GBPS, 4),
         # a rotated workload times one layer on several state instances: each launch is one token
         "decode_steps_per_s": (round(1000.0 * (L if wl.get("rotate") else 1) / ms_per_step, 2)
-                               if kind != "scan" else None),
-        "tokens_per_s": round(B * T / (ms_per_step * 1e-3 / L), 1) if kind == "scan" else None,
+                               if not seq else None),
+        "tokens_per_s": round(B * T / (ms_per_step * 1e-3 / L), 1) if seq else None,
         "state_GBps": round(state_gbps, 2) if state_gbps else None,
         "copy_GBps": round(copy_gbps, 1),
         "frac_of_copy": round(value / copy_gbps, 4),
         "roofline": {
-            "bound": "hbm" if kind != "scan" else "alu",
+            "bound": "hbm" if not seq else "alu",
             "kernel": KERNEL_NAMES[kind] + f"<{fmt}>",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
@@ -342,13 +350,17 @@ def main():
         },
         "device": torch.cuda.get_device_name(0),
     }
-    if kind == "scan":
+    if seq:
         # the state stays on-chip for all T tokens: the scan is bound by VALU issue.  Algorithmic
         # work per entry-step, in VALU lane-instructions: the two fmas of the update, the
         # row's extremes (min3 and max3 each take two new entries: one per entry; the
         # symmetric grid's |.| max3: one half), the rounding fma, and (c - z) plus one fma
-        # for the readout of the new codes; fp32: the product, the fma and the readout fma
+        # for the readout of the new codes; fp32: the product, the fma and the readout fma.
+        # The prefill runs the fp32 step (3) and, once per chunk, the extremes, the rounding
+        # and the dequantization (c - z, times s): 4 more per chunk
         ops = 3 if fmt == "fp32" else (6 if fmt.endswith("asym") else 5.5)
+        if kind == "prefill":
+            ops = 3 + 4.0 / wl["chunk"]
         achieved_ops = rows * N * T * ops / (kernel_ms_mean * 1e-3) / 1e12
         rec["roofline"].update({
             "bound": "alu", "achieved": round(achieved_ops, 3), "peak": VALU_PEAK_TOPS,
@@ -383,6 +395,15 @@ def cpu_baseline(args, wl, bytes_per_launch, rows_per_layer):
             step(st, q, k, v, al, be, 1, nmat)
             done += nmat * P
         sample = f"{nmat} matrices (128 x 128, {fmt}) of the delta layer, one step per call"
+    elif kind == "prefill":
+        Tc = 256
+        x, dt, Bm, Cm, A, D = synth.mamba2_scan_inputs(args.seed, 0, 1, Tc, H, 1, P, N)
+        done, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < args.cpu_seconds:
+            st = oracle.make_state(fmt, H * P, N)
+            oracle.mamba2_prefill(st, x, dt, A, Bm, Cm, D, chunk=wl["chunk"])
+            done += H * P * Tc
+        sample = f"one sequence ({H * P} rows, {fmt}) over a {Tc}-token prompt in chunks of {wl['chunk']}"
     else:
         R = 32768
         srows = np.arange(R, dtype=np.int64)
@@ -401,7 +422,7 @@ def cpu_baseline(args, wl, bytes_per_launch, rows_per_layer):
     out = {"value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
            "sample": sample + f", repeated for {el:.1f} s", "rows_per_s": round(rows_per_s, 1),
            "cpu": _cpu_model()}
-    if kind != "scan":
+    if kind not in ("scan", "prefill"):
         layers = 1 if wl.get("rotate") else wl["layers"]
         out["decode_steps_per_s"] = round(rows_per_s / (rows_per_layer * layers), 5)
     return out

@@ -196,6 +196,23 @@ ssq_status ssq_scan(ssq_state *state, int32_t T, const float *x, const float *dt
                     const float *B, const float *C, const float *D, float *y, int32_t readout,
                     void *stream);
 
+/* A prompt of T tokens with the state quantized only at chunk ends ("Mamba
+ * state quantization for inference", "Mamba state quantization needs
+ * phase-aware benchmarks": DAMP computes the prefill recurrence in FP32 inside
+ * each chunk and writes the chunk-final state into the packed cache, which
+ * decode then reads and rewrites).  Each row is dequantized once,
+ * fl(s*fl(c - z)); every token applies h'_n = fma(lambda, h_n, fl(w*B_n)) in
+ * fp32 and y is read from that fp32 row; after every `chunk` tokens and after
+ * the last one the row is refit and rounded (the state's rounding mode; a
+ * stochastic chunk end at token t draws the uniforms of token step + t), y of
+ * that token follows `readout`, and the row continues from its dequantized new
+ * codes.  The fp32 state runs the plain fp32 recurrence (the scan).  Shapes as
+ * ssq_scan; T > 0, chunk > 0 (a chunk of T or more quantizes once, at the
+ * end). */
+ssq_status ssq_prefill(ssq_state *state, int32_t T, int32_t chunk, const float *x, const float *dt,
+                       const float *A, const float *B, const float *C, const float *D, float *y,
+                       int32_t readout, void *stream);
+
 /* One delta-rule step for every (sequence, head) matrix S:
  *   S' = alpha*(I - beta*k*k^T)*S + beta*k*v^T,  o = S'^T q
  * ("Mamba state quantization for inference": the query reads the matrix,

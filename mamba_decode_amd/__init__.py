@@ -82,6 +82,9 @@ def _load():
     L.ssq_status_string.restype = ctypes.c_char_p
     L.ssq_last_error.argtypes = []
     L.ssq_last_error.restype = ctypes.c_char_p
+    L.ssq_prefill.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, f32p, f32p, f32p, f32p, f32p, f32p, f32p,
+                              ctypes.c_int32, vp]
+    L.ssq_prefill.restype = st
     L.ssq_kda_step.argtypes = [vp, f32p, f32p, f32p, f32p, f32p, f32p, ctypes.c_int32, vp]
     L.ssq_kda_step.restype = st
     u64 = ctypes.c_uint64
@@ -251,6 +254,17 @@ def ssq_scan(state: State, T: int, x, dt, A, B, C, D, y, readout: int = SSQ_READ
     _check(lib.ssq_scan(state.handle, T, _dev(x, "x", xs), _dev(dt, "dt", dts), _dev(A, "A", nh),
                         _dev(B, "B", bcs), _dev(C, "C", bcs), _dev(D, "D", nh), _dev(y, "y", xs),
                         readout, _stream(stream)), "ssq_scan")
+
+
+def ssq_prefill(state: State, T: int, chunk: int, x, dt, A, B, C, D, y, readout: int = SSQ_READ_POST_QUANT,
+                stream=None):
+    d = state.desc
+    Tn = max(int(T), 0)
+    xs, dts, bcs, nh = _sizes(state, SSQ_MAMBA2, d.batch * d.nheads * d.rows_per_head * Tn,
+                              d.batch * Tn * d.nheads, d.batch * Tn * d.ngroups * d.row_len, d.nheads)
+    _check(lib.ssq_prefill(state.handle, T, chunk, _dev(x, "x", xs), _dev(dt, "dt", dts), _dev(A, "A", nh),
+                           _dev(B, "B", bcs), _dev(C, "C", bcs), _dev(D, "D", nh), _dev(y, "y", xs),
+                           readout, _stream(stream)), "ssq_prefill")
 
 
 def ssq_delta_step(state: State, q, k, v, alpha, beta, o, readout: int = SSQ_READ_POST_QUANT, stream=None):

@@ -339,6 +339,23 @@ ssq_status ssq_scan(ssq_state* st, int32_t T, const float* x, const float* dt, c
     return s;
 }
 
+ssq_status ssq_prefill(ssq_state* st, int32_t T, int32_t chunk, const float* x, const float* dt, const float* A,
+                       const float* B, const float* C, const float* D, float* y, int32_t readout, void* stream)
+{
+    ssq::M2Args a;
+    ssq_status s = fill_m2(st, x, dt, A, B, C, D, y, readout, &a);
+    if (s != SSQ_OK) return s;
+    SSQ_REQUIRE(T > 0, SSQ_ERR_INVALID_ARG, "T must be positive");
+    SSQ_REQUIRE(chunk > 0, SSQ_ERR_INVALID_ARG, "chunk must be positive");
+    a.T = T;
+    a.sr = sr_args(st);
+    s = from_hip(ssq::launch_m2_prefill(st->desc.format, a, chunk, readout == SSQ_READ_PRE_QUANT,
+                                        (hipStream_t)stream),
+                 "prefill launch");
+    if (s == SSQ_OK) advance(st, (uint64_t)T);
+    return s;
+}
+
 static ssq_status delta_common(ssq_state* st, const float* q, const float* k, const float* v, const float* alpha,
                                const float* beta, float* o, int32_t readout, void* stream, bool kda)
 {

@@ -152,6 +152,45 @@ struct RowStep {
         return g.s * acc + dx;
     }
 
+    // refit and round the fp32 row h in place: h becomes f = 1.5*2^23 + code, g the new grid
+    template <bool SR>
+    __device__ __forceinline__ static void requant(float* h, RowGrid& g, uint64_t sr_seed, uint64_t ctr0)
+    {
+        using Tr = Traits<F>;
+        float mn = 0.0f, mx = 0.0f, am = 0.0f;
+        if constexpr (Tr::asym) {
+            mn = h[0];
+            mx = h[0];
+#pragma unroll
+            for (int e = 1; e < E; ++e) {
+                mn = fminf(mn, h[e]);
+                mx = fmaxf(mx, h[e]);
+            }
+            mn = group_min<LPR>(mn);
+            mx = group_max<LPR>(mx);
+        } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e) am = fmaxf(am, fabsf(h[e]));
+            am = group_max<LPR>(am);
+        }
+        if (__all(refit_fast<F>(mn, mx, am, g))) {
+            if constexpr (SR) {
+                round_codes_sr<F, E>(h, g, sr_seed, ctr0, h);
+            } else {
+#pragma unroll
+                for (int e = 0; e < E; ++e) h[e] = __builtin_fmaf(h[e], g.inv, g.Mz);
+            }
+        } else {
+            g = refit<F>(mn, mx, am);
+            if constexpr (SR) {
+                round_codes_sr<F, E>(h, g, sr_seed, ctr0, h);
+            } else {
+                const bool slow_any = Tr::asym && __any(g.slow);
+                round_codes<F, E>(h, g, slow_any, h);
+            }
+        }
+    }
+
     // fp32 control: hv in/out, returns y
     template <typename In>
     __device__ __forceinline__ static float run_f(float* hv, float lam, float w, float dx, const In& in)
@@ -459,6 +498,126 @@ __global__ __launch_bounds__(256, PRE ? SSQ_SCAN_WAVES - 1 : SSQ_SCAN_WAVES) voi
     }
 }
 
+// ---------------------------------------------------------------------------
+// prefill: the fp32 recurrence inside each chunk, the state quantized at chunk ends
+// ---------------------------------------------------------------------------
+// Same row mapping and B/C pipeline as the scan.  Each row is dequantized once,
+// s*(c - z), and kept in fp32; every token applies h = fma(lambda, h, w*B) and
+// reads y from it; at the end of each chunk of `chunk` tokens, and after the last
+// token, the row is refit and rounded (to nearest or stochastically), y follows
+// the readout flag, and the row continues from its dequantized new codes.  The
+// packed codes of the last chunk end are stored once at the end.
+#ifndef SSQ_PREFILL_WAVES
+#define SSQ_PREFILL_WAVES 3
+#endif
+template <int F, int LPR, bool PRE, bool SR>
+__global__ __launch_bounds__(256, PRE ? SSQ_PREFILL_WAVES - 1 : SSQ_PREFILL_WAVES) void k_m2_prefill(M2Args a, int chunk)
+{
+    using Tr = Traits<F>;
+    static_assert(Tr::quant, "the fp32 state's prefill is the scan");
+    using RS = RowStep<F, LPR, PRE>;
+    constexpr int E = RS::E, NW = RS::NW, RPW = 64 / LPR, ROWB = RowBytes<F>::value;
+    constexpr int PITCH = RS::LDS_PITCH, LDSF = RS::LDS_FLOATS;
+    __shared__ float4 bc_lds[4 * 2 * 2 * LDSF / 4]; // [wave][buffer][B, C][LDSF]
+    const int lane = threadIdx.x & 63, sub = lane / LPR, part = lane % LPR;
+    const int64_t it = wave_id();
+    if (it >= a.total_iters) return;
+    const int64_t row0 = it * RPW;
+    const int64_t bh = row0 / a.P;
+    const int b = (int)(bh / a.H), h = (int)(bh % a.H);
+    const int g = h / (a.H / a.G);
+    const int64_t row = row0 + sub;
+    const int p = (int)(row % a.P);
+    const int T = a.T, H = a.H, P = a.P, G = a.G;
+    const float Ah = a.A[h], Dh = a.D[h];
+
+    uint32_t cw[NW];
+    load_words<NW>(a.codes + row * ROWB + part * (NW * 4), cw);
+    float s = a.scale[row];
+    float z = Tr::asym ? a.zero[row] : 0.0f;
+    float hv[E];
+    unpack_codes<F, E>(cw, hv);
+#pragma unroll
+    for (int e = 0; e < E; ++e) hv[e] = s * (hv[e] - z); // the stored row's value, fl(s*fl(c - z))
+
+    float* const wl = reinterpret_cast<float*>(bc_lds) + (threadIdx.x >> 6) * (4 * LDSF);
+    const int n2 = 2 * lane, st_off = (n2 / E) * PITCH + n2 % E;
+    auto bc_at = [&](const float* base, int t) {
+        return *reinterpret_cast<const float2*>(base + (((int64_t)b * T + t) * G + g) * 128 + n2);
+    };
+    auto stage = [&](int buf, float2 bv, float2 cv) {
+        *reinterpret_cast<float2*>(wl + buf * (2 * LDSF) + st_off) = bv;
+        *reinterpret_cast<float2*>(wl + buf * (2 * LDSF) + LDSF + st_off) = cv;
+    };
+    auto x_idx = [&](int t) { return (((int64_t)b * T + t) * H + h) * P + p; };
+
+    stage(0, bc_at(a.Bm, 0), bc_at(a.Cm, 0));
+    const int t1 = T > 1 ? 1 : 0;
+    float2 bn = bc_at(a.Bm, t1), cn = bc_at(a.Cm, t1);
+    float xv = a.x[x_idx(0)], xn = a.x[x_idx(t1)];
+    float dt_l = 0.0f, lam_l = 0.0f;
+
+    for (int t = 0; t < T; ++t) {
+        if ((t & 63) == 0) {
+            const int tt = t + lane;
+            if (tt < T) {
+                dt_l = a.dt[((int64_t)b * T + tt) * H + h];
+                lam_l = decay(dt_l, Ah);
+            }
+        }
+        const float lam = readlane_f(lam_l, t & 63);
+        const float dtv = readlane_f(dt_l, t & 63);
+        const int t2 = t + 2 < T ? t + 2 : T - 1;
+        const float2 bf = bc_at(a.Bm, t2), cf2 = bc_at(a.Cm, t2);
+        const float xf = a.x[x_idx(t2)];
+
+        const float* const cur = wl + (t & 1) * (2 * LDSF);
+        const typename RS::RowInLds in{cur + part * PITCH, cur + LDSF + part * PITCH};
+        const float w = dtv * xv;
+        const float dx = Dh * xv;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const float wb = w * in.b(e);
+            hv[e] = __builtin_fmaf(lam, hv[e], wb);
+        }
+        const bool end = (t + 1) % chunk == 0 || t == T - 1; // wave-uniform
+        float acc = 0.0f;
+        if (!end || PRE) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc = __builtin_fmaf(in.c(e), hv[e], acc);
+        }
+        if (end) {
+            RowGrid gr;
+            const uint64_t ctr0 =
+                SR ? (((a.sr.step + (uint64_t)t) * (uint64_t)a.sr.rows + (uint64_t)row) * 128u + (uint64_t)(part * E))
+                   : 0;
+            RS::template requant<SR>(hv, gr, a.sr.seed, ctr0);
+            pack_codes<F, E>(hv, cw);
+            s = gr.s;
+            z = gr.z;
+#pragma unroll
+            for (int e = 0; e < E; ++e) hv[e] = s * ((hv[e] - kMagic) - z); // fl(s*fl(c - z))
+            if constexpr (!PRE) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc = __builtin_fmaf(in.c(e), hv[e], acc);
+            }
+        }
+        a.y[x_idx(t)] = group_sum<LPR>(acc) + dx;
+
+        stage((t + 1) & 1, bn, cn);
+        bn = bf;
+        cn = cf2;
+        xv = xn;
+        xn = xf;
+    }
+
+    store_words<NW>(a.codes + row * ROWB + part * (NW * 4), cw);
+    if (part == 0) {
+        a.scale[row] = s;
+        if constexpr (Tr::asym) a.zero[row] = z;
+    }
+}
+
 template <int F, int LPR>
 __global__ __launch_bounds__(256) void k_quantize_rows(QArgs a)
 {
@@ -683,6 +842,44 @@ static hipError_t launch_scan_f(M2Args a, bool pre, hipStream_t st)
     else
         hipLaunchKernelGGL((k_m2_scan<F, LPR, false, false>), dim3(blocks), dim3(256), 0, st, a);
     return hipGetLastError();
+}
+
+template <int F>
+static hipError_t launch_prefill_f(M2Args a, int chunk, bool pre, hipStream_t st)
+{
+    if constexpr (!Traits<F>::quant) {
+        return launch_scan_f<F>(a, pre, st); // the fp32 state's prefill is the scan
+    } else {
+        constexpr int LPR = lanes_per_row<F>();
+        constexpr int RPW = 64 / LPR;
+        a.total_iters = (int64_t)a.Bsz * a.H * a.P / RPW;
+        a.iters_per_wave = 1;
+        const unsigned blocks = (unsigned)((a.total_iters + 3) / 4);
+        if (a.sr.on) {
+            if (pre)
+                hipLaunchKernelGGL((k_m2_prefill<F, LPR, true, true>), dim3(blocks), dim3(256), 0, st, a, chunk);
+            else
+                hipLaunchKernelGGL((k_m2_prefill<F, LPR, false, true>), dim3(blocks), dim3(256), 0, st, a, chunk);
+        } else {
+            if (pre)
+                hipLaunchKernelGGL((k_m2_prefill<F, LPR, true, false>), dim3(blocks), dim3(256), 0, st, a, chunk);
+            else
+                hipLaunchKernelGGL((k_m2_prefill<F, LPR, false, false>), dim3(blocks), dim3(256), 0, st, a, chunk);
+        }
+        return hipGetLastError();
+    }
+}
+
+hipError_t launch_m2_prefill(int fmt, M2Args a, int chunk, bool pre, hipStream_t st)
+{
+    switch (fmt) {
+    case FP32: return launch_prefill_f<FP32>(a, chunk, pre, st);
+    case INT8_SYM: return launch_prefill_f<INT8_SYM>(a, chunk, pre, st);
+    case INT8_ASYM: return launch_prefill_f<INT8_ASYM>(a, chunk, pre, st);
+    case INT4_SYM: return launch_prefill_f<INT4_SYM>(a, chunk, pre, st);
+    case INT4_ASYM: return launch_prefill_f<INT4_ASYM>(a, chunk, pre, st);
+    }
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_m2_scan(int fmt, M2Args a, bool pre, hipStream_t st)

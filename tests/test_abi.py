@@ -117,6 +117,7 @@ def test_null_arguments_are_rejected_before_any_device_call():
         == ssq.SSQ_ERR_INVALID_ARG
     assert L.ssq_decode_step(None, None, None, None, None, None, None, None, 0, None) == ssq.SSQ_ERR_INVALID_ARG
     assert L.ssq_scan(None, 4, None, None, None, None, None, None, None, 0, None) == ssq.SSQ_ERR_INVALID_ARG
+    assert L.ssq_prefill(None, 4, 2, None, None, None, None, None, None, None, 0, None) == ssq.SSQ_ERR_INVALID_ARG
     assert L.ssq_delta_step(None, None, None, None, None, None, None, 0, None) == ssq.SSQ_ERR_INVALID_ARG
     assert L.ssq_kda_step(None, None, None, None, None, None, None, 0, None) == ssq.SSQ_ERR_INVALID_ARG
     assert L.ssq_dequant(None, None, None) == ssq.SSQ_ERR_INVALID_ARG
