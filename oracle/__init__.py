@@ -97,6 +97,13 @@ def bind(path: str):
     L.orc_mamba2_prefill_sr.argtypes = [ci, ci, ci, ci, ci, ci, ci, ci, ci, i32p, f32p, f32p, f32p,
                                         f32p, f32p, f32p, f32p, f32p, f32p, f32p, ci, ci, u64, u64]
     L.orc_mamba2_prefill_sr.restype = ci
+    L.orc_round_half.argtypes = [ctypes.c_float]
+    L.orc_round_half.restype = ctypes.c_float
+    L.orc_damp_step_sr.argtypes = [ci, ci, ci, ci, ci, f32p, i32p, f32p, f32p, f32p, f32p, f32p, f32p,
+                                   f32p, f32p, ci, f32p, ci, u64, u64]
+    L.orc_damp_step_sr.restype = ci
+    L.orc_damp_from_fp32.argtypes = [ci, ci, ci, ci, ci, f32p, f32p, i32p, f32p, f32p]
+    L.orc_damp_from_fp32.restype = ci
     return L
 
 
@@ -350,3 +357,66 @@ def mamba2_prefill(st: State, x, dt, A, Bm, Cm, D, chunk: int, readout: str = "p
                                      _f(Cm), _f(D), _f(y), _ro(readout), *_sr_args(sr))
     assert rc == 0
     return y
+
+
+# --------------------------------------------------------------------------
+# DAMP-style two-tier delta state: rows rotated by Hs = H_128/16, the first
+# NHI key channels of each matrix in half precision, the rest int8 asymmetric
+# --------------------------------------------------------------------------
+DAMP_NHI = 16
+
+
+@dataclass
+class DampState:
+    """``hi`` [mats][nhi][dv] half values (as float32), ``code`` [mats*(dk-nhi)][dv] int32,
+    ``scale``/``zero`` [mats*(dk-nhi)]; all rows in rotated coordinates."""
+    mats: int
+    dk: int
+    dv: int
+    nhi: int
+    hi: np.ndarray
+    code: np.ndarray
+    scale: np.ndarray
+    zero: np.ndarray
+
+    def copy(self) -> "DampState":
+        return DampState(self.mats, self.dk, self.dv, self.nhi, self.hi.copy(), self.code.copy(),
+                         self.scale.copy(), self.zero.copy())
+
+    def rotated(self) -> np.ndarray:
+        """The stored rows' values [mats][dk][dv] (rotated coordinates)."""
+        lo = dequantize_rows(self.code, self.scale, self.zero).reshape(self.mats, self.dk - self.nhi, self.dv)
+        return np.concatenate([self.hi.reshape(self.mats, self.nhi, self.dv), lo], axis=1)
+
+
+def round_half(x: float) -> float:
+    return float(lib().orc_round_half(ctypes.c_float(x)))
+
+
+def damp_from_fp32(S: np.ndarray, Bsz: int, H: int, nhi: int = DAMP_NHI) -> DampState:
+    """The two-tier state of an fp32 state ``S`` [Bsz][H][dk][dv] (original coordinates)."""
+    S = _c32(S)
+    dk, dv = S.shape[-2], S.shape[-1]
+    mats = Bsz * H
+    hi = np.empty((mats, nhi, dv), np.float32)
+    code = np.empty((mats * (dk - nhi), dv), np.int32)
+    s = np.empty(mats * (dk - nhi), np.float32)
+    z = np.empty(mats * (dk - nhi), np.float32)
+    rc = lib().orc_damp_from_fp32(Bsz, H, dk, dv, nhi, _f(S), _f(hi), _i(code), _f(s), _f(z))
+    assert rc == 0
+    return DampState(mats, dk, dv, nhi, hi, code, s, z)
+
+
+def damp_step(st: DampState, q, k, v, alpha, beta, Bsz: int, H: int, readout: str = "post",
+              diag: bool = False, sr=None):
+    """One step of the two-tier delta state; returns ``o`` [B][H][dv] (and the rotated
+    pre-rounding matrices [mats][dk][dv] with ``diag``)."""
+    q, k, v, alpha, beta = map(_c32, (q, k, v, alpha, beta))
+    assert st.mats == Bsz * H
+    o = np.empty((Bsz, H, st.dv), np.float32)
+    Spre = np.empty((st.mats, st.dk, st.dv), np.float32) if diag else None
+    rc = lib().orc_damp_step_sr(Bsz, H, st.dk, st.dv, st.nhi, _f(st.hi), _i(st.code), _f(st.scale),
+                                _f(st.zero), _f(q), _f(k), _f(v), _f(alpha), _f(beta), _f(o),
+                                _ro(readout), _f(Spre), *_sr_args(sr))
+    assert rc == 0
+    return (o, Spre) if diag else o

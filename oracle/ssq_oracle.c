@@ -751,3 +751,206 @@ int orc_mamba2_prefill_sr(int Bsz, int T, int chunk, int H, int G, int P, int N,
     free(U);
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* DAMP-style two-tier delta state                                          */
+/* ------------------------------------------------------------------------ */
+
+/* The nearest IEEE half-precision value to x (ties to even), as a float:
+ * 10 fraction bits, quantum 2^(e-10) for 2^e <= |x| < 2^(e+1) and e >= -14,
+ * 2^-24 below (subnormals); a result above 65504 is infinite.  x/q is exact
+ * (a power-of-two scaling), and rint() rounds it half to even. */
+float orc_round_half(float x)
+{
+    double a = fabs((double)x), q, r;
+    int e;
+    if (a == 0.0 || x != x)
+        return x;
+    e = (int)floor(log2(a));
+    if (ldexp(1.0, e) > a) /* log2 rounding near powers of two */
+        e -= 1;
+    else if (ldexp(1.0, e + 1) <= a)
+        e += 1;
+    if (e < -14)
+        e = -14;
+    q = ldexp(1.0, e - 10);
+    r = rint((double)x / q) * q;
+    if (fabs(r) > 65504.0)
+        return x > 0 ? INFINITY : -INFINITY;
+    return (float)r;
+}
+
+/* Entry (j, i) of the scaled Sylvester-Hadamard matrix Hs = H_128 / 16: (-1)^popcount(i & j) / 16.
+ * Hs is symmetric and Hs*Hs = I/2. */
+static double hs(int j, int i)
+{
+    int v = i & j, c = 0;
+    while (v) {
+        c += v & 1;
+        v >>= 1;
+    }
+    return (c & 1) ? -1.0 / 16.0 : 1.0 / 16.0;
+}
+
+/* One step of the two-tier delta-rule state of one layer ("Mamba state
+ * quantization for inference", "Mixed precision spends bits on persistent
+ * channels": a Hadamard transform along each key channel's value dimension,
+ * the protected key channels in FP16 and the rest in INT8 with scale and
+ * zero point, selected channels permuted to be contiguous; the fused kernel
+ * reconstructs the low tier, runs the recurrence in FP32, refits and writes
+ * the packed state back).  The protected channels are key channels 0 .. nhi-1
+ * (the model's key projection is permuted offline so that they come first).
+ * The stored matrix is the rotated St = S Hs, row by row; in those
+ * coordinates the step is the scalar-decay delta rule with v rotated and o
+ * rotated back (Hs is symmetric and Hs Hs = I/2):
+ *   vt = Hs v  (exact in double, rounded once)
+ *   ut = k^T St  (double, rounded once), wt = fl(beta*fl(vt - fl(alpha*ut)))
+ *   St'_ij = fma(alpha, St_ij, fl(k_i*wt_j))            (FP16 rows, i < nhi)
+ *   St'_ij = fma(as_i, c_ij, fma(k_i, wt_j, -fl(as_i*z_i)))  (INT8 rows)
+ *   FP16 rows stored rounded to half, INT8 rows refit and rounded (asymmetric)
+ *   ot = St'^T q over the stored (post) or pre-rounding rows, o = 2 Hs ot
+ *   (ot and o in double, o rounded once).
+ *   hi [Bsz][H][nhi][dv] (half values held in floats), code [Bsz][H][dk-nhi][dv],
+ *   s/z [Bsz][H][dk-nhi]; q, k [Bsz][H][dk], v [Bsz][H][dv], alpha/beta [Bsz][H],
+ *   o [Bsz][H][dv].  dv must be 128. */
+int orc_damp_step_sr(int Bsz, int H, int dk, int dv, int nhi, float *hi, int32_t *code, float *s,
+                     float *z, const float *q, const float *k, const float *v, const float *alpha,
+                     const float *beta, float *o, int readout_pre, float *Spre, int sr, uint64_t seed,
+                     uint64_t step)
+{
+    int64_t m, nm = (int64_t)Bsz * H;
+    int nlo = dk - nhi, i, j;
+    int64_t rows = nm * nlo;
+    float *St, *vt, *ut, *wt, *U;
+    double *ot;
+    if (Bsz <= 0 || H <= 0 || dk <= 0 || dv != 128 || nhi < 0 || nhi > dk)
+        return -1;
+    St = (float *)malloc(sizeof(float) * (size_t)dk * dv);
+    vt = (float *)malloc(sizeof(float) * (size_t)dv);
+    ut = (float *)malloc(sizeof(float) * (size_t)dv);
+    wt = (float *)malloc(sizeof(float) * (size_t)dv);
+    U = (float *)malloc(sizeof(float) * (size_t)dv);
+    ot = (double *)malloc(sizeof(double) * (size_t)dv);
+    if (!St || !vt || !ut || !wt || !U || !ot) {
+        free(St); free(vt); free(ut); free(wt); free(U); free(ot);
+        return -1;
+    }
+    for (m = 0; m < nm; ++m) {
+        float al = alpha[m], be = beta[m];
+        const float *km = k + m * dk, *qm = q + m * dk, *vm = v + m * dv;
+        float *him = hi + m * (int64_t)nhi * dv;
+        int32_t *cm = code + m * (int64_t)nlo * dv;
+        float *sm = s + m * nlo, *zm = z + m * nlo;
+        /* vt = Hs v: 128 multiples of 1/16 of floats, exact in double */
+        for (j = 0; j < dv; ++j) {
+            double a = 0.0;
+            for (i = 0; i < dv; ++i)
+                a += hs(j, i) * (double)vm[i];
+            vt[j] = (float)a;
+        }
+        /* ut = k^T St over the stored rows (exact values: half rows, s*(c - z) rows) */
+        for (j = 0; j < dv; ++j) {
+            double a = 0.0;
+            for (i = 0; i < dk; ++i) {
+                if (i < nhi) {
+                    a += (double)km[i] * (double)him[(int64_t)i * dv + j];
+                } else {
+                    int li = i - nhi;
+                    float d = (float)cm[(int64_t)li * dv + j] - zm[li];
+                    a += ((double)km[i] * (double)sm[li]) * (double)d;
+                }
+            }
+            ut[j] = (float)a;
+        }
+        for (j = 0; j < dv; ++j) {
+            float au = al * ut[j];
+            float vmj = vt[j] - au;
+            wt[j] = be * vmj;
+        }
+        for (i = 0; i < dk; ++i) {
+            for (j = 0; j < dv; ++j) {
+                float nv;
+                if (i < nhi) {
+                    float kw = km[i] * wt[j];
+                    nv = fmaf(al, him[(int64_t)i * dv + j], kw);
+                } else {
+                    int li = i - nhi;
+                    float as = al * sm[li];
+                    float az = as * zm[li];
+                    float kw = fmaf(km[i], wt[j], -az);
+                    nv = fmaf(as, (float)cm[(int64_t)li * dv + j], kw);
+                }
+                St[(int64_t)i * dv + j] = nv;
+            }
+        }
+        if (Spre)
+            memcpy(Spre + m * (int64_t)dk * dv, St, sizeof(float) * (size_t)dk * dv);
+        for (j = 0; j < dv; ++j)
+            ot[j] = 0.0;
+        if (readout_pre)
+            for (i = 0; i < dk; ++i)
+                for (j = 0; j < dv; ++j)
+                    ot[j] += (double)qm[i] * (double)St[(int64_t)i * dv + j];
+        for (i = 0; i < dk; ++i) {
+            float *row = St + (int64_t)i * dv;
+            if (i < nhi) {
+                for (j = 0; j < dv; ++j) {
+                    him[(int64_t)i * dv + j] = orc_round_half(row[j]);
+                    row[j] = him[(int64_t)i * dv + j];
+                }
+            } else {
+                int li = i - nhi;
+                if (sr)
+                    orc_sr_row_uniforms(seed, step, rows, m * nlo + li, dv, U);
+                orc_quantize_row_sr(row, dv, 8, 1, cm + (int64_t)li * dv, sm + li, zm + li, NULL,
+                                    sr ? U : NULL);
+                orc_dequantize_row(cm + (int64_t)li * dv, dv, sm[li], zm[li], row);
+            }
+        }
+        if (!readout_pre)
+            for (i = 0; i < dk; ++i)
+                for (j = 0; j < dv; ++j)
+                    ot[j] += (double)qm[i] * (double)St[(int64_t)i * dv + j];
+        /* o = 2 Hs ot */
+        for (j = 0; j < dv; ++j) {
+            double a = 0.0;
+            for (i = 0; i < dv; ++i)
+                a += hs(j, i) * ot[i];
+            o[m * dv + j] = (float)(2.0 * a);
+        }
+    }
+    free(St); free(vt); free(ut); free(wt); free(U); free(ot);
+    return 0;
+}
+
+/* The two-tier state from an fp32 state S [Bsz][H][dk][dv] (original coordinates):
+ * every row rotated, St = S Hs (double, rounded once), the first nhi rows of each
+ * matrix rounded to half, the rest quantized (asymmetric int8, to nearest). */
+int orc_damp_from_fp32(int Bsz, int H, int dk, int dv, int nhi, const float *S, float *hi,
+                       int32_t *code, float *s, float *z)
+{
+    int64_t m, nm = (int64_t)Bsz * H;
+    int nlo = dk - nhi, i, j, c;
+    float *row = (float *)malloc(sizeof(float) * (size_t)dv);
+    if (!row || dv != 128)
+        return -1;
+    for (m = 0; m < nm; ++m)
+        for (i = 0; i < dk; ++i) {
+            const float *src = S + (m * dk + i) * (int64_t)dv;
+            for (j = 0; j < dv; ++j) {
+                double a = 0.0;
+                for (c = 0; c < dv; ++c)
+                    a += (double)src[c] * hs(c, j);
+                row[j] = (float)a;
+            }
+            if (i < nhi) {
+                for (j = 0; j < dv; ++j)
+                    hi[(m * nhi + i) * (int64_t)dv + j] = orc_round_half(row[j]);
+            } else {
+                int64_t li = m * nlo + (i - nhi);
+                orc_quantize_row(row, dv, 8, 1, code + li * dv, s + li, z + li, NULL);
+            }
+        }
+    free(row);
+    return 0;
+}

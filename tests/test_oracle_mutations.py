@@ -17,6 +17,7 @@ from tests import test_oracle_pins as pins
 from tests import test_oracle_sr as sr_pins
 from tests import test_oracle_kda as kda_pins
 from tests import test_oracle_prefill as prefill_pins
+from tests import test_oracle_damp as damp_pins
 
 SRC = open(os.path.join(os.path.dirname(oracle.__file__), "ssq_oracle.c")).read()
 
@@ -90,13 +91,22 @@ MUTATIONS = [
      "sr ? U : NULL);"),
     ("chunk-end uniforms of the first token", "orc_sr_row_uniforms(seed, step + (uint64_t)t, rows, row, N, U);",
      "orc_sr_row_uniforms(seed, step, rows, row, N, U);"),
+    ("Hadamard sign from the wrong bit", "return (c & 1) ? -1.0 / 16.0 : 1.0 / 16.0;",
+     "return (c & 2) ? -1.0 / 16.0 : 1.0 / 16.0;"),
+    ("v not rotated", "a += hs(j, i) * (double)vm[i];", "a += (i == j ? 1.0 : 0.0) * (double)vm[i];"),
+    ("o not rotated back", "o[m * dv + j] = (float)(2.0 * a);", "o[m * dv + j] = (float)ot[j];"),
+    ("half tier keeps the unrounded value", "him[(int64_t)i * dv + j] = orc_round_half(row[j]);",
+     "him[(int64_t)i * dv + j] = row[j];"),
+    ("half rounding ties away from zero", "r = rint((double)x / q) * q;", "r = round((double)x / q) * q;"),
+    ("two-tier u ignores the half rows", "a += (double)km[i] * (double)him[(int64_t)i * dv + j];",
+     "a += 0.0 * (double)him[(int64_t)i * dv + j];"),
 ]
 
 
 def _pin_cases():
     cases = []
     members = []
-    for mod in (pins, sr_pins, kda_pins, prefill_pins):
+    for mod in (pins, sr_pins, kda_pins, prefill_pins, damp_pins):
         members += inspect.getmembers(mod, inspect.isfunction)
     for name, fn in members:
         if not name.startswith("test_"):
