@@ -48,6 +48,10 @@ WORKLOADS = {
     "delta_int8": dict(kind="delta", layers=30, B=256, H=32, P=128, fmt="int8_asym", init="random",
                        desc="Delta-rule (GDN/KDA-style) decode step: 30 layers x 32 heads x 128 x 128, batch 256, "
                             "int8 asymmetric per-row state, seeded random state with 5% x20 outlier rows"),
+    "damp_int8": dict(kind="delta", layers=30, B=256, H=32, P=128, fmt="damp", init="random",
+                      desc="Two-tier delta-rule decode step: 30 layers x 32 heads x 128 x 128, batch 256, key "
+                           "rows 0..15 in half precision and 16..127 as uint8 with scale and zero point, rows "
+                           "rotated by a 128-point Hadamard transform; seeded random state with 5% x20 outlier rows"),
     "kda_int8": dict(kind="kda", layers=30, B=256, H=32, P=128, fmt="int8_asym", init="random",
                      desc="KDA-style decode step (a decay per key channel): 30 layers x 32 heads x 128 x 128, "
                           "batch 256, int8 asymmetric per-row state, seeded random state with 5% x20 outlier rows"),
@@ -135,6 +139,9 @@ def main():
     lay = ssq.ssq_state_layout(desc)
     meta = 0 if fmt == "fp32" else (8 if fmt.endswith("asym") else 4)
     state_bytes_layer = 2 * rows * (lay.row_bytes + meta)  # read once + written once
+    if fmt == "damp":  # 112 uint8 rows (128 B + scale + zero) and 16 half rows (256 B) per matrix
+        mats = rows // P
+        state_bytes_layer = 2 * mats * ((P - ssq.SSQ_DAMP_NHI) * (128 + 8) + ssq.SSQ_DAMP_NHI * 256)
     log(f"[bench] workload {args.workload}: {L} layer(s), {rows} rows/layer, {fmt}, "
         f"{lay.total_bytes / 2**20:.1f} MiB state/layer")
 
@@ -384,9 +391,13 @@ def cpu_baseline(args, wl, bytes_per_launch, rows_per_layer):
     if kind in ("delta", "kda"):
         nmat = 64
         init = synth.init_state(args.seed, 0, nmat * P, N)
-        st = oracle.make_state(fmt, nmat * P, N, init)
         q, k, v, al, be = synth.delta_inputs(args.seed, 0, 1, nmat, P, N)
-        step = oracle.delta_step
+        if fmt == "damp":
+            st = oracle.damp_from_fp32(init.reshape(1, nmat, P, N), 1, nmat)
+            step = oracle.damp_step
+        else:
+            st = oracle.make_state(fmt, nmat * P, N, init)
+            step = oracle.delta_step
         if kind == "kda":
             al = synth.kda_alpha(args.seed, 0, 1, nmat, P)
             step = oracle.kda_step

@@ -86,8 +86,26 @@ typedef enum {
     SSQ_INT8_SYM = 1,  /* int8_t codes in [-127, 127], fp32 scale */
     SSQ_INT8_ASYM = 2, /* uint8_t codes in [0, 255], fp32 scale and integer-valued fp32 zero point */
     SSQ_INT4_SYM = 3,  /* 4-bit two's complement codes in [-7, 7], two per byte, fp32 scale */
-    SSQ_INT4_ASYM = 4  /* 4-bit codes in [0, 15], two per byte, fp32 scale and zero point */
+    SSQ_INT4_ASYM = 4, /* 4-bit codes in [0, 15], two per byte, fp32 scale and zero point */
+    SSQ_DAMP = 5       /* SSQ_DELTA only: two tiers, see below */
 } ssq_format;
+
+/* SSQ_DAMP: the two-tier delta-rule state of "Mamba state quantization for
+ * inference", "Mixed precision spends bits on persistent channels" (a Hadamard
+ * transform along each key channel's value dimension; the protected key
+ * channels in FP16, the rest in INT8 with scale and zero point, the protected
+ * channels permuted to be contiguous).  Here: key channels 0 .. SSQ_DAMP_NHI-1
+ * of every matrix are the protected ones (the model's key projection is
+ * permuted offline so that they come first); every row is stored rotated,
+ * St = S Hs with Hs = H_128/16 (Sylvester-ordered Hadamard, Hs Hs = I/2); the
+ * protected rows as IEEE half values (round to nearest even), the others as
+ * asymmetric uint8 codes with an fp32 scale and zero point, refit every step.
+ * 9.44 bits per value.  A step is the scalar-decay delta rule in the rotated
+ * coordinates: vt = Hs v (exact sum in double, rounded once), ut = k^T St,
+ * wt = beta*(vt - alpha*ut), St' = alpha*St + k wt^T (fma order of the fp32
+ * state for the half rows, of the quantized state for the uint8 rows), and
+ * o = 2 Hs (St'^T q).  ssq_dequant returns S = 2 St Hs. */
+#define SSQ_DAMP_NHI 16
 
 typedef enum { SSQ_MAMBA2 = 0, SSQ_DELTA = 1 } ssq_kind;
 
@@ -113,6 +131,9 @@ typedef struct {
  *          low nibble of byte j.  For SSQ_FP32 this region is the fp32 state.
  *   scale  at scale_offset: one fp32 per row (quantized formats, else 0)
  *   zero   at zero_offset:  one fp32 per row (asymmetric formats, else 0)
+ *   SSQ_DAMP: codes, scale and zero hold the uint8 rows only,
+ *          [batch][nheads][dk - SSQ_DAMP_NHI], and the half rows sit at
+ *          hi_offset.  `rows` counts every key row.
  * Every region starts 256-byte aligned.  A zero state has all bytes 0. */
 typedef struct {
     size_t rows;
@@ -121,6 +142,7 @@ typedef struct {
     size_t scale_offset;
     size_t zero_offset;
     size_t total_bytes;
+    size_t hi_offset; /* SSQ_DAMP: the half rows [batch][nheads][SSQ_DAMP_NHI][128]; else 0 */
 } ssq_layout;
 
 typedef struct ssq_state ssq_state; /* opaque handle: one layer's state */

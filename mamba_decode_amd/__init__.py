@@ -22,7 +22,8 @@ LIB_PATH = os.path.join(_HERE, "libssq.so")
 # ssq_status
 SSQ_OK, SSQ_ERR_INVALID_ARG, SSQ_ERR_UNSUPPORTED, SSQ_ERR_KIND_MISMATCH, SSQ_ERR_ALLOC, SSQ_ERR_DEVICE = range(6)
 # ssq_format
-SSQ_FP32, SSQ_INT8_SYM, SSQ_INT8_ASYM, SSQ_INT4_SYM, SSQ_INT4_ASYM = range(5)
+SSQ_FP32, SSQ_INT8_SYM, SSQ_INT8_ASYM, SSQ_INT4_SYM, SSQ_INT4_ASYM, SSQ_DAMP = range(6)
+SSQ_DAMP_NHI = 16
 # ssq_kind
 SSQ_MAMBA2, SSQ_DELTA = 0, 1
 # ssq_readout
@@ -31,8 +32,8 @@ SSQ_READ_POST_QUANT, SSQ_READ_PRE_QUANT = 0, 1
 SSQ_ROUND_NEAREST, SSQ_ROUND_STOCHASTIC = 0, 1
 
 FORMAT_NAMES = {"fp32": SSQ_FP32, "int8_sym": SSQ_INT8_SYM, "int8_asym": SSQ_INT8_ASYM,
-                "int4_sym": SSQ_INT4_SYM, "int4_asym": SSQ_INT4_ASYM}
-FORMAT_BITS = {SSQ_FP32: 32, SSQ_INT8_SYM: 8, SSQ_INT8_ASYM: 8, SSQ_INT4_SYM: 4, SSQ_INT4_ASYM: 4}
+                "int4_sym": SSQ_INT4_SYM, "int4_asym": SSQ_INT4_ASYM, "damp": SSQ_DAMP}
+FORMAT_BITS = {SSQ_FP32: 32, SSQ_INT8_SYM: 8, SSQ_INT8_ASYM: 8, SSQ_INT4_SYM: 4, SSQ_INT4_ASYM: 4, SSQ_DAMP: 8}
 
 
 class SsqError(RuntimeError):
@@ -50,7 +51,8 @@ class ssq_desc(ctypes.Structure):
 class ssq_layout(ctypes.Structure):
     _fields_ = [("rows", ctypes.c_size_t), ("row_bytes", ctypes.c_size_t),
                 ("codes_offset", ctypes.c_size_t), ("scale_offset", ctypes.c_size_t),
-                ("zero_offset", ctypes.c_size_t), ("total_bytes", ctypes.c_size_t)]
+                ("zero_offset", ctypes.c_size_t), ("total_bytes", ctypes.c_size_t),
+                ("hi_offset", ctypes.c_size_t)]
 
 
 def _load():
@@ -166,6 +168,8 @@ class State:
             raise ValueError("the library owns this state's memory; pass a torch storage to view it")
         L, s = self.layout, self.storage
         n = self.rows
+        if self.desc.format == SSQ_DAMP:  # the uint8 rows only; hi_region() holds the half rows
+            n = n // self.desc.rows_per_head * (self.desc.rows_per_head - SSQ_DAMP_NHI)
         if self.desc.format == SSQ_FP32:
             codes = s[: n * L.row_bytes].view(torch.float32).view(n, self.desc.row_len)
             return codes, None, None
@@ -173,6 +177,13 @@ class State:
         scale = s[L.scale_offset: L.scale_offset + 4 * n].view(torch.float32)
         zero = s[L.zero_offset: L.zero_offset + 4 * n].view(torch.float32) if L.zero_offset else None
         return codes, scale, zero
+
+    def hi_region(self):
+        """Two-tier state: the half rows [mats][16][row_len] as float16 (a view of the storage)."""
+        L, s, d = self.layout, self.storage, self.desc
+        mats = self.rows // d.rows_per_head
+        nb = mats * SSQ_DAMP_NHI * d.row_len * 2
+        return s[L.hi_offset: L.hi_offset + nb].view(torch.float16).view(mats, SSQ_DAMP_NHI, d.row_len)
 
     def free(self):
         if self.handle is not None:

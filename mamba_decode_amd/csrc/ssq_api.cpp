@@ -42,10 +42,13 @@ ssq_status ok()
     return SSQ_OK;
 }
 
-bool fmt_valid(int f) { return f >= SSQ_FP32 && f <= SSQ_INT4_ASYM; }
+bool fmt_valid(int f) { return f >= SSQ_FP32 && f <= SSQ_DAMP; }
 bool fmt_quant(int f) { return f != SSQ_FP32; }
-bool fmt_asym(int f) { return f == SSQ_INT8_ASYM || f == SSQ_INT4_ASYM; }
-int fmt_bits(int f) { return f == SSQ_FP32 ? 32 : (f == SSQ_INT8_SYM || f == SSQ_INT8_ASYM ? 8 : 4); }
+bool fmt_asym(int f) { return f == SSQ_INT8_ASYM || f == SSQ_INT4_ASYM || f == SSQ_DAMP; }
+int fmt_bits(int f)
+{
+    return f == SSQ_FP32 ? 32 : (f == SSQ_INT8_SYM || f == SSQ_INT8_ASYM || f == SSQ_DAMP ? 8 : 4);
+}
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -70,6 +73,8 @@ ssq_status check_desc(const ssq_desc* d, ssq_layout* lay)
         return fail(SSQ_ERR_UNSUPPORTED, "Mamba-2 kernels need rows_per_head to be a multiple of 16");
     if (d->kind == SSQ_DELTA && d->rows_per_head != 128)
         return fail(SSQ_ERR_UNSUPPORTED, "delta kernels are built for dk == 128");
+    if (d->format == SSQ_DAMP && d->kind != SSQ_DELTA)
+        return fail(SSQ_ERR_UNSUPPORTED, "the two-tier format is a delta-rule state");
 
     ssq_layout l;
     size_t rows;
@@ -78,8 +83,15 @@ ssq_status check_desc(const ssq_desc* d, ssq_layout* lay)
     const int bits = fmt_bits(d->format);
     l.rows = rows;
     l.row_bytes = (size_t)d->row_len * (size_t)bits / 8;
+    // the two-tier format keeps its uint8 rows in codes/scale/zero and the half rows apart
+    size_t qrows = rows, hi_bytes = 0;
+    if (d->format == SSQ_DAMP) {
+        const size_t mats = rows / (size_t)d->rows_per_head;
+        qrows = mats * (size_t)(d->rows_per_head - SSQ_DAMP_NHI);
+        hi_bytes = mats * SSQ_DAMP_NHI * (size_t)d->row_len * 2;
+    }
     size_t codes_bytes, meta_bytes;
-    if (!mul_ok(rows, l.row_bytes, &codes_bytes) || !mul_ok(rows, 4, &meta_bytes) || codes_bytes > SIZE_MAX / 2)
+    if (!mul_ok(qrows, l.row_bytes, &codes_bytes) || !mul_ok(qrows, 4, &meta_bytes) || codes_bytes > SIZE_MAX / 2)
         return fail(SSQ_ERR_INVALID_ARG, "state size overflows size_t");
     l.codes_offset = 0;
     size_t end = align256(codes_bytes);
@@ -92,6 +104,11 @@ ssq_status check_desc(const ssq_desc* d, ssq_layout* lay)
             l.zero_offset = end;
             end = align256(end + meta_bytes);
         }
+    }
+    l.hi_offset = 0;
+    if (hi_bytes) {
+        l.hi_offset = end;
+        end = align256(end + hi_bytes);
     }
     l.total_bytes = end;
     if (lay) *lay = l;
@@ -136,6 +153,16 @@ float* scale_ptr(const ssq_state* st)
 float* zero_ptr(const ssq_state* st)
 {
     return fmt_asym(st->desc.format) ? (float*)((uint8_t*)st->storage + st->lay.zero_offset) : nullptr;
+}
+uint16_t* hi_ptr(const ssq_state* st)
+{
+    return st->desc.format == SSQ_DAMP ? (uint16_t*)((uint8_t*)st->storage + st->lay.hi_offset) : nullptr;
+}
+// rows of the state that are rounded to a grid (the counter space of stochastic rounding)
+int64_t grid_rows(const ssq_state* st)
+{
+    if (st->desc.format != SSQ_DAMP) return (int64_t)st->lay.rows;
+    return (int64_t)(st->lay.rows / 128) * (128 - SSQ_DAMP_NHI);
 }
 
 #define SSQ_REQUIRE(cond, status, msg)            \
@@ -205,9 +232,11 @@ ssq_status ssq_alloc_state(const ssq_desc* desc, void* storage, const float* ini
         a.scale = scale_ptr(st);
         a.zero = zero_ptr(st);
         a.h32 = (float*)codes_ptr(st);
+        a.hi = hi_ptr(st);
         a.in = init;
         a.rows = (int64_t)lay.rows;
-        e = ssq::launch_rows(desc->format, a, false, hs);
+        e = desc->format == SSQ_DAMP ? ssq::launch_damp_rows(a, false, hs)
+                                     : ssq::launch_rows(desc->format, a, false, hs);
     } else {
         e = ssq::launch_zero_fill(st->storage, lay.total_bytes, hs);
     }
@@ -245,7 +274,7 @@ static ssq::SrArgs sr_args(const ssq_state* st)
     r.on = st->rounding == SSQ_ROUND_STOCHASTIC;
     r.seed = st->sr_seed;
     r.step = st->sr_step;
-    r.rows = (int64_t)st->lay.rows;
+    r.rows = grid_rows(st);
     return r;
 }
 
@@ -383,8 +412,15 @@ static ssq_status delta_common(ssq_state* st, const float* q, const float* k, co
     a.nmat = (int64_t)st->desc.batch * st->desc.nheads;
     a.kda = kda ? 1 : 0;
     a.sr = sr_args(st);
-    s = from_hip(ssq::launch_delta_step(st->desc.format, a, readout == SSQ_READ_PRE_QUANT, (hipStream_t)stream),
-                 kda ? "KDA step launch" : "delta step launch");
+    a.hi = hi_ptr(st);
+    if (st->desc.format == SSQ_DAMP) {
+        SSQ_REQUIRE(!kda, SSQ_ERR_UNSUPPORTED, "the two-tier state takes the scalar-decay step only");
+        s = from_hip(ssq::launch_damp_step(a, readout == SSQ_READ_PRE_QUANT, (hipStream_t)stream),
+                     "two-tier delta step launch");
+    } else {
+        s = from_hip(ssq::launch_delta_step(st->desc.format, a, readout == SSQ_READ_PRE_QUANT, (hipStream_t)stream),
+                     kda ? "KDA step launch" : "delta step launch");
+    }
     if (s == SSQ_OK) advance(st, 1);
     return s;
 }
@@ -415,6 +451,9 @@ ssq_status ssq_dequant(const ssq_state* st, float* out, void* stream)
     a.h32 = (float*)codes_ptr(st);
     a.out = out;
     a.rows = (int64_t)st->lay.rows;
+    a.hi = hi_ptr(st);
+    if (st->desc.format == SSQ_DAMP)
+        return from_hip(ssq::launch_damp_rows(a, true, (hipStream_t)stream), "dequant launch");
     return from_hip(ssq::launch_rows(st->desc.format, a, true, (hipStream_t)stream), "dequant launch");
 }
 

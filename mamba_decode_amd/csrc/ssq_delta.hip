@@ -265,3 +265,336 @@ hipError_t launch_delta_step(int fmt, DeltaArgs a, bool pre, hipStream_t st)
 }
 
 } // namespace ssq
+
+// ===========================================================================
+// two-tier delta state ("Mamba state quantization for inference", "Mixed
+// precision spends bits on persistent channels"): every key row rotated by
+// Hs = H_128/16 along the value dimension, key rows 0..15 of each matrix kept
+// as IEEE half values, rows 16..127 as asymmetric uint8 codes with a per-row
+// fp32 scale and zero point.  The step is the scalar-decay delta rule in the
+// rotated coordinates, v rotated in and o rotated out (Hs Hs = I/2).
+// ===========================================================================
+namespace ssq {
+
+constexpr int kNhi = 16, kNlo = 112;
+
+// (-1)^popcount(i & j) / 16: entry (i, j) of the Sylvester-ordered Hadamard matrix over 16
+__device__ __forceinline__ double hs(int i, int j)
+{
+    return (__builtin_popcount(i & j) & 1) ? -0.0625 : 0.0625;
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t b)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+}
+// The fp32 value rounded to the nearest half (ties to even).  The value is made opaque
+// first: the compiler would otherwise fold the fp32 rounding of the fma or double sum that
+// produced it into one rounding straight to half (v_fma_mix*), which differs from rounding
+// twice exactly when the fp32 value sits on a half midpoint.
+__device__ __forceinline__ uint32_t float_to_half_bits(float x)
+{
+    asm volatile("" : "+v"(x));
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
+// Mapping as k_delta_step: thread t owns key rows t/8 + 32k (k < 4) and 16 columns.  Row
+// k = 0 of threads 0..127 (waves 0 and 1) is a half row, every other row a uint8 row, so
+// the tier of a row is uniform across its wave.
+template <bool PRE, bool SR>
+__global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_damp_step(DeltaArgs a)
+{
+    constexpr int F = INT8_ASYM;
+    constexpr int LPR = 8, E = 16, RG = 32, KR = 4, NW = 4, ROWB = 128;
+    __shared__ double part_u[RG * 128]; // reused for the fp32 partials of the readout
+    __shared__ float u_s[128];
+    __shared__ float v_s[128];
+    __shared__ float vt_s[128];
+
+    const int t = threadIdx.x;
+    const int rg = t >> 3, part = t & 7, j0 = part * E;
+    const int64_t mat = blockIdx.x;
+    const int64_t mrow0 = mat * 128;
+    const float alpha = a.alpha[mat], beta = a.beta[mat];
+    const bool hi_wave = rg < kNhi; // row k = 0 of this thread is a half row
+
+    if (t < 128) v_s[t] = a.v[mrow0 + t];
+
+    float kk[KR], qq[KR], s_old[KR], z_old[KR];
+    uint32_t cw[KR][2 * NW]; // uint8 rows: 4 words of codes; half rows: 8 words of halves
+#pragma unroll
+    for (int r = 0; r < KR; ++r) {
+        const int i = rg + RG * r;
+        kk[r] = a.k[mrow0 + i];
+        qq[r] = a.q[mrow0 + i];
+        if (r == 0 && hi_wave) {
+            load_words<2 * NW>(a.hi + (mat * kNhi + i) * 128 + j0, cw[r]);
+            s_old[r] = 1.0f;
+            z_old[r] = 0.0f;
+        } else {
+            const int64_t lrow = mat * kNlo + (i - kNhi);
+            load_words<NW>(a.codes + lrow * ROWB + part * (NW * 4), cw[r]);
+            s_old[r] = a.scale[lrow];
+            z_old[r] = a.zero[lrow];
+        }
+    }
+    auto row_values = [&](int r, float* f) {
+        if (r == 0 && hi_wave) {
+#pragma unroll
+            for (int q = 0; q < NW * 2; ++q) {
+                f[2 * q] = half_bits_to_float(cw[r][q] & 0xFFFFu);
+                f[2 * q + 1] = half_bits_to_float(cw[r][q] >> 16);
+            }
+        } else {
+            unpack_codes<F, E>(cw[r], f);
+        }
+    };
+    __syncthreads();
+    // vt = Hs v: each of 128 threads sums its column in order, exact in double, rounded once
+    if (t < 128) {
+        double acc = 0.0;
+        for (int i = 0; i < 128; ++i) acc = __builtin_fma(hs(t, i), (double)v_s[i], acc);
+        vt_s[t] = (float)acc;
+    }
+
+    // ut = k^T St in double: half rows contribute k_i*St_ij, uint8 rows kap_i*(c_ij - z_i)
+    {
+        double up[E];
+        double zt = 0.0;
+#pragma unroll
+        for (int r = 0; r < KR; ++r) zt = __builtin_fma((double)kk[r] * (double)s_old[r], (double)z_old[r], zt);
+#pragma unroll
+        for (int e = 0; e < E; ++e) up[e] = -zt;
+#pragma unroll
+        for (int r = 0; r < KR; ++r) {
+            const double kap = (double)kk[r] * (double)s_old[r];
+            float f[E];
+            row_values(r, f);
+#pragma unroll
+            for (int e = 0; e < E; ++e) up[e] = __builtin_fma(kap, (double)f[e], up[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) part_u[rg * 128 + j0 + e] = up[e];
+    }
+    __syncthreads();
+    if (t < 128) {
+        double acc = 0.0;
+#pragma unroll 8
+        for (int r = 0; r < RG; ++r) acc += part_u[r * 128 + t];
+        u_s[t] = (float)acc;
+    }
+    __syncthreads();
+
+    // wt = beta*(vt - alpha*ut)
+    float ww[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const float au = alpha * u_s[j0 + e];
+        const float vm = vt_s[j0 + e] - au;
+        ww[e] = beta * vm;
+    }
+
+    float op[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) op[e] = 0.0f;
+#pragma unroll
+    for (int r = 0; r < KR; ++r) {
+        const int i = rg + RG * r;
+#pragma unroll
+        for (int q = 0; q < 2 * NW; ++q) asm volatile("" : "+v"(cw[r][q]));
+        float S[E];
+        row_values(r, S);
+        if (r == 0 && hi_wave) {
+            // half row: the fp32 order, then round to half
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const float kw = kk[r] * ww[e];
+                S[e] = __builtin_fmaf(alpha, S[e], kw);
+            }
+            if constexpr (PRE) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) op[e] = __builtin_fmaf(qq[r], S[e], op[e]);
+            }
+            uint32_t hw[2 * NW];
+#pragma unroll
+            for (int q = 0; q < 2 * NW; ++q) {
+                const uint32_t lo = float_to_half_bits(S[2 * q]), hi = float_to_half_bits(S[2 * q + 1]);
+                hw[q] = lo | (hi << 16);
+                S[2 * q] = half_bits_to_float(lo);
+                S[2 * q + 1] = half_bits_to_float(hi);
+            }
+            store_words<2 * NW>(a.hi + (mat * kNhi + i) * 128 + j0, hw);
+            if constexpr (!PRE) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) op[e] = __builtin_fmaf(qq[r], S[e], op[e]);
+            }
+        } else {
+            const int64_t lrow = mat * kNlo + (i - kNhi);
+            const float as = alpha * s_old[r];
+            const float az = as * z_old[r];
+#pragma unroll
+            for (int e = 0; e < E; ++e) S[e] = __builtin_fmaf(as, S[e], __builtin_fmaf(kk[r], ww[e], -az));
+            if constexpr (PRE) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) op[e] = __builtin_fmaf(qq[r], S[e], op[e]);
+            }
+            float mn = S[0], mx = S[0];
+#pragma unroll
+            for (int e = 1; e < E; ++e) {
+                mn = fminf(mn, S[e]);
+                mx = fmaxf(mx, S[e]);
+            }
+            mn = group_min<LPR>(mn);
+            mx = group_max<LPR>(mx);
+            RowGrid g;
+            float f[E];
+            const uint64_t ctr0 = SR ? ((a.sr.step * (uint64_t)a.sr.rows + (uint64_t)lrow) * 128u + (uint64_t)j0) : 0;
+            if (__all(refit_fast<F>(mn, mx, 0.0f, g))) {
+                if constexpr (SR) {
+                    round_codes_sr<F, E>(S, g, a.sr.seed, ctr0, f);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) f[e] = __builtin_fmaf(S[e], g.inv, g.Mz);
+                }
+            } else {
+                g = refit<F>(mn, mx, 0.0f);
+                if constexpr (SR) {
+                    round_codes_sr<F, E>(S, g, a.sr.seed, ctr0, f);
+                } else {
+                    const bool slow_any = __any(g.slow);
+                    round_codes<F, E>(S, g, slow_any, f);
+                }
+            }
+            uint32_t ow[NW];
+            pack_codes<F, E>(f, ow);
+            store_words<NW>(a.codes + lrow * ROWB + part * (NW * 4), ow);
+            if (part == 0) {
+                a.scale[lrow] = g.s;
+                a.zero[lrow] = g.z;
+            }
+            if constexpr (!PRE) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float r_ij = g.s * ((f[e] - kMagic) - g.z); // the stored value, fl(s*fl(c - z))
+                    op[e] = __builtin_fmaf(qq[r], r_ij, op[e]);
+                }
+            }
+        }
+    }
+
+    // ot = St'^T q meets in LDS; o = 2 Hs ot
+    float* part_o = reinterpret_cast<float*>(part_u);
+#pragma unroll
+    for (int e = 0; e < E; ++e) part_o[rg * 128 + j0 + e] = op[e];
+    __syncthreads();
+    if (t < 128) {
+        float acc = 0.0f;
+#pragma unroll 8
+        for (int r = 0; r < RG; ++r) acc += part_o[r * 128 + t];
+        u_s[t] = acc; // ot
+    }
+    __syncthreads();
+    if (t < 128) {
+        double acc = 0.0;
+        for (int i = 0; i < 128; ++i) acc = __builtin_fma(hs(t, i), (double)u_s[i], acc);
+        a.o[mrow0 + t] = (float)(2.0 * acc);
+    }
+}
+
+// Rows of a two-tier state, 8 lanes per key row (16 columns each).  init: rotate the fp32
+// row (each output a sum over the input row in order, in double, rounded once), then round
+// the half rows to half and refit and round the uint8 rows; dequant: S = 2 St Hs.
+template <bool DEQ>
+__global__ __launch_bounds__(256) void k_damp_rows(QArgs a)
+{
+    constexpr int F = INT8_ASYM;
+    constexpr int LPR = 8, E = 16, NW = 4, ROWB = 128;
+    const int lane = threadIdx.x & 63, sub = lane >> 3, part = lane & 7, j0 = part * E;
+    const int64_t row = ((int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)) * 8 + sub;
+    const bool live = row < a.rows; // rows come in whole matrices of 128, so a wave is all live or not
+    if (!__any(live)) return;
+    const int64_t mat = row / 128;
+    const int i = (int)(row % 128);
+    const bool hi_row = i < kNhi;
+    const int64_t lrow = mat * kNlo + (i - kNhi);
+    if constexpr (!DEQ) {
+        const float* src = a.in + row * 128;
+        float rv[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            double acc = 0.0;
+            for (int c = 0; c < 128; ++c) acc = __builtin_fma((double)src[c], hs(c, j0 + e), acc);
+            rv[e] = (float)acc;
+        }
+        if (hi_row) {
+            uint32_t hw[2 * NW];
+#pragma unroll
+            for (int q = 0; q < 2 * NW; ++q)
+                hw[q] = float_to_half_bits(rv[2 * q]) | (float_to_half_bits(rv[2 * q + 1]) << 16);
+            store_words<2 * NW>(a.hi + (mat * kNhi + i) * 128 + j0, hw);
+        } else {
+            float mn = rv[0], mx = rv[0];
+#pragma unroll
+            for (int e = 1; e < E; ++e) {
+                mn = fminf(mn, rv[e]);
+                mx = fmaxf(mx, rv[e]);
+            }
+            // a row's 8 lanes are all half rows or all uint8 rows; reduce within them
+            mn = group_min<LPR>(mn);
+            mx = group_max<LPR>(mx);
+            const RowGrid g = refit<F>(mn, mx, 0.0f);
+            float f[E];
+            round_codes<F, E>(rv, g, g.slow, f);
+            uint32_t ow[NW];
+            pack_codes<F, E>(f, ow);
+            store_words<NW>(a.codes + lrow * ROWB + part * (NW * 4), ow);
+            if (part == 0) {
+                a.scale[lrow] = g.s;
+                a.zero[lrow] = g.z;
+            }
+        }
+    } else {
+        // every lane reconstructs the whole stored row, then forms its 16 outputs
+        float r128[128];
+        if (hi_row) {
+            const uint16_t* hp = a.hi + (mat * kNhi + i) * 128;
+            for (int c = 0; c < 128; ++c) r128[c] = half_bits_to_float(hp[c]);
+        } else {
+            const uint8_t* cp = a.codes + lrow * ROWB;
+            const float s = a.scale[lrow], z = a.zero[lrow];
+            for (int c = 0; c < 128; ++c) r128[c] = s * ((float)cp[c] - z);
+        }
+        float out[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            double acc = 0.0;
+            for (int c = 0; c < 128; ++c) acc = __builtin_fma((double)r128[c], hs(c, j0 + e), acc);
+            out[e] = (float)(2.0 * acc);
+        }
+        store_f32<E>(a.out + row * 128 + j0, out);
+    }
+}
+
+hipError_t launch_damp_step(DeltaArgs a, bool pre, hipStream_t st)
+{
+    const unsigned blocks = (unsigned)a.nmat;
+    if (a.sr.on) {
+        if (pre) hipLaunchKernelGGL((k_damp_step<true, true>), dim3(blocks), dim3(256), 0, st, a);
+        else hipLaunchKernelGGL((k_damp_step<false, true>), dim3(blocks), dim3(256), 0, st, a);
+    } else {
+        if (pre) hipLaunchKernelGGL((k_damp_step<true, false>), dim3(blocks), dim3(256), 0, st, a);
+        else hipLaunchKernelGGL((k_damp_step<false, false>), dim3(blocks), dim3(256), 0, st, a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_damp_rows(QArgs a, bool dequant, hipStream_t st)
+{
+    const int64_t waves = (a.rows + 7) / 8;
+    const unsigned blocks = (unsigned)((waves + 3) / 4);
+    if (dequant) hipLaunchKernelGGL((k_damp_rows<true>), dim3(blocks), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((k_damp_rows<false>), dim3(blocks), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+} // namespace ssq

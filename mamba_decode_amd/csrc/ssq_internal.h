@@ -41,6 +41,7 @@ struct QArgs {
     float* scale;
     float* zero;
     float* h32;
+    uint16_t* hi;    // two-tier delta state: the half rows
     const float* in; // quantize: source rows [rows][128]
     float* out;      // dequantize: destination rows [rows][128]
     int64_t rows;
@@ -61,6 +62,7 @@ struct DeltaArgs {
     int64_t nmat;
     int kda;
     SrArgs sr;
+    uint16_t* hi; // two-tier state: [nmat][16][128] half rows (codes/scale/zero: the uint8 rows)
 };
 
 hipError_t launch_m2_step(int fmt, M2Args a, bool pre, int num_cus, hipStream_t st);
@@ -69,5 +71,7 @@ hipError_t launch_m2_prefill(int fmt, M2Args a, int chunk, bool pre, hipStream_t
 hipError_t launch_rows(int fmt, QArgs a, bool dequant, hipStream_t st);
 hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t st);
 hipError_t launch_delta_step(int fmt, DeltaArgs a, bool pre, hipStream_t st);
+hipError_t launch_damp_step(DeltaArgs a, bool pre, hipStream_t st);
+hipError_t launch_damp_rows(QArgs a, bool dequant, hipStream_t st);
 
 } // namespace ssq

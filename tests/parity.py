@@ -117,3 +117,22 @@ def check_codes(gpu: dict, orc_code, orc_scale, orc_zero, orc_v, fmt: str, where
 
 def dev(a) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
+
+
+# ---------------------------------------------------------------------------
+# two-tier delta state
+# ---------------------------------------------------------------------------
+def write_gpu_damp(gst, ost: "oracle.DampState"):
+    codes, scale, zero = gst.regions()
+    codes.copy_(torch.from_numpy(pack_codes(ost.code, "int8_asym")))
+    scale.copy_(torch.from_numpy(ost.scale))
+    zero.copy_(torch.from_numpy(ost.zero))
+    gst.hi_region().copy_(torch.from_numpy(ost.hi.astype(np.float16)))
+    torch.cuda.synchronize()
+
+
+def read_gpu_damp(gst) -> dict:
+    torch.cuda.synchronize()
+    codes, scale, zero = gst.regions()
+    return {"code": unpack_codes(codes.cpu().numpy(), "int8_asym"), "scale": scale.cpu().numpy().copy(),
+            "zero": zero.cpu().numpy().copy(), "hi": gst.hi_region().cpu().numpy().astype(np.float32)}

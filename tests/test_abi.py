@@ -140,3 +140,24 @@ def test_status_strings():
     for s in range(6):
         assert ssq.ssq_status_string(s).startswith("SSQ_")
     assert "unknown" in ssq.ssq_status_string(42)
+
+
+def test_two_tier_layout():
+    """SSQ_DAMP: uint8 rows (codes, scale, zero) for key rows 16..127 of each matrix, half rows
+    for 0..15, 9.44 bits per value; a delta-rule format only."""
+    d = ssq.make_desc(ssq.SSQ_DELTA, "damp", 3, 5, 128, 128)
+    lay = ssq.ssq_state_layout(d)
+    mats = 15
+    lo = mats * 112
+    assert lay.rows == mats * 128 and lay.row_bytes == 128
+    assert lay.scale_offset >= lo * 128 and lay.zero_offset >= lay.scale_offset + 4 * lo
+    assert lay.hi_offset >= lay.zero_offset + 4 * lo
+    assert lay.total_bytes >= lay.hi_offset + mats * 16 * 128 * 2
+    for off in (lay.scale_offset, lay.zero_offset, lay.hi_offset, lay.total_bytes):
+        assert off % 256 == 0
+    payload = lo * (128 + 8) + mats * 16 * 256
+    assert lay.total_bytes - payload < 4 * 256
+    assert payload * 8 / (mats * 128 * 128) == pytest.approx(9.4375)
+    bad = ssq.make_desc(ssq.SSQ_MAMBA2, "damp", 1, 2, 64)
+    h = ctypes.c_void_p()
+    assert ssq.lib.ssq_alloc_state(ctypes.byref(bad), None, None, None, ctypes.byref(h)) == ssq.SSQ_ERR_UNSUPPORTED
