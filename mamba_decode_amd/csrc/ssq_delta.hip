@@ -29,6 +29,12 @@ namespace ssq {
 #define SSQ_DELTA_WAVES 4
 #endif
 
+// Partial rows in LDS: element j of row group r sits at r*kPartPitch + j + j/16.  A wave
+// writes 8 row groups x 8 segments of 16 columns at once; without the padding every lane
+// of it lands on the same bank.
+constexpr int kPartPitch = 136;
+__device__ __forceinline__ int part_idx(int r, int j) { return r * kPartPitch + j + (j >> 4); }
+
 // KDA: a decay per key channel (alpha [matrices][128]), S' = (I - beta k k^T) Diag(alpha) S
 // + beta k v^T, evaluated as u = k^T Diag(alpha) S, w = beta*(v - u), S' = alpha_i*S + k w^T
 template <int F, bool PRE, bool SR, bool KDA>
@@ -39,7 +45,7 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_delta_step(DeltaArgs a
     constexpr int NW = Tr::quant ? E * Tr::bits / 32 : E;
     constexpr int NS = NW; // registers per row part (packed codes, or fp32 values)
     constexpr int ROWB = Tr::quant ? 128 * Tr::bits / 8 : 512;
-    __shared__ double part_u[RG * 128]; // reused for the fp32 partials of o
+    __shared__ double part_u[RG * kPartPitch]; // reused for the fp32 partials of o
     __shared__ float u_s[128];
 
     const int t = threadIdx.x;
@@ -107,13 +113,13 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_delta_step(DeltaArgs a
             for (int e = 0; e < E; ++e) up[e] = __builtin_fma(kap, (double)f[e], up[e]);
         }
 #pragma unroll
-        for (int e = 0; e < E; ++e) part_u[rg * 128 + j0 + e] = up[e];
+        for (int e = 0; e < E; ++e) part_u[part_idx(rg, j0 + e)] = up[e];
     }
     __syncthreads();
     if (t < 128) {
         double acc = 0.0;
 #pragma unroll 8
-        for (int r = 0; r < RG; ++r) acc += part_u[r * 128 + t];
+        for (int r = 0; r < RG; ++r) acc += part_u[part_idx(r, t)];
         u_s[t] = (float)acc;
     }
     __syncthreads();
@@ -216,12 +222,12 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_delta_step(DeltaArgs a
     // o = S'^T q: 32 partial rows meet in LDS
     float* part_o = reinterpret_cast<float*>(part_u);
 #pragma unroll
-    for (int e = 0; e < E; ++e) part_o[rg * 128 + j0 + e] = op[e];
+    for (int e = 0; e < E; ++e) part_o[part_idx(rg, j0 + e)] = op[e];
     __syncthreads();
     if (t < 128) {
         float acc = 0.0f;
 #pragma unroll 8
-        for (int r = 0; r < RG; ++r) acc += part_o[r * 128 + t];
+        for (int r = 0; r < RG; ++r) acc += part_o[part_idx(r, t)];
         a.o[mrow0 + t] = acc;
     }
 }
@@ -298,6 +304,28 @@ __device__ __forceinline__ uint32_t float_to_half_bits(float x)
     return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
 }
 
+// H_128 x (Sylvester order, unscaled) of the 128 values x held one per thread by threads
+// 0..127, in double: butterflies over lane distances 1..32, the last level through LDS.
+// Each output is a sum of the 128 inputs with signs; it is exact (so equal to any other
+// summation order) while the inputs span less than 2^29 in magnitude.  Holds a barrier:
+// every thread of the block calls it; threads 128..255 return their x unchanged.
+__device__ __forceinline__ double wht128(double x, double* xch)
+{
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int h = 1; h < 64; h <<= 1) {
+        const double p = __shfl_xor(x, h);
+        x = (t & h) ? p - x : x + p;
+    }
+    if (t < 128) xch[t] = x;
+    __syncthreads();
+    if (t < 128) {
+        const double p = xch[t ^ 64];
+        x = (t & 64) ? p - x : x + p;
+    }
+    return x;
+}
+
 // Mapping as k_delta_step: thread t owns key rows t/8 + 32k (k < 4) and 16 columns.  Row
 // k = 0 of threads 0..127 (waves 0 and 1) is a half row, every other row a uint8 row, so
 // the tier of a row is uniform across its wave.
@@ -306,10 +334,10 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_damp_step(DeltaArgs a)
 {
     constexpr int F = INT8_ASYM;
     constexpr int LPR = 8, E = 16, RG = 32, KR = 4, NW = 4, ROWB = 128;
-    __shared__ double part_u[RG * 128]; // reused for the fp32 partials of the readout
+    __shared__ double part_u[RG * kPartPitch]; // reused for the fp32 partials of the readout
     __shared__ float u_s[128];
-    __shared__ float v_s[128];
     __shared__ float vt_s[128];
+    __shared__ double xch[128];
 
     const int t = threadIdx.x;
     const int rg = t >> 3, part = t & 7, j0 = part * E;
@@ -318,7 +346,7 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_damp_step(DeltaArgs a)
     const float alpha = a.alpha[mat], beta = a.beta[mat];
     const bool hi_wave = rg < kNhi; // row k = 0 of this thread is a half row
 
-    if (t < 128) v_s[t] = a.v[mrow0 + t];
+    const double vj = t < 128 ? (double)a.v[mrow0 + t] : 0.0;
 
     float kk[KR], qq[KR], s_old[KR], z_old[KR];
     uint32_t cw[KR][2 * NW]; // uint8 rows: 4 words of codes; half rows: 8 words of halves
@@ -349,12 +377,10 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_damp_step(DeltaArgs a)
             unpack_codes<F, E>(cw[r], f);
         }
     };
-    __syncthreads();
-    // vt = Hs v: each of 128 threads sums its column in order, exact in double, rounded once
-    if (t < 128) {
-        double acc = 0.0;
-        for (int i = 0; i < 128; ++i) acc = __builtin_fma(hs(t, i), (double)v_s[i], acc);
-        vt_s[t] = (float)acc;
+    // vt = Hs v, rounded once
+    {
+        const double x = wht128(vj, xch);
+        if (t < 128) vt_s[t] = (float)(x * 0.0625);
     }
 
     // ut = k^T St in double: half rows contribute k_i*St_ij, uint8 rows kap_i*(c_ij - z_i)
@@ -374,13 +400,13 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_damp_step(DeltaArgs a)
             for (int e = 0; e < E; ++e) up[e] = __builtin_fma(kap, (double)f[e], up[e]);
         }
 #pragma unroll
-        for (int e = 0; e < E; ++e) part_u[rg * 128 + j0 + e] = up[e];
+        for (int e = 0; e < E; ++e) part_u[part_idx(rg, j0 + e)] = up[e];
     }
     __syncthreads();
     if (t < 128) {
         double acc = 0.0;
 #pragma unroll 8
-        for (int r = 0; r < RG; ++r) acc += part_u[r * 128 + t];
+        for (int r = 0; r < RG; ++r) acc += part_u[part_idx(r, t)];
         u_s[t] = (float)acc;
     }
     __syncthreads();
@@ -485,20 +511,15 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_damp_step(DeltaArgs a)
     // ot = St'^T q meets in LDS; o = 2 Hs ot
     float* part_o = reinterpret_cast<float*>(part_u);
 #pragma unroll
-    for (int e = 0; e < E; ++e) part_o[rg * 128 + j0 + e] = op[e];
+    for (int e = 0; e < E; ++e) part_o[part_idx(rg, j0 + e)] = op[e];
     __syncthreads();
+    float ot = 0.0f;
     if (t < 128) {
-        float acc = 0.0f;
 #pragma unroll 8
-        for (int r = 0; r < RG; ++r) acc += part_o[r * 128 + t];
-        u_s[t] = acc; // ot
+        for (int r = 0; r < RG; ++r) ot += part_o[part_idx(r, t)];
     }
-    __syncthreads();
-    if (t < 128) {
-        double acc = 0.0;
-        for (int i = 0; i < 128; ++i) acc = __builtin_fma(hs(t, i), (double)u_s[i], acc);
-        a.o[mrow0 + t] = (float)(2.0 * acc);
-    }
+    const double x = wht128((double)ot, xch);
+    if (t < 128) a.o[mrow0 + t] = (float)(x * 0.125);
 }
 
 // Rows of a two-tier state, 8 lanes per key row (16 columns each).  init: rotate the fp32
