@@ -225,9 +225,14 @@ def sr_row_uniforms(seed: int, step: int, rows: int, r: int, n_len: int) -> np.n
 
 
 def quantize_row_sr(h: np.ndarray, fmt: str, U: np.ndarray | None):
-    """One row refit and rounded; stochastically with uniforms ``U`` (same length), or to
-    nearest when ``U`` is None.  Returns (code, scale, zero)."""
+    """One row refit and rounded; stochastically with uniforms ``U`` (same length, each a
+    multiple of 2^-16 in [0, 1)), or to nearest when ``U`` is None.  Returns (code, scale,
+    zero)."""
     h = _c32(h)
+    if U is not None:
+        K = _c32(U).astype(np.float64) * 65536.0
+        if not (np.all(K == np.floor(K)) and np.all(K >= 0) and np.all(K < 65536)):
+            raise ValueError("stochastic rounding takes uniforms that are multiples of 2^-16 in [0, 1)")
     n = h.shape[0]
     bits, asym = FORMATS[fmt]
     code = np.empty(n, np.int32)

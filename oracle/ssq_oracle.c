@@ -111,15 +111,18 @@ static double rne_sum(double p, double z)
 
 /* Stochastic rounding ("ssm-state-quantization" README, Findings 9: the state
  * rounded stochastically instead of to nearest).  The code is floor(v + U)
- * for the exact real v = h*inv + z and a uniform U in [0, 1): it rounds up
- * with probability equal to the fractional part of v.  floor(p) and p - floor(p)
- * are exact in double, and so is 1 - U (U has 24 bits), so the decision
- * frac >= 1 - U is exact. */
+ * for the exact real v = p + z (p = h*inv, z an integer) and a uniform U in
+ * [0, 1) that is a multiple of 2^-16, U = K/2^16: it rounds up with the
+ * probability that the fraction of v, taken down to a multiple of 2^-16, reaches
+ * 1 - U.  floor(p + U) = floor(p) + [t + K >= 2^16] with t = floor(2^16 frac(p))
+ * = floor(2^16 p) - 2^16 floor(p): both terms are exact integers in double and
+ * so is their difference (it lies in [0, 2^16)), for every p. */
 static double sr_sum(double p, double z, float u)
 {
+    double K = (double)u * 65536.0;
     double f = floor(p);
-    double r = p - f;
-    return f + z + (r >= 1.0 - (double)u ? 1.0 : 0.0);
+    double t = floor(p * 65536.0) - f * 65536.0;
+    return f + z + (t + K >= 65536.0 ? 1.0 : 0.0);
 }
 
 /* SplitMix64 (Steele, Lea and Flood, "Fast splittable pseudorandom number
@@ -134,12 +137,16 @@ uint64_t orc_splitmix64(uint64_t seed, uint64_t i)
     return x ^ (x >> 31);
 }
 
-/* The uniform that entry n of state row r draws at token `step`: the top 24
- * bits of output number ctr + 1, ctr = (step*rows + r)*N + n, scaled by 2^-24. */
+/* The uniform that entry n of state row r draws at token `step`, for the flat
+ * counter ctr = (step*rows + r)*N + n: every output of the generator gives four
+ * 16-bit uniforms, counter ctr taking bits 16k .. 16k+15 (k = ctr mod 4) of
+ * output number floor(ctr/4) + 1, scaled by 2^-16. */
 float orc_sr_uniform(uint64_t seed, uint64_t step, int64_t rows, int64_t r, int N, int n)
 {
     uint64_t ctr = (step * (uint64_t)rows + (uint64_t)r) * (uint64_t)N + (uint64_t)n;
-    return (float)(orc_splitmix64(seed, ctr + 1) >> 40) * (1.0f / 16777216.0f);
+    uint64_t out = orc_splitmix64(seed, ctr / 4 + 1);
+    uint32_t K = (uint32_t)(out >> (16 * (ctr % 4))) & 0xFFFFu;
+    return (float)K * (1.0f / 65536.0f);
 }
 
 /* the N uniforms of state row r at token `step` */

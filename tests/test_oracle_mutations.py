@@ -60,15 +60,21 @@ MUTATIONS = [
      "double kd = avec ? (double)k[i] * (double)avec[i] : (double)k[i];",
      "double kd = avec ? (double)k[i] * (double)avec[i] : (double)k[j % dk];"),
     ("dequantization scale dropped", "        out[i] = s * d;", "        out[i] = d;"),
-    ("stochastic rounding compares with U, not 1 - U",
-     "return f + z + (r >= 1.0 - (double)u ? 1.0 : 0.0);", "return f + z + (r > (double)u ? 1.0 : 0.0);"),
+    ("stochastic rounding rounds up below the threshold",
+     "return f + z + (t + K >= 65536.0 ? 1.0 : 0.0);", "return f + z + (t + K > 65536.0 ? 1.0 : 0.0);"),
     ("stochastic rounding drops the zero point",
-     "return f + z + (r >= 1.0 - (double)u ? 1.0 : 0.0);", "return f + (r >= 1.0 - (double)u ? 1.0 : 0.0);"),
+     "return f + z + (t + K >= 65536.0 ? 1.0 : 0.0);", "return f + (t + K >= 65536.0 ? 1.0 : 0.0);"),
+    ("stochastic rounding compares U with the fraction, not 1 - U",
+     "return f + z + (t + K >= 65536.0 ? 1.0 : 0.0);", "return f + z + (K > t ? 1.0 : 0.0);"),
+    ("stochastic rounding takes the fraction from the rounded sum",
+     "double t = floor(p * 65536.0) - f * 65536.0;", "double t = floor((p - f) * 65536.0);"),
     ("uniform counter ignores the token",
      "uint64_t ctr = (step * (uint64_t)rows + (uint64_t)r) * (uint64_t)N + (uint64_t)n;",
      "uint64_t ctr = ((uint64_t)r) * (uint64_t)N + (uint64_t)n;"),
-    ("uniform keeps 24 low bits", "return (float)(orc_splitmix64(seed, ctr + 1) >> 40) * (1.0f / 16777216.0f);",
-     "return (float)(orc_splitmix64(seed, ctr + 1) & 0xFFFFFF) * (1.0f / 16777216.0f);"),
+    ("uniform pieces taken high first", "uint32_t K = (uint32_t)(out >> (16 * (ctr % 4))) & 0xFFFFu;",
+     "uint32_t K = (uint32_t)(out >> (16 * (3 - ctr % 4))) & 0xFFFFu;"),
+    ("one output per uniform", "uint64_t out = orc_splitmix64(seed, ctr / 4 + 1);",
+     "uint64_t out = orc_splitmix64(seed, ctr + 1);"),
     ("scan reuses the first token's uniforms", "ys, readout_pre, NULL, NULL, sr, seed, step + (uint64_t)t);",
      "ys, readout_pre, NULL, NULL, sr, seed, step);"),
     ("delta draws the uniforms of the matrix's first row",

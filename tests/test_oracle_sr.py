@@ -5,17 +5,20 @@ the "ssm-state-quantization" README tests in Findings 9.  The pages name it
 only, so the plain textbook definition is used: the code is floor(v + U) for
 the exact real v = h*inv + z and a uniform U in [0, 1), i.e. the row rounds up
 with probability equal to the fractional part of v; the grid (scale and zero
-point) is the one round-to-nearest refits.  The uniforms are the top 24 bits
-of SplitMix64 (Steele, Lea and Flood, OOPSLA 2014) output number ctr + 1 for
-the state's seed, ctr = (step*rows + row)*N + n.
+point) is the one round-to-nearest refits.  U is a 16-bit uniform, a multiple of
+2^-16: counter ctr = (step*rows + row)*N + n takes bits 16k .. 16k+15 (k = ctr
+mod 4) of SplitMix64 (Steele, Lea and Flood, OOPSLA 2014) output number
+ctr/4 + 1 for the state's seed, four uniforms per output.
 
-The pins: the generator's published output sequence; the uniforms'
-distribution; hand-worked rows; every code brackets its exact value; the mean
-code is the exact value (unbiasedness); values on the grid are kept; and the
-decode step, scan and delta step draw the uniforms of the rows and tokens they
-update.
+The pins: the generator's published output sequence and how its outputs split
+into uniforms; the uniforms' distribution; hand-worked rows; every code is
+floor(v + U) computed in exact rational arithmetic, down to values a hair below
+zero; the mean code over many draws is the exact value up to the 2^-16 grid of U
+(unbiasedness); values on the grid are kept; and the decode step, scan and delta
+step draw the uniforms of the rows and tokens they update.
 """
 import math
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -33,17 +36,19 @@ def test_splitmix64_published_sequence():
     assert oracle.splitmix64(0, 1) == 0xE220A8397B1DCDAF
     assert oracle.splitmix64(0, 2) == 0x6E789E6AA1B965F4
     assert oracle.splitmix64(0, 3) == 0x06C45D188009454F
-    # the uniform of counter 0 is the top 24 bits of output number 1, and so on
-    for ctr, out in enumerate([0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F]):
-        assert oracle.sr_uniform(0, 0, 1, 0, 3, ctr) == (out >> 40) / 2.0 ** 24
+    # counters 0..3 take the four 16-bit pieces of output number 1, low piece first;
+    # counters 4..7 those of output number 2, and so on
+    pieces = [0xCDAF, 0x7B1D, 0xA839, 0xE220, 0x65F4, 0xA1B9, 0x9E6A, 0x6E78, 0x454F, 0x8009, 0x5D18, 0x06C4]
+    for ctr, piece in enumerate(pieces):
+        assert oracle.sr_uniform(0, 0, 1, 0, 12, ctr) == piece / 2.0 ** 16
 
 
-def test_uniforms_are_24_bit_and_uniform():
+def test_uniforms_are_16_bit_and_uniform():
     n = 1 << 16
     u = oracle.sr_row_uniforms(7, 3, 1000, 11, n).astype(F64)
     assert u[12345] == oracle.sr_uniform(7, 3, 1000, 11, n, 12345)
     assert np.all(u >= 0.0) and np.all(u < 1.0)
-    assert np.array_equal(u * 2.0 ** 24, np.floor(u * 2.0 ** 24))  # 24-bit fractions
+    assert np.array_equal(u * 2.0 ** 16, np.floor(u * 2.0 ** 16))  # 16-bit fractions
     assert abs(u.mean() - 0.5) < 5 * math.sqrt(1 / 12 / n)
     counts = np.bincount((u * 16).astype(int), minlength=16)
     chi2 = ((counts - n / 16) ** 2 / (n / 16)).sum()
@@ -60,21 +65,35 @@ def test_uniforms_follow_the_flat_counter():
     assert oracle.sr_uniform(1, 0, rows, 0, N, 0) != oracle.sr_uniform(2, 0, rows, 0, N, 0)
 
 
+def _grid16(u):
+    return np.round(np.asarray(u, F64) * 65536) / 65536
+
+
 def test_hand_worked_rows():
     # asymmetric 2-bit grid over [0, 3]: s = 1, z = 0, so v = h
     h = np.array([0.0, 3.0, 1.25, 1.25, 2.5, 2.5], np.float32)
-    U = np.array([0.9, 0.9, 0.74, 0.76, 0.49, 0.51], np.float32)
+    U = _grid16([0.9, 0.9, 0.74, 0.76, 0.49, 0.51])
     code2, s2, z2 = _q(h, 2, 1, U)
     assert (s2, z2) == (1.0, 0.0)
     # floor(v + U): 0.9 -> 0, 3.9 -> 3, 1.99 -> 1, 2.01 -> 2, 2.99 -> 2, 3.01 -> 3
     assert code2.tolist() == [0, 3, 1, 2, 2, 3]
     # symmetric 2-bit grid: amax 2, step 2, v = h/2 in [-1, 1]
     h = np.array([-2.0, 2.0, -1.0, -1.0, 0.5, 0.5], np.float32)
-    U = np.array([0.3, 0.3, 0.49, 0.51, 0.74, 0.76], np.float32)
+    U = _grid16([0.3, 0.3, 0.49, 0.51, 0.74, 0.76])
     code3, s3, z3 = _q(h, 2, 0, U)
     assert (s3, z3) == (2.0, 0.0)
     # v = -1, 1, -0.5, -0.5, 0.25, 0.25 -> floor(v + U)
     assert code3.tolist() == [-1, 1, -1, 0, 0, 1]
+    # symmetric 8-bit grid with amax 127: s = 1, v = h.  A value a hair below zero
+    # rounds down to -1 only when U = 0; a hair below 3 reaches 3 once U >= 2^-16
+    h = np.array([127.0, -1e-30, -1e-30, -1e-30, np.nextafter(np.float32(3), np.float32(0)),
+                  np.nextafter(np.float32(3), np.float32(0)), -127.0], np.float32)
+    U = np.array([0.0, 0.0, 2.0 ** -16, 1 - 2.0 ** -16, 0.0, 2.0 ** -16, 0.0])
+    code8, s8, z8 = _q(h, 8, 0, U)
+    assert (s8, z8) == (1.0, 0.0)
+    assert code8.tolist() == [127, -1, 0, 0, 2, 3, -127]
+    with pytest.raises(ValueError):
+        oracle.quantize_row_sr(np.ones(4, np.float32), "int8_sym", np.full(4, 0.3))  # off the 2^-16 grid
 
 
 def _q(h, bits, asym, U):
@@ -91,7 +110,16 @@ def _q(h, bits, asym, U):
 def _rows():
     h = synth.init_state(21, 1, 24, 128)
     r = synth.normal(21, 98, 0, np.arange(4 * 128)).reshape(4, 128)
-    return np.concatenate([h, 10.0 + 1e-2 * r, -3.0 + 1e-3 * r]).astype(np.float32)
+    tiny = 1e-12 * r[:1]  # values a hair either side of zero
+    # the last row's offset is huge against its spread: |z| ~ 2^29
+    return np.concatenate([h, 10.0 + 1e-2 * r, -3.0 + 1e-3 * r, tiny, 1000.0 + 1e-4 * r[:1]]).astype(np.float32)
+
+
+def _floor_exact(h, inv, z, U):
+    """floor(h*inv + z + U) per entry, in exact rational arithmetic."""
+    fi = Fraction(float(inv))
+    return np.array([math.floor(Fraction(float(a)) * fi + int(z) + Fraction(float(u))) for a, u in zip(h, U)],
+                    np.int64)
 
 
 @pytest.mark.parametrize("fmt", QUANT)
@@ -103,19 +131,16 @@ def test_codes_bracket_the_exact_value_and_keep_the_grid(fmt):
         c_rtn, s_rtn, z_rtn = oracle.quantize_row_sr(h, fmt, None)
         c, s, z = oracle.quantize_row_sr(h, fmt, U)
         assert (s, z) == (s_rtn, z_rtn)          # the grid does not depend on the rounding
+        assert s >= np.finfo(np.float32).tiny  # no degenerate row here
         inv = np.float32(1.0) / np.float32(s)
-        v = h.astype(F64) * F64(inv) + F64(z)     # exact: float products fit in double
-        fl = np.floor(v)
-        ok = (c == np.clip(fl, lo, hi)) | (c == np.clip(fl + 1, lo, hi))
-        assert ok.all(), (fmt, i)
-        # up exactly when frac(v) >= 1 - U
-        up = (v - fl) >= 1.0 - U.astype(F64)
-        assert np.array_equal(c, np.clip(fl + up, lo, hi).astype(np.int32))
+        ref = np.clip(_floor_exact(h, inv, z, U), lo, hi)
+        assert np.array_equal(c, ref), (fmt, i)
 
 
 @pytest.mark.parametrize("fmt", QUANT)
 def test_stochastic_rounding_is_unbiased(fmt):
-    # one row drawn 4096 times with fresh uniforms: the mean code is the exact value
+    # one row drawn 4096 times with fresh uniforms: entry v rounds up with probability
+    # floor(2^16 frac(v))/2^16, within 2^-16 of frac(v); the mean code follows it
     h = synth.init_state(23, 1, 1, 128)[0].astype(np.float32)
     c0, s, z = oracle.quantize_row_sr(h, fmt, None)
     inv = np.float32(1.0) / np.float32(s)
@@ -130,8 +155,10 @@ def test_stochastic_rounding_is_unbiased(fmt):
         total += oracle.quantize_row_sr(h, fmt, U)[0]
     mean = total / draws
     frac = v - np.floor(v)
-    sd = np.sqrt(np.maximum(frac * (1 - frac), 1e-12) / draws)
-    assert np.all(np.abs(mean - v)[inside] <= 5 * sd[inside] + 1e-12)
+    p_up = np.floor(frac * 65536) / 65536
+    assert np.all(np.abs(np.floor(v) + p_up - v) < 2.0 ** -16)
+    sd = np.sqrt(p_up * (1 - p_up) / draws)
+    assert np.all(np.abs(mean - (np.floor(v) + p_up))[inside] <= 5 * sd[inside] + 1e-12)
 
 
 @pytest.mark.parametrize("fmt", QUANT)
