@@ -184,10 +184,12 @@ ssq_status ssq_state_info(const ssq_state *state, ssq_desc *desc, void **storage
  * SSQ_ROUND_STOCHASTIC keeps the same grid (scale, zero point) and sets each
  * code to floor(v + U) for the exact real v = h'*inv + z', clamped to the
  * code range, so a row rounds up with probability equal to the fractional
- * part of v.  Entry n of state row r at token t draws U = (top 24 bits of
- * SplitMix64 output number ctr + 1 for `seed`) * 2^-24 with
- * ctr = (t*rows + r)*row_len + n (Steele, Lea and Flood, "Fast splittable
- * pseudorandom number generators", OOPSLA 2014), rows = the state's rows.
+ * part of v taken down to a multiple of 2^-16.  Entry n of state row r at
+ * token t draws U = K * 2^-16 for the counter ctr = (t*rows + r)*row_len + n:
+ * K is bits 16k .. 16k+15, k = ctr mod 4, of SplitMix64 output number
+ * ctr/4 + 1 for `seed` (Steele, Lea and Flood, "Fast splittable pseudorandom
+ * number generators", OOPSLA 2014), rows = the state's rows (for the two-tier
+ * state, its uint8 rows).
  * `step` is the token the next call starts at: ssq_decode_step and
  * ssq_delta_step use it and advance it by one, ssq_scan uses step .. step+T-1
  * and advances it by T, at enqueue time.  A captured graph replays the tokens

@@ -185,7 +185,7 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_delta_step(DeltaArgs a
             const uint64_t ctr0 = SR ? ((a.sr.step * (uint64_t)a.sr.rows + (uint64_t)row) * 128u + (uint64_t)j0) : 0;
             if (__all(refit_fast<F>(mn, mx, am, g))) {
                 if constexpr (SR) {
-                    round_codes_sr<F, E>(S, g, a.sr.seed, ctr0, f);
+                    round_codes_sr<F, E, true>(S, g, a.sr.seed, ctr0, f);
                 } else {
 #pragma unroll
                     for (int e = 0; e < E; ++e) f[e] = __builtin_fmaf(S[e], g.inv, g.Mz);
@@ -193,7 +193,7 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_delta_step(DeltaArgs a
             } else {
                 g = refit<F>(mn, mx, am);
                 if constexpr (SR) {
-                    round_codes_sr<F, E>(S, g, a.sr.seed, ctr0, f);
+                    round_codes_sr<F, E, false>(S, g, a.sr.seed, ctr0, f);
                 } else {
                     const bool slow_any = Tr::asym && __any(g.slow);
                     round_codes<F, E>(S, g, slow_any, f);
@@ -477,7 +477,7 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_damp_step(DeltaArgs a)
             const uint64_t ctr0 = SR ? ((a.sr.step * (uint64_t)a.sr.rows + (uint64_t)lrow) * 128u + (uint64_t)j0) : 0;
             if (__all(refit_fast<F>(mn, mx, 0.0f, g))) {
                 if constexpr (SR) {
-                    round_codes_sr<F, E>(S, g, a.sr.seed, ctr0, f);
+                    round_codes_sr<F, E, true>(S, g, a.sr.seed, ctr0, f);
                 } else {
 #pragma unroll
                     for (int e = 0; e < E; ++e) f[e] = __builtin_fmaf(S[e], g.inv, g.Mz);
@@ -485,7 +485,7 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_damp_step(DeltaArgs a)
             } else {
                 g = refit<F>(mn, mx, 0.0f);
                 if constexpr (SR) {
-                    round_codes_sr<F, E>(S, g, a.sr.seed, ctr0, f);
+                    round_codes_sr<F, E, false>(S, g, a.sr.seed, ctr0, f);
                 } else {
                     const bool slow_any = __any(g.slow);
                     round_codes<F, E>(S, g, slow_any, f);

@@ -321,37 +321,57 @@ __device__ __forceinline__ void round_codes(const float* h, const RowGrid& g, bo
 // ---------------------------------------------------------------------------
 // stochastic rounding ("ssm-state-quantization" README, Findings 9): the code
 // is floor(v + U) for the exact real v = h*inv + z and U uniform in [0, 1), on
-// the grid round-to-nearest refits.  U is the top 24 bits of SplitMix64
-// (Steele, Lea and Flood, OOPSLA 2014) output number ctr + 1 for the state's
-// seed: the state advanced ctr + 1 times by the golden gamma, then mixed.
+// the grid round-to-nearest refits.  U = K/2^16: counter ctr takes the 16-bit
+// piece k = ctr mod 4 (bits 16k .. 16k+15) of SplitMix64 (Steele, Lea and Flood,
+// OOPSLA 2014) output number ctr/4 + 1 for the state's seed, i.e. of the state
+// advanced ctr/4 + 1 times by the golden gamma and mixed.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float sr_uniform(uint64_t seed, uint64_t ctr)
+constexpr uint64_t kGoldenGamma = 0x9E3779B97F4A7C15ull;
+
+__device__ __forceinline__ uint64_t splitmix_mix(uint64_t x)
 {
-    uint64_t x = seed + (ctr + 1) * 0x9E3779B97F4A7C15ull;
     x = (x ^ (x >> 30)) * 0xBF58476D1CE4E5B9ull;
     x = (x ^ (x >> 27)) * 0x94D049BB133111EBull;
-    // the finalizer's last step, x ^= x >> 31, leaves bits 40..63 as they are
-    return (float)(uint32_t)(x >> 40) * (1.0f / 16777216.0f);
+    return x ^ (x >> 31);
 }
 
-// f = 1.5*2^23 + clamp(floor(h*inv + z + U)) for E entries whose uniforms are
-// counters ctr0 .. ctr0 + E - 1.  h*inv is exact in double, floor(p) and
-// p - floor(p) are exact, and 1 - U is exact (24 bits), so the decision to round
-// up, frac >= 1 - U, is exact.
-template <int F, int E>
+// f = 1.5*2^23 + clamp(floor(h*inv + z + U)) for E entries (E a multiple of 4) whose
+// uniforms are counters ctr0 .. ctr0 + E - 1 (ctr0 a multiple of 4): one generator
+// output per four entries.  With p = h*inv (exact in double) and K integer,
+// floor(p + K/2^16) = floor(p) + [t + K >= 2^16], t = floor(2^16 p) - 2^16 floor(p),
+// every term an exact integer in double.  FAST (the refit fast path: |z| < 2^21, so
+// |p| < 2^22) uses the equal form floor((floor(2^16 p) + K) / 2^16), exact while
+// |p| < 2^37, and finishes in fp32 with the row's 1.5*2^23 + z.
+template <int F, int E, bool FAST>
 __device__ __forceinline__ void round_codes_sr(const float* h, const RowGrid& g, uint64_t seed, uint64_t ctr0,
                                                float* f)
 {
-    constexpr double lo = (double)Traits<F>::lo;
-    constexpr double hi = (double)Traits<F>::hi;
+    static_assert(E % 4 == 0, "four uniforms per generator output");
+    constexpr float flo = kMagic + (float)Traits<F>::lo;
+    constexpr float fhi = kMagic + (float)Traits<F>::hi;
+    const double inv16 = (double)g.inv * 65536.0;
+    uint64_t x = seed + ((ctr0 >> 2) + 1) * kGoldenGamma;
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const double p = (double)h[e] * (double)g.inv;
-        const double fl = floor(p);
-        const float u = sr_uniform(seed, ctr0 + (uint64_t)e);
-        double c = fl + (double)g.zc + ((p - fl) >= 1.0 - (double)u ? 1.0 : 0.0);
-        c = fmin(fmax(c, lo), hi);
-        f[e] = kMagic + (float)c;
+    for (int q = 0; q < E / 4; ++q) {
+        const uint64_t o = splitmix_mix(x);
+        x += kGoldenGamma;
+        const uint32_t lo32 = (uint32_t)o, hi32 = (uint32_t)(o >> 32);
+        const uint32_t K[4] = {lo32 & 0xFFFFu, lo32 >> 16, hi32 & 0xFFFFu, hi32 >> 16};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int e = 4 * q + k;
+            const double P = (double)h[e] * inv16; // 2^16 h inv, exact
+            if constexpr (FAST) {
+                const double c = floor((floor(P) + (double)K[k]) * (1.0 / 65536.0));
+                f[e] = __builtin_amdgcn_fmed3f((float)c + g.Mz, flo, fhi);
+            } else {
+                const double fl = floor((double)h[e] * (double)g.inv);
+                const double t = __builtin_fma(-65536.0, fl, floor(P));
+                double c = fl + (double)g.zc + (t + (double)K[k] >= 65536.0 ? 1.0 : 0.0);
+                c = fmin(fmax(c, (double)Traits<F>::lo), (double)Traits<F>::hi);
+                f[e] = kMagic + (float)c;
+            }
+        }
     }
 }
 

@@ -118,7 +118,7 @@ struct RowStep {
         if (__all(refit_fast<F>(mn, mx, am, g))) {
             // every row of the wave is inside the verified ranges and needs no clamp
             if constexpr (SR) {
-                round_codes_sr<F, E>(h, g, sr_seed, ctr0, h);
+                round_codes_sr<F, E, true>(h, g, sr_seed, ctr0, h);
             } else {
 #pragma unroll
                 for (int e = 0; e < E; ++e) h[e] = __builtin_fmaf(h[e], g.inv, g.Mz);
@@ -126,7 +126,7 @@ struct RowStep {
         } else {
             g = refit<F>(mn, mx, am);
             if constexpr (SR) {
-                round_codes_sr<F, E>(h, g, sr_seed, ctr0, h);
+                round_codes_sr<F, E, false>(h, g, sr_seed, ctr0, h);
             } else {
                 const bool slow_any = Tr::asym && __any(g.slow);
                 round_codes<F, E>(h, g, slow_any, h);
@@ -175,7 +175,7 @@ struct RowStep {
         }
         if (__all(refit_fast<F>(mn, mx, am, g))) {
             if constexpr (SR) {
-                round_codes_sr<F, E>(h, g, sr_seed, ctr0, h);
+                round_codes_sr<F, E, true>(h, g, sr_seed, ctr0, h);
             } else {
 #pragma unroll
                 for (int e = 0; e < E; ++e) h[e] = __builtin_fmaf(h[e], g.inv, g.Mz);
@@ -183,7 +183,7 @@ struct RowStep {
         } else {
             g = refit<F>(mn, mx, am);
             if constexpr (SR) {
-                round_codes_sr<F, E>(h, g, sr_seed, ctr0, h);
+                round_codes_sr<F, E, false>(h, g, sr_seed, ctr0, h);
             } else {
                 const bool slow_any = Tr::asym && __any(g.slow);
                 round_codes<F, E>(h, g, slow_any, h);
