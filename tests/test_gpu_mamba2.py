@@ -240,6 +240,33 @@ def test_8b_decode_layer_full_size(fmt):
 
 
 @pytest.mark.parametrize("fmt", ["int8_sym", "int4_asym"])
+def test_8b_decode_256_steps(fmt):
+    """8B-shaped decode at batch 256 for 256 steps, free-running from a zero state (8 of the 128
+    heads: every row is independent, and the full 128 heads run in the test above).  The oracle
+    follows 256 sampled rows; after 256 rounded steps y stays within 1e-3 and at most 1e-4 of the
+    codes differ."""
+    B, H, P, T, seed = 256, 8, 64, 256, 6
+    rows = B * H * P
+    sample = np.unique(np.linspace(0, rows - 1, 256).astype(np.int64))
+    say(f"8b decode {fmt}: {T} steps at batch {B}")
+    gst = par.new_gpu_state(m2desc(fmt, B, H, P))
+    ost = oracle.make_state(fmt, len(sample), 128)
+    xr, dtr, Br, Cr, Ar, Dr = synth.mamba2_rows_scan_inputs(seed, 0, B, T, H, 1, P, 128, sample)
+    yo = oracle.mamba2_rows_scan(ost, xr, dtr, Ar, Br, Cr, Dr)
+    yg = np.empty((len(sample), T), np.float32)
+    for t in range(T):
+        x, dt, Bm, Cm, A, D = synth.mamba2_step_inputs(seed, 0, B, H, 1, P, 128, t=t)
+        yg[:, t] = run_step(gst, x, dt, A, Bm, Cm, D, ssq.SSQ_READ_POST_QUANT).reshape(-1)[sample]
+    assert par.block_rel(yg, yo, axis=1) <= 1e-3
+    g = par.read_gpu_state(gst, fmt)
+    mism = (g["code"][sample] != ost.code).mean()
+    say(f"  code mismatch fraction after {T} steps: {mism}")
+    assert mism <= 1e-4
+    deq_g = oracle.dequantize_rows(g["code"][sample], g["scale"][sample], g["zero"][sample])
+    assert par.block_rel(deq_g, ost.dequant(), axis=1) <= 1e-3
+
+
+@pytest.mark.parametrize("fmt", ["int8_sym", "int4_asym"])
 def test_8b_long_scan_sampled(fmt):
     """Mamba-2 8B-shaped heads over 8192 tokens with the state rounded every token (16 heads of one
     sequence here; the oracle follows 64 sampled rows)."""
