@@ -356,7 +356,7 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_damp_step(DeltaArgs a)
         kk[r] = a.k[mrow0 + i];
         qq[r] = a.q[mrow0 + i];
         if (r == 0 && hi_wave) {
-            load_words<2 * NW>(a.hi + (mat * kNhi + i) * 128 + j0, cw[r]);
+            load_words<2 * NW, false>(a.hi + (mat * kNhi + i) * 128 + j0, cw[r]);
             s_old[r] = 1.0f;
             z_old[r] = 0.0f;
         } else {
@@ -449,7 +449,7 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_damp_step(DeltaArgs a)
                 S[2 * q] = half_bits_to_float(lo);
                 S[2 * q + 1] = half_bits_to_float(hi);
             }
-            store_words<2 * NW>(a.hi + (mat * kNhi + i) * 128 + j0, hw);
+            store_words<2 * NW, false>(a.hi + (mat * kNhi + i) * 128 + j0, hw);
             if constexpr (!PRE) {
 #pragma unroll
                 for (int e = 0; e < E; ++e) op[e] = __builtin_fmaf(qq[r], S[e], op[e]);
@@ -552,7 +552,7 @@ __global__ __launch_bounds__(256) void k_damp_rows(QArgs a)
 #pragma unroll
             for (int q = 0; q < 2 * NW; ++q)
                 hw[q] = float_to_half_bits(rv[2 * q]) | (float_to_half_bits(rv[2 * q + 1]) << 16);
-            store_words<2 * NW>(a.hi + (mat * kNhi + i) * 128 + j0, hw);
+            store_words<2 * NW, false>(a.hi + (mat * kNhi + i) * 128 + j0, hw);
         } else {
             float mn = rv[0], mx = rv[0];
 #pragma unroll

@@ -441,28 +441,33 @@ __device__ __forceinline__ bool refit_fast(float mn, float mx, float amax, RowGr
 // vector memory helpers: NW consecutive 32-bit words at a 4*NW-byte aligned address
 // ---------------------------------------------------------------------------
 // The state is streamed: every byte is read once and written once per step.
-// With SSQ_NT the state's loads and stores carry the non-temporal hint.
+// SSQ_NT_LD / SSQ_NT_ST put the non-temporal hint on the state's loads / stores.
+// The hint pays where one store instruction covers whole 64-byte segments (a
+// quantized row's lanes hold adjacent 16-byte pieces).  Where a lane's pieces
+// are 16 bytes at a wider stride (fp32 rows, half rows), the hinted stores
+// leave partial segments that reach HBM unmerged: those rows go without it
+// (an fp32 decode step took 2.9x as long with it).
 #ifndef SSQ_NT
 #define SSQ_NT 1
 #endif
+#ifndef SSQ_NT_LD
+#define SSQ_NT_LD SSQ_NT
+#endif
+#ifndef SSQ_NT_ST
+#define SSQ_NT_ST SSQ_NT
+#endif
 
-template <typename T>
+template <typename T, bool NT = true>
 __device__ __forceinline__ T ld_stream(const T* p)
 {
-#if SSQ_NT
-    return __builtin_nontemporal_load(p);
-#else
-    return *p;
-#endif
+    if constexpr (NT && SSQ_NT_LD) return __builtin_nontemporal_load(p);
+    else return *p;
 }
-template <typename T>
+template <typename T, bool NT = true>
 __device__ __forceinline__ void st_stream(T* p, T v)
 {
-#if SSQ_NT
-    __builtin_nontemporal_store(v, p);
-#else
-    *p = v;
-#endif
+    if constexpr (NT && SSQ_NT_ST) __builtin_nontemporal_store(v, p);
+    else *p = v;
 }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -475,7 +480,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // ---------------------------------------------------------------------------
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 constexpr int kRsrcWord3 = 0x00020000; // gfx9 family: 32-bit data format, no swizzle, no stride
-constexpr int kAuxStream = SSQ_NT ? 2 : 0; // the non-temporal hint on state traffic
+constexpr int kAuxLoad = SSQ_NT_LD ? 2 : 0;  // the non-temporal hint on state loads
+constexpr int kAuxStore = SSQ_NT_ST ? 2 : 0; // ... and stores
 
 __device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes)
 {
@@ -529,38 +535,38 @@ __device__ __forceinline__ void buf_store_f32(float v, Rsrc r, uint32_t voff, ui
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, AUX);
 }
 
-template <int NW>
+template <int NW, bool NT = true>
 __device__ __forceinline__ void load_words(const void* p, uint32_t* w)
 {
     if constexpr (NW % 4 == 0) {
 #pragma unroll
         for (int i = 0; i < NW / 4; ++i) {
-            const u32x4 v = ld_stream(reinterpret_cast<const u32x4*>(p) + i);
+            const u32x4 v = ld_stream<u32x4, NT>(reinterpret_cast<const u32x4*>(p) + i);
             w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
         }
     } else if constexpr (NW == 2) {
-        const u32x2 v = ld_stream(reinterpret_cast<const u32x2*>(p));
+        const u32x2 v = ld_stream<u32x2, NT>(reinterpret_cast<const u32x2*>(p));
         w[0] = v.x; w[1] = v.y;
     } else {
         static_assert(NW == 1, "unsupported lane width");
-        w[0] = ld_stream(reinterpret_cast<const uint32_t*>(p));
+        w[0] = ld_stream<uint32_t, NT>(reinterpret_cast<const uint32_t*>(p));
     }
 }
 
-template <int NW>
+template <int NW, bool NT = true>
 __device__ __forceinline__ void store_words(void* p, const uint32_t* w)
 {
     if constexpr (NW % 4 == 0) {
 #pragma unroll
         for (int i = 0; i < NW / 4; ++i) {
             const u32x4 v = {w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
-            st_stream(reinterpret_cast<u32x4*>(p) + i, v);
+            st_stream<u32x4, NT>(reinterpret_cast<u32x4*>(p) + i, v);
         }
     } else if constexpr (NW == 2) {
         const u32x2 v = {w[0], w[1]};
-        st_stream(reinterpret_cast<u32x2*>(p), v);
+        st_stream<u32x2, NT>(reinterpret_cast<u32x2*>(p), v);
     } else {
-        st_stream(reinterpret_cast<uint32_t*>(p), w[0]);
+        st_stream<uint32_t, NT>(reinterpret_cast<uint32_t*>(p), w[0]);
     }
 }
 

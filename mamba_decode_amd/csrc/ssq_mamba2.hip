@@ -257,12 +257,12 @@ __global__ __launch_bounds__(256, W) void k_m2_step(M2Args a, int64_t it_base)
     auto issue = [&](int slot, int i) {
         const uint32_t sw = (uint32_t)i * RPW * WB, sr = (uint32_t)i * RPW * 4;
         if constexpr (Tr::quant) {
-            buf_load_words<NW, kAuxStream>(r_w, off_w, sw, ring[slot]);
-            rs[slot] = buf_load_f32<kAuxStream>(r_s, off_r, sr);
-            if constexpr (Tr::asym) rz[slot] = buf_load_f32<kAuxStream>(r_z, off_r, sr);
+            buf_load_words<NW, kAuxLoad>(r_w, off_w, sw, ring[slot]);
+            rs[slot] = buf_load_f32<kAuxLoad>(r_s, off_r, sr);
+            if constexpr (Tr::asym) rz[slot] = buf_load_f32<kAuxLoad>(r_z, off_r, sr);
             else rz[slot] = 0.0f;
         } else {
-            buf_load_words<E, kAuxStream>(r_w, off_w, sw, ring[slot]);
+            buf_load_words<E, 0>(r_w, off_w, sw, ring[slot]); // fp32 rows: no hint
             rs[slot] = 0.0f;
             rz[slot] = 0.0f;
         }
@@ -348,15 +348,15 @@ __global__ __launch_bounds__(256, W) void k_m2_step(M2Args a, int64_t it_base)
             float yv;
             if constexpr (BCL) yv = RS::template run_q<true, SR>(cf, ls, lz, w, dx, rin_l, ow, g, a.sr.seed, ctr0);
             else yv = RS::template run_q<true, SR>(cf, ls, lz, w, dx, rin, ow, g, a.sr.seed, ctr0);
-            buf_store_words<NW, kAuxStream>(r_w, off_w, sw, ow);
-            buf_store_f32<kAuxStream>(g.s, r_s, off_r, sr);
-            if constexpr (Tr::asym) buf_store_f32<kAuxStream>(g.z, r_z, off_r, sr);
+            buf_store_words<NW, kAuxStore>(r_w, off_w, sw, ow);
+            buf_store_f32<kAuxStore>(g.s, r_s, off_r, sr);
+            if constexpr (Tr::asym) buf_store_f32<kAuxStore>(g.z, r_z, off_r, sr);
             buf_store_f32<0>(yv, r_y, off_r, sr);
         } else {
             float yv;
             if constexpr (BCL) yv = RS::run_f(cf, lam, w, dx, rin_l);
             else yv = RS::run_f(cf, lam, w, dx, rin);
-            buf_store_words<E, kAuxStream>(r_w, off_w, sw, reinterpret_cast<const uint32_t*>(cf));
+            buf_store_words<E, 0>(r_w, off_w, sw, reinterpret_cast<const uint32_t*>(cf)); // fp32 rows: no hint
             buf_store_f32<0>(yv, r_y, off_r, sr);
         }
         if (++jh == ipH) {
