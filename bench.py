@@ -32,8 +32,12 @@ sys.path.insert(0, ROOT)
 
 METRIC = "state-update GB/s + % of HBM peak; decode steps/s at batch 256"
 HBM_PEAK_GBPS = 8000.0
-# fp32 vector issue without packed instructions: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
-VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+# VALU roofline of the on-chip paths, in lane-operations/s: the fp32 vector peak (157.3 TFLOP/s,
+# an fma counted as two flops) is 78.6 T fp32 operations per second (256 CUs x 4 SIMDs x 32
+# lanes x 2.4 GHz).  The kernels are built without packed fp32, so three-operand instructions
+# (fma, med3) issue at half of it, one wave64 instruction per 4 cycles per SIMD (36.4 T/s
+# measured with independent fma chains); two-operand ones issue faster (v_add_f32: 58.5 T/s).
+VALU_PEAK_TOPS = 256 * 4 * 32 * 2.4e9 / 1e12
 
 WORKLOADS = {
     # name: kind, layers, batch, heads, rows_per_head, format, init, tokens (scan), instances

@@ -233,6 +233,15 @@ __device__ __forceinline__ void pack_codes(const float* f, uint32_t* w)
     }
 }
 
+// h = fma(a, h, c), one rounding, written back into the register that holds h: the same
+// instruction as __builtin_fmaf.  For a value carried from one token to the next, the
+// compiler picks the form that writes the addend's register (v_fmac) and then copies every
+// result back, one move per entry and token.
+__device__ __forceinline__ void fma_in_place(float a, float& h, float c)
+{
+    asm("v_fma_f32 %0, %1, %0, %2" : "+v"(h) : "v"(a), "v"(c));
+}
+
 // ---------------------------------------------------------------------------
 // refit of one row from its statistics (every lane of the row computes it)
 // ---------------------------------------------------------------------------

@@ -578,7 +578,7 @@ __global__ __launch_bounds__(256, PRE ? SSQ_PREFILL_WAVES - 1 : SSQ_PREFILL_WAVE
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             const float wb = w * in.b(e);
-            hv[e] = __builtin_fmaf(lam, hv[e], wb);
+            fma_in_place(lam, hv[e], wb);
         }
         const bool end = (t + 1) % chunk == 0 || t == T - 1; // wave-uniform
         float acc = 0.0f;
