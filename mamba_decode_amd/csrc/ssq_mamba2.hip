@@ -348,9 +348,10 @@ __global__ __launch_bounds__(256, W) void k_m2_step(M2Args a, int64_t it_base)
             float yv;
             if constexpr (BCL) yv = RS::template run_q<true, SR>(cf, ls, lz, w, dx, rin_l, ow, g, a.sr.seed, ctr0);
             else yv = RS::template run_q<true, SR>(cf, ls, lz, w, dx, rin, ow, g, a.sr.seed, ctr0);
-            buf_store_words<NW, kAuxStore>(r_w, off_w, sw, ow);
-            buf_store_f32<kAuxStore>(g.s, r_s, off_r, sr);
-            if constexpr (Tr::asym) buf_store_f32<kAuxStore>(g.z, r_z, off_r, sr);
+            constexpr int AUXS = Tr::bits == 4 ? kAuxStoreWhole : kAuxStore;
+            buf_store_words<NW, AUXS>(r_w, off_w, sw, ow);
+            buf_store_f32<AUXS>(g.s, r_s, off_r, sr);
+            if constexpr (Tr::asym) buf_store_f32<AUXS>(g.z, r_z, off_r, sr);
             buf_store_f32<0>(yv, r_y, off_r, sr);
         } else {
             float yv;
