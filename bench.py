@@ -288,19 +288,44 @@ def main():
     # included, which makes the figure conservative)
     kernel_ms_mean = ms_per_step / L
 
+    # ---------------- eager back-to-back steps (no events between launches): context ----------------
+    if not seq:
+        s = vp(torch.cuda.current_stream().cuda_stream)
+        run_step()
+        torch.cuda.synchronize()
+        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b0.record()
+        for _ in range(kreps):
+            run_step()
+        b1.record()
+        b1.synchronize()
+        eager_ms_per_step = b0.elapsed_time(b1) / kreps
+    else:
+        eager_ms_per_step = None
+
     # ---------------- copy bandwidth in the same run (context) ----------------
-    nbytes = 1 << 30
+    # the library's streaming copy kernel over 2 GiB (4 GiB of traffic), and the runtime's copy
+    nbytes = 1 << 31
     src = torch.empty(nbytes // 4, device=dev)
     dst = torch.empty_like(src)
-    dst.copy_(src)
+    ssq.ssq_stream_copy(dst, src)
     torch.cuda.synchronize()
     c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     c0.record()
-    for _ in range(10):
-        dst.copy_(src)
+    for _ in range(5):
+        ssq.ssq_stream_copy(dst, src)
     c1.record()
     c1.synchronize()
-    copy_gbps = 2 * nbytes * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    copy_gbps = 2 * nbytes * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    n1 = (1 << 30) // 4  # the runtime's copy of 1 GiB (the traffic passes are calibrated on it)
+    dst[:n1].copy_(src[:n1])
+    torch.cuda.synchronize()
+    c0.record()
+    for _ in range(5):
+        dst[:n1].copy_(src[:n1])
+    c1.record()
+    c1.synchronize()
+    runtime_copy_gbps = 2 * (1 << 30) * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del src, dst
 
     total_bytes_step = bytes_per_launch * L
@@ -344,8 +369,12 @@ def main():
                                if not seq else None),
         "tokens_per_s": round(B * T / (ms_per_step * 1e-3 / L), 1) if seq else None,
         "state_GBps": round(state_gbps, 2) if state_gbps else None,
+        "decode_steps_per_s_eager": (round(1000.0 * (L if wl.get("rotate") else 1) / eager_ms_per_step, 2)
+                                     if eager_ms_per_step else None),
         "copy_GBps": round(copy_gbps, 1),
+        "copy_kind": "ssq_stream_copy, 2 GiB (4 GiB of traffic), same run",
         "frac_of_copy": round(value / copy_gbps, 4),
+        "runtime_copy_GBps": round(runtime_copy_gbps, 1),
         "roofline": {
             "bound": "hbm" if not seq else "alu",
             "kernel": KERNEL_NAMES[kind] + f"<{fmt}>",

@@ -272,6 +272,14 @@ ssq_status ssq_kda_step(ssq_state *state, const float *q, const float *k, const 
  * fp32 for SSQ_FP32): out [batch][nheads][rows_per_head][row_len]. */
 ssq_status ssq_dequant(const ssq_state *state, float *out, void *stream);
 
+/* A streaming copy of `bytes` bytes from device memory src to device memory dst,
+ * enqueued on `stream`: the plain read-and-write kernel a state step's bandwidth is
+ * compared with on the same device (one 16-byte load and store per lane, with the
+ * non-temporal hint).  Not part of the state update.  bytes: a multiple of 16, at most
+ * 2^40 (0 enqueues nothing); dst and src 16-byte aligned and not overlapping, else
+ * SSQ_ERR_INVALID_ARG before anything is enqueued.  The caller owns both buffers. */
+ssq_status ssq_stream_copy(void *dst, const void *src, size_t bytes, void *stream);
+
 /* Static text for a status code. */
 const char *ssq_status_string(ssq_status status);
 

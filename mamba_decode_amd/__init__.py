@@ -80,6 +80,8 @@ def _load():
     L.ssq_delta_step.restype = st
     L.ssq_dequant.argtypes = [vp, f32p, vp]
     L.ssq_dequant.restype = st
+    L.ssq_stream_copy.argtypes = [vp, vp, ctypes.c_size_t, vp]
+    L.ssq_stream_copy.restype = st
     L.ssq_status_string.argtypes = [ctypes.c_int]
     L.ssq_status_string.restype = ctypes.c_char_p
     L.ssq_last_error.argtypes = []
@@ -299,3 +301,16 @@ def ssq_kda_step(state: State, q, k, v, alpha, beta, o, readout: int = SSQ_READ_
 def ssq_dequant(state: State, out, stream=None):
     _check(lib.ssq_dequant(state.handle, _dev(out, "out", state.rows * state.desc.row_len), _stream(stream)),
            "ssq_dequant")
+
+
+def ssq_stream_copy(dst, src, nbytes: int | None = None, stream=None):
+    """Copy ``nbytes`` (default: all of ``src``) from one CUDA tensor to another with the
+    library's streaming copy kernel."""
+    for name, t in (("dst", dst), ("src", src)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous CUDA tensor")
+    n = src.numel() * src.element_size() if nbytes is None else int(nbytes)
+    if n > src.numel() * src.element_size() or n > dst.numel() * dst.element_size():
+        raise ValueError("nbytes exceeds a tensor")
+    _check(lib.ssq_stream_copy(ctypes.c_void_p(dst.data_ptr()), ctypes.c_void_p(src.data_ptr()), n, _stream(stream)),
+           "ssq_stream_copy")

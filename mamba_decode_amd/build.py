@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libssq.so")
 
-SOURCES = ["ssq_api.cpp", "ssq_mamba2.hip", "ssq_delta.hip"]
+SOURCES = ["ssq_api.cpp", "ssq_mamba2.hip", "ssq_delta.hip", "ssq_copy.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

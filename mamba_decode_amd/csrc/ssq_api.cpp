@@ -457,6 +457,17 @@ ssq_status ssq_dequant(const ssq_state* st, float* out, void* stream)
     return from_hip(ssq::launch_rows(st->desc.format, a, true, (hipStream_t)stream), "dequant launch");
 }
 
+ssq_status ssq_stream_copy(void* dst, const void* src, size_t bytes, void* stream)
+{
+    SSQ_REQUIRE(dst && src, SSQ_ERR_INVALID_ARG, "dst and src must not be NULL");
+    SSQ_REQUIRE(aligned(dst, 16) && aligned(src, 16), SSQ_ERR_INVALID_ARG, "dst and src must be 16-byte aligned");
+    SSQ_REQUIRE(bytes % 16 == 0, SSQ_ERR_INVALID_ARG, "bytes must be a multiple of 16");
+    SSQ_REQUIRE(bytes <= ((size_t)1 << 40), SSQ_ERR_INVALID_ARG, "bytes must not exceed 2^40");
+    const uintptr_t s = (uintptr_t)src, d = (uintptr_t)dst;
+    SSQ_REQUIRE(d + bytes <= s || s + bytes <= d, SSQ_ERR_INVALID_ARG, "dst and src must not overlap");
+    return from_hip(ssq::launch_stream_copy(dst, src, (int64_t)bytes, (hipStream_t)stream), "copy launch");
+}
+
 const char* ssq_status_string(ssq_status status)
 {
     switch (status) {

@@ -73,5 +73,6 @@ hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t st);
 hipError_t launch_delta_step(int fmt, DeltaArgs a, bool pre, hipStream_t st);
 hipError_t launch_damp_step(DeltaArgs a, bool pre, hipStream_t st);
 hipError_t launch_damp_rows(QArgs a, bool dequant, hipStream_t st);
+hipError_t launch_stream_copy(void* dst, const void* src, int64_t bytes, hipStream_t st);
 
 } // namespace ssq

@@ -161,3 +161,20 @@ def test_two_tier_layout():
     bad = ssq.make_desc(ssq.SSQ_MAMBA2, "damp", 1, 2, 64)
     h = ctypes.c_void_p()
     assert ssq.lib.ssq_alloc_state(ctypes.byref(bad), None, None, None, ctypes.byref(h)) == ssq.SSQ_ERR_UNSUPPORTED
+
+
+def test_stream_copy_validates_before_launch():
+    """Rejected copies return INVALID_ARG from the argument checks alone (no device work)."""
+    import mamba_decode_amd as ssq
+    vp = ctypes.c_void_p
+    cases = [
+        (None, vp(4096), 64),            # NULL dst
+        (vp(4096), None, 64),            # NULL src
+        (vp(4096 + 8), vp(1 << 20), 64),  # misaligned dst
+        (vp(4096), vp(1 << 20), 40),     # not a multiple of 16
+        (vp(4096), vp(4096 + 32), 64),   # overlapping
+        (vp(4096 + 32), vp(4096), 64),   # overlapping the other way
+    ]
+    for dst, src, n in cases:
+        assert ssq.lib.ssq_stream_copy(dst, src, n, None) == ssq.SSQ_ERR_INVALID_ARG, (dst, src, n)
+        assert ssq.ssq_last_error()
