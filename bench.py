@@ -20,7 +20,6 @@ print the same schema.
 from __future__ import annotations
 
 import argparse
-import glob
 import hashlib
 import json
 import os
@@ -101,10 +100,16 @@ def parse():
     return ap.parse_args()
 
 
-def src_hash() -> str:
+KERNEL_SOURCES = {"m2": "ssq_mamba2.hip", "scan": "ssq_mamba2.hip", "prefill": "ssq_mamba2.hip",
+                  "delta": "ssq_delta.hip", "kda": "ssq_delta.hip"}
+
+
+def src_hash(kind: str) -> str:
+    """Hash of the sources a workload's kernel is built from (the committed traffic figures
+    hold only while it is unchanged)."""
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "mamba_decode_amd", "csrc", "*"))):
-        h.update(open(p, "rb").read())
+    for name in ("ssq_device.h", "ssq_internal.h", KERNEL_SOURCES[kind]):
+        h.update(open(os.path.join(ROOT, "mamba_decode_amd", "csrc", name), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -338,7 +343,7 @@ def main():
     tpath = os.path.join(ROOT, "profiles", "traffic.json")
     if os.path.exists(tpath):
         tr = json.load(open(tpath)).get(args.workload)
-        if tr and tr.get("src_hash") == src_hash():
+        if tr and tr.get("src_hash") == src_hash(kind):
             traffic = tr.get("hbm_bytes_per_launch")
 
     rec = {
