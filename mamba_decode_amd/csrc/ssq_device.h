@@ -490,10 +490,11 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 constexpr int kRsrcWord3 = 0x00020000; // gfx9 family: 32-bit data format, no swizzle, no stride
 // cache-policy bits of the state's buffer loads and stores: sc0 = 1, nt = 2, sc1 = 16.
-// kAuxStoreWhole is for stores whose instruction covers whole 64-byte segments (an int4
-// row's four lanes store its 64 bytes at once): sc1 | nt measured 2.6% faster than nt alone
-// on the 370m int4 decode step.  Where a lane's pieces leave partial segments (int8 rows:
-// two 16-byte pieces 32 bytes apart) sc1 doubled the step's time: those keep nt.
+// kAuxStoreWhole is for stores whose instruction covers whole 64-byte segments (a lane
+// holding 16 contiguous bytes of a row, so a row's lanes store it at once): sc1 | nt
+// measured 2.6% faster than nt alone on the 370m int4 decode step.  Where a lane's pieces
+// leave partial segments (two 16-byte pieces 32 bytes apart) sc1 doubled the step's time:
+// those keep nt.
 #ifndef SSQ_STORE_POLICY
 #define SSQ_STORE_POLICY (SSQ_NT_ST ? 2 : 0)
 #endif

@@ -348,7 +348,8 @@ __global__ __launch_bounds__(256, W) void k_m2_step(M2Args a, int64_t it_base)
             float yv;
             if constexpr (BCL) yv = RS::template run_q<true, SR>(cf, ls, lz, w, dx, rin_l, ow, g, a.sr.seed, ctr0);
             else yv = RS::template run_q<true, SR>(cf, ls, lz, w, dx, rin, ow, g, a.sr.seed, ctr0);
-            constexpr int AUXS = Tr::bits == 4 ? kAuxStoreWhole : kAuxStore;
+            // a lane's 16 bytes of a row: one store instruction writes whole rows
+            constexpr int AUXS = 128 * Tr::bits / 8 / LPR == 16 ? kAuxStoreWhole : kAuxStore;
             buf_store_words<NW, AUXS>(r_w, off_w, sw, ow);
             buf_store_f32<AUXS>(g.s, r_s, off_r, sr);
             if constexpr (Tr::asym) buf_store_f32<AUXS>(g.z, r_z, off_r, sr);
@@ -718,11 +719,26 @@ constexpr int lanes_per_row()
 {
     return F == FP32 ? SSQ_LPR_FP32 : (Traits<F>::bits == 8 ? SSQ_LPR_INT8 : SSQ_LPR_INT4);
 }
+// The decode step spreads an int8 row over 8 lanes: a lane then holds 16 contiguous bytes
+// of the row, one store instruction writes whole rows (with the write-through streaming
+// policy), and shorter waves keep more rows in flight; 8B-shaped int8 step 120.8 to about
+// 100 us.  The scan and prefill keep 4: they store the state once per launch, and with
+// 16 entries per lane their per-token refit would cost twice the VALU per entry.
+#ifndef SSQ_STEP_LPR_INT8
+#define SSQ_STEP_LPR_INT8 8
+#endif
+template <int F>
+constexpr int step_lanes_per_row()
+{
+    return F != FP32 && Traits<F>::bits == 8 ? SSQ_STEP_LPR_INT8 : lanes_per_row<F>();
+}
 
 // iterations per wave (straight-line code), prefetch distance and the waves per
 // SIMD the register budget is sized for (launch bounds), per code width.  With B
 // and C in LDS and buffer addressing both quantized widths fit 128 registers
-// (4 waves per SIMD); K = 8 then makes one round of resident waves at 370m shape.
+// (4 waves per SIMD); int4: K = 8 makes one round of resident waves at 370m shape;
+// int8 (8 rows per wave-iteration): K = 4 with every iteration's loads issued up front
+// measured fastest (K = 8 with a ring of 4 about 3% slower, K = 1 or a ring of 3 about 20%).
 #ifndef SSQ_ITERS_INT4
 #define SSQ_ITERS_INT4 8
 #endif
@@ -733,10 +749,10 @@ constexpr int lanes_per_row()
 #define SSQ_WAVES_INT4 4
 #endif
 #ifndef SSQ_ITERS_INT8
-#define SSQ_ITERS_INT8 8
+#define SSQ_ITERS_INT8 4
 #endif
 #ifndef SSQ_RING_INT8
-#define SSQ_RING_INT8 3
+#define SSQ_RING_INT8 4
 #endif
 #ifndef SSQ_WAVES_INT8
 #define SSQ_WAVES_INT8 4
@@ -772,7 +788,7 @@ constexpr int step_waves()
 template <int F, bool PRE, bool SR>
 static hipError_t launch_step_fp(M2Args a, hipStream_t st)
 {
-    constexpr int LPR = lanes_per_row<F>();
+    constexpr int LPR = step_lanes_per_row<F>();
     constexpr int RPW = 64 / LPR;
     a.total_iters = (int64_t)a.Bsz * a.H * a.P / RPW;
     constexpr int kStepIters = step_iters<F>();

@@ -54,6 +54,16 @@ def init_rows(seed, layer, nrows, N=128, special=True):
     return h
 
 
+def assert_same_y(y_scan, y_step, fmt):
+    """y of a scan against y of the same tokens as decode steps.  The decode step spreads an
+    int8 row over 8 lanes and the scan over 4, so for int8 the C.h sum runs in another order
+    (the states are bit-identical all the same); otherwise y is bit-identical too."""
+    if fmt.startswith("int8"):
+        assert par.block_rel(y_scan, y_step, axis=-1) <= 1e-5  # the y tolerance of the contract
+    else:
+        assert np.array_equal(np.asarray(y_scan, np.float32).view(np.uint32), np.asarray(y_step, np.float32).view(np.uint32))
+
+
 def run_step(gst, x, dt, A, Bm, Cm, D, readout):
     y = torch.empty(x.shape, dtype=torch.float32, device="cuda")
     ssq.ssq_decode_step(gst, par.dev(x), par.dev(dt), par.dev(A), par.dev(Bm), par.dev(Cm), par.dev(D), y,
@@ -136,7 +146,7 @@ def test_config0_free_running_and_scan_equivalence():
     gs = par.read_gpu_state(gsc, fmt)
     assert np.array_equal(gs["code"], g["code"]) and np.array_equal(gs["scale"], g["scale"])
     assert np.array_equal(gs["zero"], g["zero"])
-    assert np.array_equal(y_scan.cpu().numpy().view(np.uint32), y_step.view(np.uint32))
+    assert_same_y(y_scan.cpu().numpy(), y_step, fmt)
 
 
 @pytest.mark.parametrize("readout", ["post", "pre"])
@@ -157,7 +167,7 @@ def test_scan_equals_repeated_steps_and_oracle(fmt, readout):
     for k in s1:
         assert np.array_equal(s1[k].view(np.uint32) if s1[k].dtype == np.float32 else s1[k],
                               s2[k].view(np.uint32) if s2[k].dtype == np.float32 else s2[k]), k
-    assert np.array_equal(y1.cpu().numpy().view(np.uint32), y2.view(np.uint32))
+    assert_same_y(y1.cpu().numpy(), y2, fmt)
     ost = oracle.make_state(fmt, rows, 128, init)
     yo = oracle.mamba2_scan(ost, x, dt, A, Bm, Cm, D, readout=readout)
     if fmt == "fp32":
