@@ -29,6 +29,16 @@ namespace ssq {
 #define SSQ_DELTA_WAVES 4
 #endif
 
+// A quantized key row's piece (4*NW bytes at `off` within the block's rows) stored through a
+// buffer descriptor over the block's own rows, with the write-through streaming policy: the
+// row's 8 lanes store it whole with one instruction.
+template <int NW>
+__device__ __forceinline__ void store_row_piece(uint8_t* rows_base, uint32_t rows_bytes, uint32_t off,
+                                                const uint32_t* w)
+{
+    buf_store_words<NW, kAuxStoreWhole>(make_rsrc(rows_base, rows_bytes), off, 0u, w);
+}
+
 // Partial rows in LDS: element j of row group r sits at r*kPartPitch + j + j/16.  A wave
 // writes 8 row groups x 8 segments of 16 columns at once; without the padding every lane
 // of it lands on the same bank.
@@ -201,7 +211,9 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_delta_step(DeltaArgs a
             }
             uint32_t ow[NW];
             pack_codes<F, E>(f, ow);
-            store_words<NW>(a.codes + row * ROWB + part * (NW * 4), ow);
+            if constexpr (Tr::quant)
+                store_row_piece<NW>(a.codes + mrow0 * ROWB, 128u * ROWB,
+                                    (uint32_t)((row - mrow0) * ROWB + part * (NW * 4)), ow);
             if (part == 0) {
                 a.scale[row] = g.s;
                 if constexpr (Tr::asym) a.zero[row] = g.z;
@@ -493,7 +505,8 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_damp_step(DeltaArgs a)
             }
             uint32_t ow[NW];
             pack_codes<F, E>(f, ow);
-            store_words<NW>(a.codes + lrow * ROWB + part * (NW * 4), ow);
+            store_row_piece<NW>(a.codes + mat * kNlo * ROWB, (uint32_t)(kNlo * ROWB),
+                                (uint32_t)((lrow - mat * kNlo) * ROWB + part * (NW * 4)), ow);
             if (part == 0) {
                 a.scale[lrow] = g.s;
                 a.zero[lrow] = g.z;
