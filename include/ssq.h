@@ -213,7 +213,9 @@ ssq_status ssq_decode_step(ssq_state *state, const float *x, const float *dt, co
 
 /* T Mamba-2 tokens in one launch, the state rounded after every token (the
  * sequential per-token scan of the README's Setup, which rounds the state at
- * every step).  Bit-identical to T calls of ssq_decode_step.
+ * every step).  The state it leaves is bit-identical to T calls of
+ * ssq_decode_step; y agrees to the order of its C.h sum (bit-identical too
+ * for int4 and fp32 states, whose rows both kernels spread over the same lanes).
  *   x [batch][T][nheads][P], dt [batch][T][nheads], B, C [batch][T][ngroups][N],
  *   A, D [nheads]; y [batch][T][nheads][P] is written. */
 ssq_status ssq_scan(ssq_state *state, int32_t T, const float *x, const float *dt, const float *A,
