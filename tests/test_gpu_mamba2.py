@@ -121,6 +121,32 @@ def test_decode_step_teacher_forced(fmt, readout):
     say(f"  flipped codes: {flips}")
 
 
+@pytest.mark.parametrize("readout", ["post", "pre"])
+@pytest.mark.parametrize("shape", [(1, 5, 1, 16), (3, 7, 7, 48), (2, 9, 3, 80)])
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_decode_ragged_wave_tails(fmt, shape, readout):
+    """Row counts that leave part of a wave's iterations to the one-iteration tail launch
+    (80, 1,008 and 1,440 rows: an int4 or fp32 wave-iteration takes 16 rows and a wave 8 of
+    them, an int8 wave-iteration 8 rows and a wave 4), groups shared by 1, 1 or 3 heads."""
+    B, H, G, P = shape
+    rows = B * H * P
+    ro = ssq.SSQ_READ_PRE_QUANT if readout == "pre" else ssq.SSQ_READ_POST_QUANT
+    say(f"ragged fmt={fmt} shape={shape} readout={readout}")
+    ost = oracle.make_state(fmt, rows, 128, init_rows(43, 2, rows))
+    gst = par.new_gpu_state(m2desc(fmt, B, H, P, G))
+    for t in range(2):
+        x, dt, Bm, Cm, A, D = synth.mamba2_step_inputs(43, 2, B, H, G, P, 128, t=t)
+        par.write_gpu_state(gst, ost)
+        yg = run_step(gst, x, dt, A, Bm, Cm, D, ro)
+        yo, _, vq = oracle.mamba2_step(ost, x, dt, A, Bm, Cm, D, readout=readout, diag=True)
+        g = par.read_gpu_state(gst, fmt)
+        if fmt == "fp32":
+            assert np.array_equal(g["h"], ost.h), t
+        else:
+            par.check_codes(g, ost.code, ost.scale, ost.zero, vq, fmt, f"t={t}")
+        assert par.block_rel(yg, yo, axis=2) <= 1e-5, t
+
+
 def test_config0_free_running_and_scan_equivalence():
     """Single Mamba-2 layer, batch 1, 24 heads x 64 x 128, T = 64, int8 asymmetric, state from 0,
     seed 0: 64 decode steps against the oracle, and one 64-token scan that must equal them bit for bit."""
