@@ -97,6 +97,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--seed", type=int, default=2)
+    ap.add_argument("--layers", type=int, default=None,
+                    help="fewer layers than the workload names (quick checks only; recorded in config)")
     return ap.parse_args()
 
 
@@ -131,7 +133,11 @@ def main():
     import mamba_decode_amd as ssq
     import synth
 
-    wl = WORKLOADS[args.workload]
+    wl = dict(WORKLOADS[args.workload])
+    if args.layers is not None:
+        if args.layers < 1:
+            raise SystemExit("--layers must be positive")
+        wl["layers"] = args.layers
     kind = wl["kind"]
     seq = kind in ("scan", "prefill")  # T tokens per launch, the state on-chip
     steps = args.steps if args.steps is not None else (3 if seq else 100)
@@ -367,6 +373,7 @@ def main():
             "launch": ("hipGraph replay of " if graph is not None else "back-to-back launches of ")
                       + f"{L} per-layer kernels per step",
             "parallelism": "single GPU",
+            **({"layers_reduced_from": WORKLOADS[args.workload]["layers"]} if args.layers is not None else {}),
         },
         "hbm_frac": round(value / HBM_PEAK_GBPS, 4),
         # a rotated workload times one layer on several state instances: each launch is one token

@@ -58,7 +58,9 @@
  *  - Every argument is validated before anything is enqueued; a rejected
  *    call returns a non-zero status, changes nothing and leaves a detail
  *    message for ssq_last_error().  Non-finite inputs are not checked: the
- *    codes they produce are unspecified.
+ *    codes, scales and outputs of the rows they reach (for the delta rule,
+ *    the matrices) are unspecified; the call completes and every other row
+ *    is computed as usual.
  *  - Kernels support row_len == 128, and rows_per_head a multiple of 16 for
  *    SSQ_MAMBA2, dk == 128 for SSQ_DELTA.
  */

@@ -220,3 +220,33 @@ def test_kda_layer_full_size_sampled_with_stochastic_rounding():
             assert np.array_equal(sub["code"], ost.code)
             assert np.array_equal(sub["scale"], ost.scale) and np.array_equal(sub["zero"], ost.zero)
         assert par.block_rel(og[mats], oo[0], axis=1) <= 1e-5
+
+
+@pytest.mark.parametrize("fmt", ["int8_asym", "int4_sym", "fp32"])
+def test_non_finite_inputs_stay_in_their_matrix(fmt):
+    """A NaN in v of one matrix and an infinite beta of another: the call completes, and every
+    other matrix matches the oracle run on clean inputs."""
+    B, H = 2, 3
+    rows = B * H * 128
+    say(f"delta non-finite fmt={fmt}")
+    init = synth.init_state(92, 0, rows, 128)
+    ost = oracle.make_state(fmt, rows, 128, init)
+    gst = par.new_gpu_state(ddesc(fmt, B, H))
+    par.write_gpu_state(gst, ost)
+    q, k, v, al, be = synth.delta_inputs(92, 0, B, H, 128, 128)
+    oo, _, vq = oracle.delta_step(ost, q, k, v, al, be, B, H, diag=True)
+    vb, beb = v.copy(), be.copy()
+    vb[0, 1, 7] = np.nan
+    beb[1, 2] = np.inf
+    og = run_delta(gst, q, k, vb, al, beb, ssq.SSQ_READ_POST_QUANT)
+    torch.cuda.synchronize()
+    okm = np.ones((B, H), bool)
+    okm[0, 1] = okm[1, 2] = False
+    okr = np.repeat(okm.reshape(-1), 128)
+    g = par.read_gpu_state(gst, fmt)
+    if fmt == "fp32":
+        assert par.block_rel(g["h"][okr], ost.h[okr]) <= 1e-5
+    else:
+        par.check_codes({kk: vv[okr] for kk, vv in g.items()}, ost.code[okr], ost.scale[okr], ost.zero[okr],
+                        vq[okr], fmt, "finite matrices")
+    assert par.block_rel(og[okm], oo[okm], axis=-1) <= 1e-5

@@ -347,6 +347,38 @@ def test_edge_shapes_and_zero_input():
         assert par.block_rel(yg, yo, axis=2) <= 1e-5
 
 
+@pytest.mark.parametrize("fmt", ["fp32", "int8_asym", "int4_asym", "int8_sym"])
+def test_non_finite_inputs_stay_in_their_rows(fmt):
+    """NaN and infinity in x (two rows) and an infinite dt (one head of one sequence): the call
+    completes, and every row those values do not reach matches the oracle run on clean inputs."""
+    B, H, G, P = 2, 4, 1, 16
+    rows = B * H * P
+    say(f"non-finite fmt={fmt}")
+    init = init_rows(44, 0, rows)
+    ost = oracle.make_state(fmt, rows, 128, init)
+    gst = par.new_gpu_state(m2desc(fmt, B, H, P, G))
+    par.write_gpu_state(gst, ost)
+    x, dt, Bm, Cm, A, D = synth.mamba2_step_inputs(44, 0, B, H, G, P, 128)
+    yo, _, vq = oracle.mamba2_step(ost, x, dt, A, Bm, Cm, D, diag=True)
+    xb, dtb = x.copy(), dt.copy()
+    xb[0, 1, 3] = np.nan
+    xb[1, 2, 5] = np.inf
+    dtb[1, 3] = np.inf
+    yg = run_step(gst, xb, dtb, A, Bm, Cm, D, ssq.SSQ_READ_POST_QUANT)
+    torch.cuda.synchronize()
+    bad = np.zeros((B, H, P), bool)
+    bad[0, 1, 3] = bad[1, 2, 5] = True
+    bad[1, 3, :] = True
+    ok = ~bad.reshape(-1)
+    g = par.read_gpu_state(gst, fmt)
+    if fmt == "fp32":
+        assert np.array_equal(g["h"][ok], ost.h[ok])
+    else:
+        par.check_codes({k: v[ok] for k, v in g.items()}, ost.code[ok], ost.scale[ok], ost.zero[ok], vq[ok], fmt,
+                        "finite rows")
+    assert par.block_rel(yg.reshape(-1)[ok], yo.reshape(-1)[ok]) <= 1e-5
+
+
 def test_repeat_runs_are_bit_identical():
     B, H, P, fmt = 4, 8, 64, "int4_asym"
     rows = B * H * P
