@@ -97,6 +97,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--seed", type=int, default=2)
+    ap.add_argument("--shared-state", action="store_true",
+                    help="diagnostic: every launch updates one state instance, which then stays in the "
+                         "last-level cache when it fits (separates the kernel's own time from HBM)")
     ap.add_argument("--layers", type=int, default=None,
                     help="fewer layers than the workload names (quick checks only; recorded in config)")
     return ap.parse_args()
@@ -164,7 +167,7 @@ def main():
     gen = torch.Generator(device=dev)
     gen.manual_seed(args.seed)
     states, storages = [], []
-    for layer in range(L):
+    for layer in range(1 if args.shared_state else L):
         storage = torch.empty(lay.total_bytes, dtype=torch.uint8, device=dev)
         if wl["init"] == "random":
             h = torch.randn(rows, N, generator=gen, device=dev)
@@ -179,6 +182,8 @@ def main():
             ssq.ssq_set_rounding(st, ssq.SSQ_ROUND_STOCHASTIC, args.seed * 1000 + layer, 0)
         states.append(st)
         storages.append(storage)
+    if args.shared_state:
+        states = states * L
     torch.cuda.synchronize()
 
     # ---------------- inputs (synth, seeded), resident in HBM ----------------
@@ -373,6 +378,7 @@ def main():
             "launch": ("hipGraph replay of " if graph is not None else "back-to-back launches of ")
                       + f"{L} per-layer kernels per step",
             "parallelism": "single GPU",
+            "state_instances": 1 if args.shared_state else L,
             **({"layers_reduced_from": WORKLOADS[args.workload]["layers"]} if args.layers is not None else {}),
         },
         "hbm_frac": round(value / HBM_PEAK_GBPS, 4),
