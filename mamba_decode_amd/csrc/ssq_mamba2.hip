@@ -39,6 +39,19 @@ __device__ __forceinline__ int64_t wave_id()
     return (int64_t)blockIdx.x * (blockDim.x >> 6) + w;
 }
 
+// Workgroups are dispatched to the 8 XCDs in turn (workgroup i to XCD i mod 8), each XCD with
+// its own L2.  Numbered this way instead, each XCD runs one contiguous range of rows, so the
+// waves of a sequence share an XCD and its L2 fetches that sequence's B and C once per token
+// rather than once per XCD.  A permutation of the waves: any grid stays correct.
+__device__ __forceinline__ int64_t wave_id_xcd_grouped()
+{
+    constexpr int kXcds = 8;
+    const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int64_t nb = gridDim.x, bid = blockIdx.x;
+    const int64_t lb = nb % kXcds == 0 ? (bid % kXcds) * (nb / kXcds) + bid / kXcds : bid;
+    return lb * (blockDim.x >> 6) + w;
+}
+
 // ---------------------------------------------------------------------------
 // one row, one token: dequantize, decay + write, refit, round, pack, read out.
 // ---------------------------------------------------------------------------
@@ -226,7 +239,8 @@ __global__ __launch_bounds__(256, W) void k_m2_step(M2Args a, int64_t it_base)
     constexpr int NS = Tr::quant ? NW : E; // registers per slot for the row's words
     constexpr int DD = D < K ? D : K;
     const int lane = threadIdx.x & 63, sub = lane / LPR, part = lane % LPR;
-    const int64_t it0 = it_base + wave_id() * K;
+    const int64_t it0 = it_base + wave_id() * K; // round-robin over the XCDs: grouping the
+    // decode's workgroups by XCD (as the scan does) made it 7-8% slower
     if (it0 + K > a.total_iters) return;
 
     const int ipH = a.P / RPW; // iterations per head (RPW divides P)
@@ -399,7 +413,7 @@ __global__ __launch_bounds__(256, PRE ? SSQ_SCAN_WAVES - 1 : SSQ_SCAN_WAVES) voi
     constexpr int PITCH = RS::LDS_PITCH, LDSF = RS::LDS_FLOATS;
     __shared__ float4 bc_lds[4 * 2 * 2 * LDSF / 4]; // [wave][buffer][B, C][LDSF]
     const int lane = threadIdx.x & 63, sub = lane / LPR, part = lane % LPR;
-    const int64_t it = wave_id();
+    const int64_t it = wave_id_xcd_grouped();
     if (it >= a.total_iters) return;
     const int64_t row0 = it * RPW;
     const int64_t bh = row0 / a.P;
@@ -522,7 +536,7 @@ __global__ __launch_bounds__(256, PRE ? SSQ_PREFILL_WAVES - 1 : SSQ_PREFILL_WAVE
     constexpr int PITCH = RS::LDS_PITCH, LDSF = RS::LDS_FLOATS;
     __shared__ float4 bc_lds[4 * 2 * 2 * LDSF / 4]; // [wave][buffer][B, C][LDSF]
     const int lane = threadIdx.x & 63, sub = lane / LPR, part = lane % LPR;
-    const int64_t it = wave_id();
+    const int64_t it = wave_id_xcd_grouped();
     if (it >= a.total_iters) return;
     const int64_t row0 = it * RPW;
     const int64_t bh = row0 / a.P;
