@@ -56,7 +56,7 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_delta_step(DeltaArgs a
     constexpr int NS = NW; // registers per row part (packed codes, or fp32 values)
     constexpr int ROWB = Tr::quant ? 128 * Tr::bits / 8 : 512;
     __shared__ double part_u[RG * kPartPitch]; // reused for the fp32 partials of o
-    __shared__ float u_s[128];
+    __shared__ float w_s[128];
 
     const int t = threadIdx.x;
     const int rg = t >> 3, part = t & 7, j0 = part * E;
@@ -93,8 +93,8 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_delta_step(DeltaArgs a
             for (int e = 0; e < E; ++e) f[e] = __uint_as_float(cw[r][e]);
         }
     };
-    float vv[E];
-    load_f32<E>(a.v + mrow0 + j0, vv);
+    // column t's value of v, for the threads that form w_t
+    const float vcol = t < 128 ? a.v[mrow0 + t] : 0.0f;
 
     // u = k^T S in double: sum_i kap_i*c_ij - sum_i kap_i*z_i with kap_i = k_i*s_i exact
     // (quantized), or sum_i k_i*S_ij (fp32); the z term is the same for every column.
@@ -130,18 +130,18 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_delta_step(DeltaArgs a
         double acc = 0.0;
 #pragma unroll 8
         for (int r = 0; r < RG; ++r) acc += part_u[part_idx(r, t)];
-        u_s[t] = (float)acc;
+        // w_t = beta*(v_t - alpha*u_t), or beta*(v_t - u_t) for KDA (the decay is
+        // already in u), formed once per column and shared
+        const float u = (float)acc;
+        const float au = KDA ? u : alpha * u;
+        const float vm = vcol - au;
+        w_s[t] = beta * vm;
     }
     __syncthreads();
 
-    // w = beta*(v - alpha*u), or beta*(v - u) for KDA (the decay is already in u)
     float ww[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const float au = KDA ? u_s[j0 + e] : alpha * u_s[j0 + e];
-        const float vm = vv[e] - au;
-        ww[e] = beta * vm;
-    }
+    for (int e = 0; e < E; ++e) ww[e] = w_s[j0 + e];
 
     // S' = alpha*S + k w^T, row by row; refit, round and store each row
     float op[E];
@@ -347,8 +347,7 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_damp_step(DeltaArgs a)
     constexpr int F = INT8_ASYM;
     constexpr int LPR = 8, E = 16, RG = 32, KR = 4, NW = 4, ROWB = 128;
     __shared__ double part_u[RG * kPartPitch]; // reused for the fp32 partials of the readout
-    __shared__ float u_s[128];
-    __shared__ float vt_s[128];
+    __shared__ float w_s[128];
     __shared__ double xch[128];
 
     const int t = threadIdx.x;
@@ -389,11 +388,8 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_damp_step(DeltaArgs a)
             unpack_codes<F, E>(cw[r], f);
         }
     };
-    // vt = Hs v, rounded once
-    {
-        const double x = wht128(vj, xch);
-        if (t < 128) vt_s[t] = (float)(x * 0.0625);
-    }
+    // vt = Hs v, rounded once; thread t < 128 holds column t
+    const float vt = (float)(wht128(vj, xch) * 0.0625);
 
     // ut = k^T St in double: half rows contribute k_i*St_ij, uint8 rows kap_i*(c_ij - z_i)
     {
@@ -419,18 +415,16 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_damp_step(DeltaArgs a)
         double acc = 0.0;
 #pragma unroll 8
         for (int r = 0; r < RG; ++r) acc += part_u[part_idx(r, t)];
-        u_s[t] = (float)acc;
+        // wt = beta*(vt - alpha*ut), formed once per column and shared
+        const float au = alpha * (float)acc;
+        const float vm = vt - au;
+        w_s[t] = beta * vm;
     }
     __syncthreads();
 
-    // wt = beta*(vt - alpha*ut)
     float ww[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const float au = alpha * u_s[j0 + e];
-        const float vm = vt_s[j0 + e] - au;
-        ww[e] = beta * vm;
-    }
+    for (int e = 0; e < E; ++e) ww[e] = w_s[j0 + e];
 
     float op[E];
 #pragma unroll
