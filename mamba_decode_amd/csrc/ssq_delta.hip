@@ -39,6 +39,25 @@ __device__ __forceinline__ void store_row_piece(uint8_t* rows_base, uint32_t row
     buf_store_words<NW, kAuxStoreWhole>(make_rsrc(rows_base, rows_bytes), off, 0u, w);
 }
 
+// Exact kap*c in one fma for an unsigned integer code c.  The code's bits as the low word of a
+// double (high word zero) read as the subnormal c*2^-1074, so fma(kap*2^562, that, acc*2^-512)
+// is the exact sum kap*c + acc scaled by 2^-512.  kap is a product of at most three fp32 values
+// (k, the decay, the scale), so it lies below 2^384 (kap*2^562 stays finite) and is a multiple
+// of 2^-447, and so is every exact product and sum of the accumulation; scaled, each is zero or
+// at least 2^-959, in the normal range, where rounding commutes with a power-of-two scaling.
+// The accumulation therefore rounds exactly as fma(kap, (double)c, acc) does, for every finite
+// input, and saves the code's conversion to double.
+constexpr double kSubScale = 0x1p562, kSubUnscale = 0x1p512;
+// Code e (0-based, in unpacking order) of a row part held as packed BITS-wide fields
+template <int BITS>
+__device__ __forceinline__ double code_as_subnormal(const uint32_t* w, int e)
+{
+    static_assert(BITS == 4 || BITS == 8, "packed codes");
+    constexpr int per = 32 / BITS;
+    const uint32_t c = (w[e / per] >> (BITS * (e % per))) & ((1u << BITS) - 1u);
+    return __builtin_bit_cast(double, (uint64_t)c);
+}
+
 // Partial rows in LDS: element j of row group r sits at r*kPartPitch + j + j/16.  A wave
 // writes 8 row groups x 8 segments of 16 columns at once; without the padding every lane
 // of it lands on the same bank.
@@ -107,20 +126,31 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_delta_step(DeltaArgs a
             kaps[r] = Tr::quant ? kd * (double)s_old[r] : kd;
         }
         double up[E];
-        double zt = 0.0;
         if constexpr (Tr::asym) {
+            double zt = 0.0;
 #pragma unroll
             for (int r = 0; r < KR; ++r) zt = __builtin_fma(kaps[r], (double)z_old[r], zt);
-        }
+            // unsigned codes: the same sums 2^512 lower, without converting the codes (the
+            // column sums are scaled back once they are complete)
 #pragma unroll
-        for (int e = 0; e < E; ++e) up[e] = -zt;
+            for (int e = 0; e < E; ++e) up[e] = -zt * (1.0 / kSubUnscale);
 #pragma unroll
-        for (int r = 0; r < KR; ++r) {
-            const double kap = kaps[r];
-            float f[E];
-            row_values(r, f);
+            for (int r = 0; r < KR; ++r) {
+                const double K = kaps[r] * kSubScale;
 #pragma unroll
-            for (int e = 0; e < E; ++e) up[e] = __builtin_fma(kap, (double)f[e], up[e]);
+                for (int e = 0; e < E; ++e) up[e] = __builtin_fma(K, code_as_subnormal<Tr::bits>(cw[r], e), up[e]);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e) up[e] = 0.0;
+#pragma unroll
+            for (int r = 0; r < KR; ++r) {
+                const double kap = kaps[r];
+                float f[E];
+                row_values(r, f);
+#pragma unroll
+                for (int e = 0; e < E; ++e) up[e] = __builtin_fma(kap, (double)f[e], up[e]);
+            }
         }
 #pragma unroll
         for (int e = 0; e < E; ++e) part_u[part_idx(rg, j0 + e)] = up[e];
@@ -132,7 +162,7 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_delta_step(DeltaArgs a
         for (int r = 0; r < RG; ++r) acc += part_u[part_idx(r, t)];
         // w_t = beta*(v_t - alpha*u_t), or beta*(v_t - u_t) for KDA (the decay is
         // already in u), formed once per column and shared
-        const float u = (float)acc;
+        const float u = (float)(Tr::asym ? acc * kSubUnscale : acc);
         const float au = KDA ? u : alpha * u;
         const float vm = vcol - au;
         w_s[t] = beta * vm;
@@ -397,15 +427,23 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_damp_step(DeltaArgs a)
         double zt = 0.0;
 #pragma unroll
         for (int r = 0; r < KR; ++r) zt = __builtin_fma((double)kk[r] * (double)s_old[r], (double)z_old[r], zt);
+        // the uint8 rows' codes as subnormals, the sums 2^512 lower until the column sums are done
 #pragma unroll
-        for (int e = 0; e < E; ++e) up[e] = -zt;
+        for (int e = 0; e < E; ++e) up[e] = -zt * (1.0 / kSubUnscale);
 #pragma unroll
         for (int r = 0; r < KR; ++r) {
             const double kap = (double)kk[r] * (double)s_old[r];
-            float f[E];
-            row_values(r, f);
+            if (r == 0 && hi_wave) {
+                const double kh = kap * (1.0 / kSubUnscale);
+                float f[E];
+                row_values(r, f);
 #pragma unroll
-            for (int e = 0; e < E; ++e) up[e] = __builtin_fma(kap, (double)f[e], up[e]);
+                for (int e = 0; e < E; ++e) up[e] = __builtin_fma(kh, (double)f[e], up[e]);
+            } else {
+                const double K = kap * kSubScale;
+#pragma unroll
+                for (int e = 0; e < E; ++e) up[e] = __builtin_fma(K, code_as_subnormal<8>(cw[r], e), up[e]);
+            }
         }
 #pragma unroll
         for (int e = 0; e < E; ++e) part_u[part_idx(rg, j0 + e)] = up[e];
@@ -416,7 +454,7 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_damp_step(DeltaArgs a)
 #pragma unroll 8
         for (int r = 0; r < RG; ++r) acc += part_u[part_idx(r, t)];
         // wt = beta*(vt - alpha*ut), formed once per column and shared
-        const float au = alpha * (float)acc;
+        const float au = alpha * (float)(acc * kSubUnscale);
         const float vm = vt - au;
         w_s[t] = beta * vm;
     }

@@ -78,6 +78,37 @@ def test_delta_step_teacher_forced(fmt, readout):
         assert par.block_rel(og, oo, axis=2) <= 1e-5, t
 
 
+@pytest.mark.parametrize("kda", [False, True])
+@pytest.mark.parametrize("fmt", ["int8_asym", "int4_asym"])
+@pytest.mark.parametrize("mag", [2.0 ** -118, 2.0 ** 100])
+def test_delta_step_far_from_unit_scale(mag, fmt, kda):
+    """States, v and part of k far from unit size: the products k_i*s_i*c_ij of u sit near
+    2^-130 or 2^100 and some keys are tiny, which the codes-as-subnormal accumulation of u
+    must round exactly as the plain one."""
+    B, H = 2, 2
+    rows = B * H * 128
+    init = (synth.init_state(98, 0, rows, 128).astype(np.float64) * mag).astype(np.float32)
+    ost = oracle.make_state(fmt, rows, 128, init)
+    gst = par.new_gpu_state(ddesc(fmt, B, H))
+    q, k, v, al, be = synth.delta_inputs(98, 0, B, H, 128, 128)
+    v = (v.astype(np.float64) * mag).astype(np.float32)
+    k = k.copy()
+    k.reshape(B * H, 128)[:, ::5] *= np.float32(2.0 ** -60)
+    say(f"delta far from unit scale mag=2^{int(np.log2(mag))} fmt={fmt} kda={kda}")
+    par.write_gpu_state(gst, ost)
+    if kda:
+        al = synth.kda_alpha(98, 0, B, H, 128)
+        og = run_kda(gst, q, k, v, al, be, ssq.SSQ_READ_POST_QUANT)
+        oo, _, vq = oracle.kda_step(ost, q, k, v, al, be, B, H, readout="post", diag=True)
+    else:
+        og = run_delta(gst, q, k, v, al, be, ssq.SSQ_READ_POST_QUANT)
+        oo, _, vq = oracle.delta_step(ost, q, k, v, al, be, B, H, readout="post", diag=True)
+    g = par.read_gpu_state(gst, fmt)
+    assert np.all(np.isfinite(ost.scale)) and np.all(ost.scale > 0)
+    par.check_codes(g, ost.code, ost.scale, ost.zero, vq, fmt, "far from unit scale")
+    assert par.block_rel(og, oo, axis=2) <= 1e-5
+
+
 def test_delta_identity_and_decay_on_gpu():
     """alpha = beta = 1 with unit k writes v at key k (fp32 state); beta = 0 is a pure decay
     that keeps the codes of full-range rows."""
