@@ -223,7 +223,7 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_delta_step(DeltaArgs a
             float f[E];
             // stochastic rounding: this lane's first counter, (step*rows + row)*128 + j0
             const uint64_t ctr0 = SR ? ((a.sr.step * (uint64_t)a.sr.rows + (uint64_t)row) * 128u + (uint64_t)j0) : 0;
-            if (__all(refit_fast<F>(mn, mx, am, g))) {
+            if (__all(refit_fast<F, SR>(mn, mx, am, g))) {
                 if constexpr (SR) {
                     round_codes_sr<F, E, true>(S, g, a.sr.seed, ctr0, f);
                 } else {
@@ -519,7 +519,7 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_damp_step(DeltaArgs a)
             RowGrid g;
             float f[E];
             const uint64_t ctr0 = SR ? ((a.sr.step * (uint64_t)a.sr.rows + (uint64_t)lrow) * 128u + (uint64_t)j0) : 0;
-            if (__all(refit_fast<F>(mn, mx, 0.0f, g))) {
+            if (__all(refit_fast<F, SR>(mn, mx, 0.0f, g))) {
                 if constexpr (SR) {
                     round_codes_sr<F, E, true>(S, g, a.sr.seed, ctr0, f);
                 } else {

@@ -351,6 +351,25 @@ __device__ __forceinline__ uint64_t splitmix_mix(uint64_t x)
 // every term an exact integer in double.  FAST (the refit fast path: |z| < 2^21, so
 // |p| < 2^22) uses the equal form floor((floor(2^16 p) + K) / 2^16), exact while
 // |p| < 2^37, and finishes in fp32 with the row's 1.5*2^23 + z.
+//
+// Asymmetric rows on the fast path decide in fp32 instead.  With A = 2^16 inv and
+// Kz = K + 2^16 z (an integer below 2^24 in magnitude, so exact), X = h*A + Kz is
+// 2^16 (h inv + z + K/2^16) exactly and v = fma(h, A, Kz) rounds it once.  Multiples of
+// 2^16 are representable, so rounding never carries X across one: floor(X / 2^16) =
+// floor(v / 2^16), except when v is itself a multiple of 2^16 that X lies just below;
+// an entry with such a v (on the fast path about one in 2^14 or fewer) is decided in
+// double.  |z| <= 255 keeps Kz within 2^24 (sr_f32_ok); other rows take the general path.
+// (A v too small for v/2^16 to be exact can only occur for codes -1 and 0, which the
+// clamp maps to 0 alike.)
+template <int F>
+__device__ __forceinline__ bool sr_f32_ok(const RowGrid& g)
+{
+    if constexpr (Traits<F>::asym)
+        return fabsf(g.z) <= 255.0f;
+    else
+        return true;
+}
+
 template <int F, int E, bool FAST>
 __device__ __forceinline__ void round_codes_sr(const float* h, const RowGrid& g, uint64_t seed, uint64_t ctr0,
                                                float* f)
@@ -358,7 +377,10 @@ __device__ __forceinline__ void round_codes_sr(const float* h, const RowGrid& g,
     static_assert(E % 4 == 0, "four uniforms per generator output");
     constexpr float flo = kMagic + (float)Traits<F>::lo;
     constexpr float fhi = kMagic + (float)Traits<F>::hi;
+    constexpr bool F32 = FAST && Traits<F>::asym;
     const double inv16 = (double)g.inv * 65536.0;
+    const float A = g.inv * 65536.0f;                 // exact
+    const float zk = g.z * 65536.0f - 8388608.0f;     // 2^16 z - 2^23, a multiple of 2^16: exact
     uint64_t x = seed + ((ctr0 >> 2) + 1) * kGoldenGamma;
 #pragma unroll
     for (int q = 0; q < E / 4; ++q) {
@@ -369,11 +391,23 @@ __device__ __forceinline__ void round_codes_sr(const float* h, const RowGrid& g,
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int e = 4 * q + k;
-            const double P = (double)h[e] * inv16; // 2^16 h inv, exact
-            if constexpr (FAST) {
+            if constexpr (F32) {
+                const float Kz = __uint_as_float(K[k] | 0x4B000000u) + zk; // (2^23 + K) + zk, exact
+                const float v = __builtin_fmaf(h[e], A, Kz);
+                const float y = v * (1.0f / 65536.0f);
+                float m = floorf(y);
+                if (__builtin_expect(y == m, 0)) {
+                    // v a multiple of 2^16: this entry is decided in double (f may alias h)
+                    const double P = (double)h[e] * inv16; // 2^16 h inv, exact
+                    m = (float)floor((floor(P) + (double)K[k]) * (1.0 / 65536.0)) + g.z;
+                }
+                f[e] = __builtin_amdgcn_fmed3f(m + kMagic, flo, fhi);
+            } else if constexpr (FAST) {
+                const double P = (double)h[e] * inv16; // 2^16 h inv, exact
                 const double c = floor((floor(P) + (double)K[k]) * (1.0 / 65536.0));
                 f[e] = __builtin_amdgcn_fmed3f((float)c + g.Mz, flo, fhi);
             } else {
+                const double P = (double)h[e] * inv16; // 2^16 h inv, exact
                 const double fl = floor((double)h[e] * (double)g.inv);
                 const double t = __builtin_fma(-65536.0, fl, floor(P));
                 double c = fl + (double)g.zc + (t + (double)K[k] >= 65536.0 ? 1.0 : 0.0);
@@ -411,7 +445,8 @@ __device__ __forceinline__ float recip_rn(float s)
     return __builtin_fmaf(__builtin_fmaf(-s, y, 1.0f), y, y);
 }
 
-template <int F>
+// SR: the row is also rounded stochastically, which on this path needs sr_f32_ok
+template <int F, bool SR = false>
 __device__ __forceinline__ bool refit_fast(float mn, float mx, float amax, RowGrid& g)
 {
     constexpr float lo_ok = 7.88860905e-31f; // 2^-100
@@ -430,7 +465,7 @@ __device__ __forceinline__ bool refit_fast(float mn, float mx, float amax, RowGr
         g.Mr = g.Mz;
         const float top = __builtin_fmaf(mx, inv, g.Mz);
         return range >= lo_ok && range <= hi_ok && fabsf(z) < kSlowZero &&
-               top <= kMagic + (float)Traits<F>::hi;
+               top <= kMagic + (float)Traits<F>::hi && (!SR || sr_f32_ok<F>(g));
     } else {
         const float s = div_by_const<Traits<F>::hi>(amax);
         const float inv = recip_rn(s);

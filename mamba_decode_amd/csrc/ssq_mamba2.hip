@@ -128,7 +128,7 @@ struct RowStep {
             am = group_max<LPR>(am);
         }
         // h becomes f = 1.5*2^23 + code in place
-        if (__all(refit_fast<F>(mn, mx, am, g))) {
+        if (__all(refit_fast<F, SR>(mn, mx, am, g))) {
             // every row of the wave is inside the verified ranges and needs no clamp
             if constexpr (SR) {
                 round_codes_sr<F, E, true>(h, g, sr_seed, ctr0, h);
@@ -186,7 +186,7 @@ struct RowStep {
             for (int e = 0; e < E; ++e) am = fmaxf(am, fabsf(h[e]));
             am = group_max<LPR>(am);
         }
-        if (__all(refit_fast<F>(mn, mx, am, g))) {
+        if (__all(refit_fast<F, SR>(mn, mx, am, g))) {
             if constexpr (SR) {
                 round_codes_sr<F, E, true>(h, g, sr_seed, ctr0, h);
             } else {
