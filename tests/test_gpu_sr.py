@@ -61,6 +61,47 @@ def test_decode_step_stochastic_teacher_forced(fmt, readout):
         assert ssq.ssq_get_rounding(gst) == (ssq.SSQ_ROUND_STOCHASTIC, seed, step0 + t + 1)
 
 
+def _rows_with_zero_points(zs, qa, per, n_rows, seed):
+    """Rows spanning [-z/qa, 1 - z/qa] (range 1, so the grid's zero point is z), `per` rows for
+    each z, the remaining rows seeded random."""
+    rng = np.random.default_rng(seed)
+    rows = synth.init_state(seed, 0, n_rows, 128).astype(np.float64)
+    k = 0
+    for z in zs:
+        for _ in range(per):
+            u = rng.permutation(np.linspace(0.0, 1.0, 128))
+            rows[k] = -z / qa + u
+            k += 1
+    return rows.astype(np.float32)
+
+
+@pytest.mark.parametrize("fmt", ["int4_asym", "int8_asym"])
+def test_decode_stochastic_zero_points_around_the_fp32_bound(fmt):
+    """Asymmetric rows decide stochastic rounding in fp32 while |z| <= 255 and take the
+    general path beyond; rows with zero points on both sides of that bound and at it.  x = 0
+    keeps each row's zero point through the step (the update only decays the row)."""
+    qa = 15 if fmt == "int4_asym" else 255
+    zs = [-300, -256, -255, -254, -40, 0, 3, 127, 200, 254, 255, 256, 300, 1000]
+    B, H, G, P = 1, 4, 1, 64
+    rows = B * H * P
+    seed, step0 = 4242, 3
+    init = _rows_with_zero_points(zs, qa, 12, rows, 64)
+    ost = oracle.make_state(fmt, rows, 128, init)
+    assert set(zs) <= set(np.unique(ost.zero).astype(int))
+    gst = par.new_gpu_state(ssq.make_desc(ssq.SSQ_MAMBA2, fmt, B, H, P, 128, G))
+    ssq.ssq_set_rounding(gst, ssq.SSQ_ROUND_STOCHASTIC, seed, step0)
+    for t in range(3):
+        say(f"stochastic decode around |z| = 255 fmt={fmt} t={t}")
+        x, dt, Bm, Cm, A, D = synth.mamba2_step_inputs(64, 1, B, H, G, P, 128, t=t)
+        x[:] = 0.0
+        par.write_gpu_state(gst, ost)
+        y = torch.empty(x.shape, dtype=torch.float32, device="cuda")
+        ssq.ssq_decode_step(gst, par.dev(x), par.dev(dt), par.dev(A), par.dev(Bm), par.dev(Cm), par.dev(D), y)
+        yo = oracle.mamba2_step(ost, x, dt, A, Bm, Cm, D, sr=(seed, step0 + t))
+        _same_state(par.read_gpu_state(gst, fmt), ost, f"t={t}")
+        assert par.block_rel(y.cpu().numpy(), yo, axis=2) <= 1e-5, t
+
+
 @pytest.mark.parametrize("fmt", ["int8_asym", "int4_asym", "int8_sym"])
 def test_scan_stochastic_equals_steps_and_oracle(fmt):
     B, H, G, P, T = 2, 4, 1, 16, 20
