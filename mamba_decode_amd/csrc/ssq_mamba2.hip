@@ -71,6 +71,8 @@ struct RowStep {
         }
         __device__ __forceinline__ float b(int e) const { return B[e]; }
         __device__ __forceinline__ float c(int e) const { return C[e]; }
+        __device__ __forceinline__ float4 b4(int q) const { return make_float4(B[4 * q], B[4 * q + 1], B[4 * q + 2], B[4 * q + 3]); }
+        __device__ __forceinline__ float4 c4(int q) const { return make_float4(C[4 * q], C[4 * q + 1], C[4 * q + 2], C[4 * q + 3]); }
     };
     // ... or in LDS: the wave's copy of B and C, E entries per lane group, rows of E + 4
     // floats so that the LPR groups' 16-byte reads fall in different banks
@@ -81,6 +83,10 @@ struct RowStep {
         const float* Cp;
         __device__ __forceinline__ float b(int e) const { return Bp[e]; }
         __device__ __forceinline__ float c(int e) const { return Cp[e]; }
+        // four entries with one 16-byte read: written out, so that no inline asm in a loop
+        // that uses them keeps the compiler from merging the reads
+        __device__ __forceinline__ float4 b4(int q) const { return reinterpret_cast<const float4*>(Bp)[q]; }
+        __device__ __forceinline__ float4 c4(int q) const { return reinterpret_cast<const float4*>(Cp)[q]; }
     };
 
     // quantized formats: the old codes as floats (h, overwritten) in -> the new packed codes
@@ -208,12 +214,18 @@ struct RowStep {
     template <typename In>
     __device__ __forceinline__ static float run_f(float* hv, float lam, float w, float dx, const In& in)
     {
+        // h = fma(lambda, h, w*B) written into h's own register (fma_in_place): the
+        // compiler's own form accumulates into w*B's register and copies every entry back
         float acc = 0.0f;
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const float wb = w * in.b(e);
-            hv[e] = __builtin_fmaf(lam, hv[e], wb);
-            acc = __builtin_fmaf(in.c(e), hv[e], acc);
+        for (int q = 0; q < E / 4; ++q) {
+            const float4 b = in.b4(q), c = in.c4(q);
+            const float bb[4] = {b.x, b.y, b.z, b.w}, cc[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                fma_in_place(lam, hv[4 * q + k], w * bb[k]);
+                acc = __builtin_fmaf(cc[k], hv[4 * q + k], acc);
+            }
         }
         return group_sum<LPR>(acc) + dx;
     }
@@ -592,9 +604,11 @@ __global__ __launch_bounds__(256, PRE ? SSQ_PREFILL_WAVES - 1 : SSQ_PREFILL_WAVE
         const float w = dtv * xv;
         const float dx = Dh * xv;
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const float wb = w * in.b(e);
-            fma_in_place(lam, hv[e], wb);
+        for (int q = 0; q < E / 4; ++q) {
+            const float4 b = in.b4(q);
+            const float bb[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) fma_in_place(lam, hv[4 * q + k], w * bb[k]);
         }
         const bool end = (t + 1) % chunk == 0 || t == T - 1; // wave-uniform
         float acc = 0.0f;
