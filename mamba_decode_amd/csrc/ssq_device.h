@@ -539,6 +539,7 @@ constexpr int kRsrcWord3 = 0x00020000; // gfx9 family: 32-bit data format, no sw
 constexpr int kAuxLoad = SSQ_NT_LD ? 2 : 0; // the non-temporal hint on state loads
 constexpr int kAuxStore = SSQ_STORE_POLICY;
 constexpr int kAuxStoreWhole = SSQ_STORE_POLICY_WHOLE;
+constexpr int kAuxStoreSc1 = 16; // write-through alone: y of a decode iteration of 16 rows
 
 __device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes)
 {

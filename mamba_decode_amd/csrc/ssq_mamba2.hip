@@ -379,7 +379,9 @@ __global__ __launch_bounds__(256, W) void k_m2_step(M2Args a, int64_t it_base)
             buf_store_words<NW, AUXS>(r_w, off_w, sw, ow);
             buf_store_f32<AUXS>(g.s, r_s, off_r, sr);
             if constexpr (Tr::asym) buf_store_f32<AUXS>(g.z, r_z, off_r, sr);
-            buf_store_f32<0>(yv, r_y, off_r, sr);
+            // y of 16 rows is one whole 64-byte segment: written through (sc1); 8 rows'
+            // 32 bytes go without a hint
+            buf_store_f32<RPW == 16 ? kAuxStoreSc1 : 0>(yv, r_y, off_r, sr);
         } else {
             float yv;
             if constexpr (BCL) yv = RS::run_f(cf, lam, w, dx, rin_l);
