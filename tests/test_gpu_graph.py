@@ -89,3 +89,40 @@ def test_scan_in_a_graph():
     st.storage.copy_(start)
     g = _capture(lambda: ssq.ssq_scan(st, T, x, dt, A, Bm, Cm, D, y))
     _check_replays(st, start, eager_state, eager_y, y, g, "scan")
+
+
+def test_prefill_in_a_graph():
+    B, H, P, T, chunk = 2, 4, 64, 40, 16
+    rows = B * H * P
+    say("graph prefill")
+    st = par.new_gpu_state(ssq.make_desc(ssq.SSQ_MAMBA2, "int8_asym", B, H, P), synth.init_state(74, 0, rows, 128))
+    x, dt, Bm, Cm, A, D = (par.dev(a) for a in synth.mamba2_scan_inputs(74, 0, B, T, H, 1, P, 128))
+    y = torch.empty(x.shape, dtype=torch.float32, device="cuda")
+    start = st.storage.clone()
+    ssq.ssq_prefill(st, T, chunk, x, dt, A, Bm, Cm, D, y)
+    torch.cuda.synchronize()
+    eager_state, eager_y = st.storage.clone(), y.clone()
+    st.storage.copy_(start)
+    g = _capture(lambda: ssq.ssq_prefill(st, T, chunk, x, dt, A, Bm, Cm, D, y))
+    _check_replays(st, start, eager_state, eager_y, y, g, "prefill")
+
+
+def test_stochastic_decode_in_a_graph():
+    """The counter of stochastic rounding is an argument fixed at capture: every replay draws
+    the uniforms of the token it was captured with."""
+    B, H, P = 4, 8, 64
+    rows = B * H * P
+    seed, step0 = 777, 5
+    say("graph stochastic decode")
+    st = par.new_gpu_state(ssq.make_desc(ssq.SSQ_MAMBA2, "int4_asym", B, H, P), synth.init_state(75, 0, rows, 128))
+    x, dt, Bm, Cm, A, D = (par.dev(a) for a in synth.mamba2_step_inputs(75, 0, B, H, 1, P, 128))
+    y = torch.empty(x.shape, dtype=torch.float32, device="cuda")
+    start = st.storage.clone()
+    ssq.ssq_set_rounding(st, ssq.SSQ_ROUND_STOCHASTIC, seed, step0)
+    g = _capture(lambda: ssq.ssq_decode_step(st, x, dt, A, Bm, Cm, D, y))  # warm call: step0, captured: step0 + 1
+    st.storage.copy_(start)
+    ssq.ssq_set_rounding(st, ssq.SSQ_ROUND_STOCHASTIC, seed, step0 + 1)
+    ssq.ssq_decode_step(st, x, dt, A, Bm, Cm, D, y)
+    torch.cuda.synchronize()
+    eager_state, eager_y = st.storage.clone(), y.clone()
+    _check_replays(st, start, eager_state, eager_y, y, g, "stochastic decode")
