@@ -102,6 +102,8 @@ def parse():
                          "last-level cache when it fits (separates the kernel's own time from HBM)")
     ap.add_argument("--layers", type=int, default=None,
                     help="fewer layers than the workload names (quick checks only; recorded in config)")
+    ap.add_argument("--batch", type=int, default=None,
+                    help="another batch size than the workload names (a sweep over batch; recorded in config)")
     return ap.parse_args()
 
 
@@ -141,6 +143,10 @@ def main():
         if args.layers < 1:
             raise SystemExit("--layers must be positive")
         wl["layers"] = args.layers
+    if args.batch is not None:
+        if args.batch < 1:
+            raise SystemExit("--batch must be positive")
+        wl["B"] = args.batch
     kind = wl["kind"]
     seq = kind in ("scan", "prefill")  # T tokens per launch, the state on-chip
     steps = args.steps if args.steps is not None else (3 if seq else 100)
@@ -354,7 +360,7 @@ def main():
     tpath = os.path.join(ROOT, "profiles", "traffic.json")
     if os.path.exists(tpath):
         tr = json.load(open(tpath)).get(args.workload)
-        if tr and tr.get("src_hash") == src_hash(kind):
+        if tr and tr.get("src_hash") == src_hash(kind) and args.batch is None:
             traffic = tr.get("hbm_bytes_per_launch")
 
     rec = {
@@ -380,6 +386,7 @@ def main():
             "parallelism": "single GPU",
             "state_instances": 1 if args.shared_state else L,
             **({"layers_reduced_from": WORKLOADS[args.workload]["layers"]} if args.layers is not None else {}),
+            **({"batch_changed_from": WORKLOADS[args.workload]["B"]} if args.batch is not None else {}),
         },
         "hbm_frac": round(value / HBM_PEAK_GBPS, 4),
         # a rotated workload times one layer on several state instances: each launch is one token
