@@ -192,9 +192,12 @@ ssq_status ssq_state_info(const ssq_state *state, ssq_desc *desc, void **storage
  * ctr/4 + 1 for `seed` (Steele, Lea and Flood, "Fast splittable pseudorandom
  * number generators", OOPSLA 2014), rows = the state's rows (for the two-tier
  * state, its uint8 rows).
- * `step` is the token the next call starts at: ssq_decode_step and
- * ssq_delta_step use it and advance it by one, ssq_scan uses step .. step+T-1
- * and advances it by T, at enqueue time.  A captured graph replays the tokens
+ * `step` is the token the next call starts at: in SSQ_ROUND_STOCHASTIC mode
+ * ssq_decode_step and ssq_delta_step use it and advance it by one, ssq_scan
+ * uses step .. step+T-1 and advances it by T, at enqueue time (round to
+ * nearest leaves it as it is).  The storage bytes plus this mode, seed and
+ * step are all a state holds: restored into new storage under a new handle
+ * they continue bit for bit.  A captured graph replays the tokens
  * it was captured with.  The fp32 state is never rounded:
  * SSQ_ROUND_STOCHASTIC on it gives SSQ_ERR_UNSUPPORTED.  Host-side only:
  * changes nothing already enqueued. */
