@@ -108,9 +108,11 @@ def bind(path: str):
 
 
 def lib():
+    """The oracle library: the build next to the source, or the build of the same source
+    named by the environment variable SSQ_ORACLE_LIB (the tests' sanitized build)."""
     global _lib
     if _lib is None:
-        _lib = bind(build())
+        _lib = bind(os.environ.get("SSQ_ORACLE_LIB") or build())
     return _lib
 
 
