@@ -287,8 +287,10 @@ ssq_status ssq_dequant(const ssq_state *state, float *out, void *stream);
  * SSQ_ERR_INVALID_ARG before anything is enqueued.  The caller owns both buffers. */
 ssq_status ssq_stream_copy(void *dst, const void *src, size_t bytes, void *stream);
 
-/* Static text for a status code. */
-const char *ssq_status_string(ssq_status status);
+/* Static text for a status code (an ssq_status value); any other value gives
+ * "unknown ssq_status".  Taken as int32_t so that an out-of-range code is an
+ * ordinary argument, not an invalid enum value. */
+const char *ssq_status_string(int32_t status);
 
 /* Detail of the last failed call on this thread ("" if none). */
 const char *ssq_last_error(void);

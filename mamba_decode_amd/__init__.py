@@ -17,7 +17,8 @@ import os
 import torch  # imported first: the library binds to the HIP runtime torch has loaded
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libssq.so")
+# SSQ_LIBRARY names another build of the same sources (the host tests' sanitized build)
+LIB_PATH = os.environ.get("SSQ_LIBRARY") or os.path.join(_HERE, "libssq.so")
 
 # ssq_status
 SSQ_OK, SSQ_ERR_INVALID_ARG, SSQ_ERR_UNSUPPORTED, SSQ_ERR_KIND_MISMATCH, SSQ_ERR_ALLOC, SSQ_ERR_DEVICE = range(6)
@@ -82,7 +83,7 @@ def _load():
     L.ssq_dequant.restype = st
     L.ssq_stream_copy.argtypes = [vp, vp, ctypes.c_size_t, vp]
     L.ssq_stream_copy.restype = st
-    L.ssq_status_string.argtypes = [ctypes.c_int]
+    L.ssq_status_string.argtypes = [ctypes.c_int32]
     L.ssq_status_string.restype = ctypes.c_char_p
     L.ssq_last_error.argtypes = []
     L.ssq_last_error.restype = ctypes.c_char_p

@@ -468,7 +468,7 @@ ssq_status ssq_stream_copy(void* dst, const void* src, size_t bytes, void* strea
     return from_hip(ssq::launch_stream_copy(dst, src, (int64_t)bytes, (hipStream_t)stream), "copy launch");
 }
 
-const char* ssq_status_string(ssq_status status)
+const char* ssq_status_string(int32_t status)
 {
     switch (status) {
     case SSQ_OK: return "SSQ_OK";
