@@ -344,69 +344,98 @@ __device__ __forceinline__ uint64_t splitmix_mix(uint64_t x)
     return x ^ (x >> 31);
 }
 
-// f = 1.5*2^23 + clamp(floor(h*inv + z + U)) for E entries (E a multiple of 4) whose
+// f = 1.5*2^23 + clamp(floor(h*inv + z + U)) for E entries (E a multiple of 8) whose
 // uniforms are counters ctr0 .. ctr0 + E - 1 (ctr0 a multiple of 4): one generator
-// output per four entries.  With p = h*inv (exact in double) and K integer,
-// floor(p + K/2^16) = floor(p) + [t + K >= 2^16], t = floor(2^16 p) - 2^16 floor(p),
-// every term an exact integer in double.  FAST (the refit fast path: |z| < 2^21, so
-// |p| < 2^22) uses the equal form floor((floor(2^16 p) + K) / 2^16), exact while
-// |p| < 2^37, and finishes in fp32 with the row's 1.5*2^23 + z.
+// output per four entries.  Off the fast path, with p = h*inv (exact in double) and K
+// integer, floor(p + K/2^16) = floor(p) + [t + K >= 2^16], t = floor(2^16 p) - 2^16 floor(p),
+// every term an exact integer in double.
 //
-// Asymmetric rows on the fast path decide in fp32 instead.  With A = 2^16 inv and
-// Kz = K + 2^16 z (an integer below 2^24 in magnitude, so exact), X = h*A + Kz is
-// 2^16 (h inv + z + K/2^16) exactly and v = fma(h, A, Kz) rounds it once.  Multiples of
-// 2^16 are representable, so rounding never carries X across one: floor(X / 2^16) =
-// floor(v / 2^16), except when v is itself a multiple of 2^16 that X lies just below;
-// an entry with such a v (on the fast path about one in 2^14 or fewer) is decided in
-// double.  |z| <= 255 keeps Kz within 2^24 (sr_f32_ok); other rows take the general path.
-// (A v too small for v/2^16 to be exact can only occur for codes -1 and 0, which the
-// clamp maps to 0 alike.)
+// On the fast path (|z| <= 255, inv <= 2^100) the decision is taken in fp32 with the wave's
+// rounding mode set to round toward -infinity (RD).  With A = 2^16 inv (exact) and
+// Kz = K + 2^16 z (an integer below 2^24 in magnitude, exact), X = h*A + Kz is
+// 2^16 (h inv + z + K/2^16) exactly and v = fma(h, A, Kz) under RD is RD(X).  Multiples of
+// 2^16 are representable and RD never rounds above X, so floor(v / 2^16) = floor(X / 2^16)
+// for every X; then f = RD(v * 2^-16 + 1.5*2^23) = 1.5*2^23 + floor(v / 2^16) (one rounding
+// of an exact sum, |v / 2^16| < 2^22).  Two fp32 operations per entry and no exceptions.
+// The two operations and the mode switches sit in one asm block, so that no other
+// floating-point instruction is scheduled while the mode is RD.  Other rows take double.
 template <int F>
 __device__ __forceinline__ bool sr_f32_ok(const RowGrid& g)
 {
-    if constexpr (Traits<F>::asym)
-        return fabsf(g.z) <= 255.0f;
-    else
-        return true;
+    return fabsf(g.z) <= 255.0f && g.inv <= 0x1p100f;
+}
+
+// MODE register, FP_ROUND bits 1:0 (single precision): 0 nearest even, 2 toward -infinity
+#define SSQ_MODE_ROUND_F32 "hwreg(HW_REG_MODE, 0, 2)"
+
+// kz[i] = RD(RD(h[i]*A + kz[i]) * 2^-16 + M) for 8 entries, the mode RD only inside the
+// block (s_nop 1: the two wait states between a mode write and a VALU that reads it).
+__device__ __forceinline__ void sr_decide8_rd(const float* h, float A, float M, float* kz)
+{
+    asm volatile("s_setreg_imm32_b32 " SSQ_MODE_ROUND_F32 ", 2\n\t"
+                 "s_nop 1\n\t"
+                 "v_fmac_f32 %0, %8, %16\n\t"
+                 "v_fmac_f32 %1, %9, %16\n\t"
+                 "v_fmac_f32 %2, %10, %16\n\t"
+                 "v_fmac_f32 %3, %11, %16\n\t"
+                 "v_fmac_f32 %4, %12, %16\n\t"
+                 "v_fmac_f32 %5, %13, %16\n\t"
+                 "v_fmac_f32 %6, %14, %16\n\t"
+                 "v_fmac_f32 %7, %15, %16\n\t"
+                 "v_fmamk_f32 %0, %0, 0x37800000, %17\n\t"
+                 "v_fmamk_f32 %1, %1, 0x37800000, %17\n\t"
+                 "v_fmamk_f32 %2, %2, 0x37800000, %17\n\t"
+                 "v_fmamk_f32 %3, %3, 0x37800000, %17\n\t"
+                 "v_fmamk_f32 %4, %4, 0x37800000, %17\n\t"
+                 "v_fmamk_f32 %5, %5, 0x37800000, %17\n\t"
+                 "v_fmamk_f32 %6, %6, 0x37800000, %17\n\t"
+                 "v_fmamk_f32 %7, %7, 0x37800000, %17\n\t"
+                 "s_setreg_imm32_b32 " SSQ_MODE_ROUND_F32 ", 0\n\t"
+                 "s_nop 1"
+                 : "+v"(kz[0]), "+v"(kz[1]), "+v"(kz[2]), "+v"(kz[3]), "+v"(kz[4]), "+v"(kz[5]), "+v"(kz[6]),
+                   "+v"(kz[7])
+                 : "v"(h[0]), "v"(h[1]), "v"(h[2]), "v"(h[3]), "v"(h[4]), "v"(h[5]), "v"(h[6]), "v"(h[7]),
+                   "v"(A), "v"(M));
 }
 
 template <int F, int E, bool FAST>
 __device__ __forceinline__ void round_codes_sr(const float* h, const RowGrid& g, uint64_t seed, uint64_t ctr0,
                                                float* f)
 {
-    static_assert(E % 4 == 0, "four uniforms per generator output");
+    static_assert(E % 8 == 0, "eight entries per fp32 decision block");
     constexpr float flo = kMagic + (float)Traits<F>::lo;
     constexpr float fhi = kMagic + (float)Traits<F>::hi;
-    constexpr bool F32 = FAST && Traits<F>::asym;
     const double inv16 = (double)g.inv * 65536.0;
     const float A = g.inv * 65536.0f;                 // exact
     const float zk = g.z * 65536.0f - 8388608.0f;     // 2^16 z - 2^23, a multiple of 2^16: exact
     uint64_t x = seed + ((ctr0 >> 2) + 1) * kGoldenGamma;
 #pragma unroll
-    for (int q = 0; q < E / 4; ++q) {
-        const uint64_t o = splitmix_mix(x);
-        x += kGoldenGamma;
-        const uint32_t lo32 = (uint32_t)o, hi32 = (uint32_t)(o >> 32);
-        const uint32_t K[4] = {lo32 & 0xFFFFu, lo32 >> 16, hi32 & 0xFFFFu, hi32 >> 16};
+    for (int q8 = 0; q8 < E / 8; ++q8) {
+        uint32_t K[8];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int e = 4 * q + k;
-            if constexpr (F32) {
-                const float Kz = __uint_as_float(K[k] | 0x4B000000u) + zk; // (2^23 + K) + zk, exact
-                const float v = __builtin_fmaf(h[e], A, Kz);
-                const float y = v * (1.0f / 65536.0f);
-                float m = floorf(y);
-                if (__builtin_expect(y == m, 0)) {
-                    // v a multiple of 2^16: this entry is decided in double (f may alias h)
-                    const double P = (double)h[e] * inv16; // 2^16 h inv, exact
-                    m = (float)floor((floor(P) + (double)K[k]) * (1.0 / 65536.0)) + g.z;
-                }
-                f[e] = __builtin_amdgcn_fmed3f(m + kMagic, flo, fhi);
-            } else if constexpr (FAST) {
-                const double P = (double)h[e] * inv16; // 2^16 h inv, exact
-                const double c = floor((floor(P) + (double)K[k]) * (1.0 / 65536.0));
-                f[e] = __builtin_amdgcn_fmed3f((float)c + g.Mz, flo, fhi);
-            } else {
+        for (int half = 0; half < 2; ++half) {
+            const uint64_t o = splitmix_mix(x);
+            x += kGoldenGamma;
+            const uint32_t lo32 = (uint32_t)o, hi32 = (uint32_t)(o >> 32);
+            K[4 * half + 0] = lo32 & 0xFFFFu;
+            K[4 * half + 1] = lo32 >> 16;
+            K[4 * half + 2] = hi32 & 0xFFFFu;
+            K[4 * half + 3] = hi32 >> 16;
+        }
+        const int e0 = 8 * q8;
+        if constexpr (FAST) {
+            float kz[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                kz[k] = __uint_as_float(K[k] | 0x4B000000u) + zk; // (2^23 + K) + zk, exact
+            sr_decide8_rd(h + e0, A, kMagic, kz);
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                f[e0 + k] = __builtin_amdgcn_fmed3f(kz[k], flo, fhi);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int e = e0 + k;
                 const double P = (double)h[e] * inv16; // 2^16 h inv, exact
                 const double fl = floor((double)h[e] * (double)g.inv);
                 const double t = __builtin_fma(-65536.0, fl, floor(P));

@@ -197,3 +197,29 @@ def test_rounding_mode_errors_and_reset():
     assert ssq.ssq_get_rounding(gq)[2] == 22
     ssq.ssq_set_rounding(gq, ssq.SSQ_ROUND_NEAREST, 0, 0)
     assert ssq.ssq_get_rounding(gq) == (ssq.SSQ_ROUND_NEAREST, 0, 0)
+
+
+@pytest.mark.parametrize("mag_exp", [-118, -95, -60, 100])
+@pytest.mark.parametrize("fmt", ["int4_asym", "int8_asym", "int8_sym"])
+def test_decode_stochastic_far_from_unit_scale(fmt, mag_exp):
+    """Rows scaled by 2^mag_exp, a fifth of their entries exactly zero, x = 0 (the state only
+    decays): scales whose reciprocal is far above and below 2^16 and reaches past 2^100, where
+    the fp32 decision's A = 2^16 inv would leave the fp32 range, with exact-zero entries."""
+    B, H, G, P, T = 2, 4, 1, 32, 3
+    rows = B * H * P
+    seed, step0 = 424242 + mag_exp, 7
+    init = synth.init_state(70, 0, rows, 128).astype(np.float64) * 2.0 ** mag_exp
+    init[:, ::5] = 0.0
+    ost = oracle.make_state(fmt, rows, 128, init.astype(np.float32))
+    gst = par.new_gpu_state(ssq.make_desc(ssq.SSQ_MAMBA2, fmt, B, H, P, 128, G))
+    ssq.ssq_set_rounding(gst, ssq.SSQ_ROUND_STOCHASTIC, seed, step0)
+    for t in range(T):
+        say(f"stochastic decode far from unit scale fmt={fmt} mag=2^{mag_exp} t={t}")
+        x, dt, Bm, Cm, A, D = synth.mamba2_step_inputs(71, 0, B, H, G, P, 128, t=t)
+        x = np.zeros_like(x)
+        par.write_gpu_state(gst, ost)
+        y = torch.empty(x.shape, dtype=torch.float32, device="cuda")
+        ssq.ssq_decode_step(gst, par.dev(x), par.dev(dt), par.dev(A), par.dev(Bm), par.dev(Cm), par.dev(D), y)
+        yo = oracle.mamba2_step(ost, x, dt, A, Bm, Cm, D, sr=(seed, step0 + t))
+        _same_state(par.read_gpu_state(gst, fmt), ost, f"t={t}")
+        assert par.block_rel(y.cpu().numpy(), yo, axis=2) <= 1e-5, t
