@@ -350,19 +350,21 @@ __device__ __forceinline__ uint64_t splitmix_mix(uint64_t x)
 // integer, floor(p + K/2^16) = floor(p) + [t + K >= 2^16], t = floor(2^16 p) - 2^16 floor(p),
 // every term an exact integer in double.
 //
-// On the fast path (|z| <= 255, inv <= 2^100) the decision is taken in fp32 with the wave's
-// rounding mode set to round toward -infinity (RD).  With A = 2^16 inv (exact) and
-// Kz = K + 2^16 z (an integer below 2^24 in magnitude, exact), X = h*A + Kz is
-// 2^16 (h inv + z + K/2^16) exactly and v = fma(h, A, Kz) under RD is RD(X).  Multiples of
-// 2^16 are representable and RD never rounds above X, so floor(v / 2^16) = floor(X / 2^16)
-// for every X; then f = RD(v * 2^-16 + 1.5*2^23) = 1.5*2^23 + floor(v / 2^16) (one rounding
-// of an exact sum, |v / 2^16| < 2^22).  Two fp32 operations per entry and no exceptions.
-// The two operations and the mode switches sit in one asm block, so that no other
-// floating-point instruction is scheduled while the mode is RD.  Other rows take double.
+// On the fast path (inv <= 2^100) the decision is taken in fp32 with the wave's rounding
+// mode set to round toward -infinity (RD).  With A = 2^16 inv (exact), X = h*A + (2^23 + K)
+// is 2^23 + 2^16 (h inv + K/2^16) exactly and v = fma(h, A, 2^23 + K) under RD is RD(X).
+// Multiples of 2^16 (below 2^40) are representable and RD never rounds above X, so
+// floor(v / 2^16) = floor(X / 2^16) for every X; with z an integer,
+// f = RD(v * 2^-16 + (1.5*2^23 + z - 128)) = 1.5*2^23 + z + floor(v / 2^16) - 128
+//   = 1.5*2^23 + floor(h inv + z + K/2^16)
+// (one rounding of an exact sum inside the magic number's range).  Two fp32 operations per
+// entry and no exceptions.  The two operations and the mode switches sit in one asm block,
+// so that no other floating-point instruction is scheduled while the mode is RD.  Rows
+// whose A would leave the fp32 range take double.
 template <int F>
 __device__ __forceinline__ bool sr_f32_ok(const RowGrid& g)
 {
-    return fabsf(g.z) <= 255.0f && g.inv <= 0x1p100f;
+    return g.inv <= 0x1p100f;
 }
 
 // MODE register, FP_ROUND bits 1:0 (single precision): 0 nearest even, 2 toward -infinity
@@ -407,7 +409,7 @@ __device__ __forceinline__ void round_codes_sr(const float* h, const RowGrid& g,
     constexpr float fhi = kMagic + (float)Traits<F>::hi;
     const double inv16 = (double)g.inv * 65536.0;
     const float A = g.inv * 65536.0f;                 // exact
-    const float zk = g.z * 65536.0f - 8388608.0f;     // 2^16 z - 2^23, a multiple of 2^16: exact
+    const float Mz128 = g.Mz - 128.0f;               // 1.5*2^23 + z - 2^23/2^16, exact
     uint64_t x = seed + ((ctr0 >> 2) + 1) * kGoldenGamma;
 #pragma unroll
     for (int q8 = 0; q8 < E / 8; ++q8) {
@@ -427,8 +429,8 @@ __device__ __forceinline__ void round_codes_sr(const float* h, const RowGrid& g,
             float kz[8];
 #pragma unroll
             for (int k = 0; k < 8; ++k)
-                kz[k] = __uint_as_float(K[k] | 0x4B000000u) + zk; // (2^23 + K) + zk, exact
-            sr_decide8_rd(h + e0, A, kMagic, kz);
+                kz[k] = __uint_as_float(K[k] | 0x4B000000u); // 2^23 + K
+            sr_decide8_rd(h + e0, A, Mz128, kz);
 #pragma unroll
             for (int k = 0; k < 8; ++k)
                 f[e0 + k] = __builtin_amdgcn_fmed3f(kz[k], flo, fhi);

@@ -1,15 +1,15 @@
 """The step kernels' fp32 decision of stochastic rounding equals the exact definition.
 
-For rows on the refit fast path with |z| <= 255 and inv <= 2^100 the kernels decide
+For rows on the refit fast path with inv <= 2^100 the kernels decide
 floor(h*inv + z + K/2^16) in fp32 with the rounding mode set toward -infinity (RD):
-A = 2^16 inv, Kz = K + 2^16 z (built as (2^23 + K) + (2^16 z - 2^23)), v = RD(h*A + Kz) by
-one fma, f = RD(v*2^-16 + 1.5*2^23) by another, code = f - 1.5*2^23.  This models that
-arithmetic with exact rationals (each operation the value of its exact result rounded
-down to fp32) and checks it against the definition over codes across the whole range,
-zero points in [-255, 255] (0 for the symmetric grid), scales from 2^-60 to 2^60 and up to
-the 2^100 bound, and values aimed at code boundaries, exactly on them included.  It also
-checks that rounding to nearest in the same two operations would be wrong at such
-boundaries, which is what the mode switch is for.  Host arithmetic only; no GPU.
+A = 2^16 inv, v = RD(h*A + (2^23 + K)) by one fma, f = RD(v*2^-16 + (1.5*2^23 + z - 128))
+by another, code = f - 1.5*2^23.  This models that arithmetic with exact rationals (each
+operation the value of its exact result rounded down to fp32) and checks it against the
+definition over codes across the whole range, zero points far beyond the code range (0 for
+the symmetric grid), scales from 2^-60 to 2^60 and up to the 2^100 bound, and values aimed
+at code boundaries, exactly on them included.  It also checks that rounding to nearest in
+the same two operations would be wrong at such boundaries, which is what the mode switch
+is for.  Host arithmetic only; no GPU.
 """
 import math
 import random
@@ -49,12 +49,12 @@ def decide(h, inv, z, K, down=True):
     """The code the kernels' two fp32 operations give (before the clamp)."""
     A = f32(inv * 65536.0)
     assert A == inv * 65536.0
-    zk = f32(z * 65536.0 - 8388608.0)
     kf = float(np.array([K | 0x4B000000], np.uint32).view(np.float32)[0])
-    Kz = f32(kf + zk)
-    assert Kz == K + 65536 * z  # exact
-    v = round32(Fraction(h) * Fraction(A) + Fraction(Kz), down)
-    f = round32(Fraction(v) / 65536 + Fraction(MAGIC), down)
+    assert kf == 2.0 ** 23 + K
+    mz = f32(f32(MAGIC + z) - 128.0)
+    assert mz == MAGIC + z - 128  # exact
+    v = round32(Fraction(h) * Fraction(A) + Fraction(kf), down)
+    f = round32(Fraction(v) / 65536 + Fraction(mz), down)
     return f - MAGIC
 
 
@@ -70,7 +70,7 @@ def test_fp32_decision_matches_the_definition():
         sym = rng.random() < 0.25
         qa = (1 << bits) - 1
         lo, hi = (-(qa // 2), qa // 2) if sym else (0, qa)
-        z = 0 if sym else rng.randint(-255, 255)
+        z = 0 if sym else rng.choice([rng.randint(-255, 255), rng.randint(-(2 ** 20), 2 ** 20)])
         inv_exp = rng.randint(-60, 60) if i % 10 else rng.randint(90, 99)
         inv = f32(rng.uniform(0.5, 2.0) * 2.0 ** inv_exp)
         K = rng.randint(0, 65535)
