@@ -41,11 +41,9 @@
  * order; fl() is one fp32 rounding):
  *    lambda = fl32(exp_double(fl(dt*A)))          exp taken in double
  *    w      = fl(dt*x)
- *    quantized row (scale s, zero z, codes c), the decay acting on the scale:
- *      ls   = fl(lambda*s)
- *      h'_n = fma(ls, c_n, fma(w, B_n, -fl(ls*z)))
- *             i.e. lambda*s*(c_n - z) + w*B_n, the offset -ls*z folded into
- *             the write term (z = 0 for the symmetric grid)
+ *    quantized row (scale s, zero z, codes c): reconstruct, then recur
+ *      hh_n = fl(s*fl(c_n - z))                   the stored row in fp32
+ *      h'_n = fma(lambda, hh_n, fl(w*B_n))         the fp32 update below
  *    fp32 row:  h'_n = fma(lambda, h_n, fl(w*B_n))
  *    refit, asymmetric: mn, mx = min/max h'; s' = fl(fl(mx-mn)/(2^b-1));
  *      inv = fl(1/s'); z' = -rne(mn*inv);
@@ -62,11 +60,15 @@
  *    dequantized value: fl(s*fl(c - z)).
  *    Readouts (y, o) are output only: they are accumulated here in double and
  *    rounded once, so they are the most accurate value any order can give.
- *    Delta rule: u_j = RN32(sum_i k_i*S_ij) with the products and the sum
- *      taken in double (for a quantized S, S_ij = s_i*(c_ij - z_i) as a real
- *      number); w_j = fl(beta*fl(v_j - fl(alpha*u_j)));
- *      S'_ij = fma(as_i, c_ij, fma(k_i, w_j, -fl(as_i*z_i))), as_i = fl(alpha*s_i)
- *      (quantized) or fma(alpha, S_ij, fl(k_i*w_j)) (fp32).
+ *    Delta rule: a quantized S is first reconstructed row by row,
+ *      S_ij = fl(s_i*fl(c_ij - z_i)); then u_j = RN32(sum_i k_i*S_ij) with the
+ *      products and the sum taken in double; w_j = fl(beta*fl(v_j - fl(alpha*u_j)));
+ *      S'_ij = fma(alpha, S_ij, fl(k_i*w_j)).
+ *    The quantized paths thus run the fp32 recurrence on the reconstructed
+ *    state ("Mamba state quantization for inference", "Mixed precision spends
+ *    bits on persistent channels": the fused kernel reconstructs the low tier,
+ *    computes the recurrence in FP32, refits and writes back; README, Setup:
+ *    the decay and the write act on the state).
  */
 #include <float.h>
 #include <math.h>
@@ -313,15 +315,13 @@ static float mamba2_row_step(int N, int bits, int asym, int32_t *code, float *s,
         return (float)(acc + (double)dx);
     }
 
-    {
-        float ls = lam * (*s);
-        float lz = ls * (*z);
-        for (n = 0; n < N; ++n) {
-            float wb = fmaf(w, Bn[n], -lz);
-            work[n] = fmaf(ls, (float)code[n], wb);
-            if (hpre)
-                hpre[n] = work[n];
-        }
+    /* reconstruct the stored row, then the fp32 update of the row above */
+    orc_dequantize_row(code, N, *s, *z, work);
+    for (n = 0; n < N; ++n) {
+        float wb = w * Bn[n];
+        work[n] = fmaf(lam, work[n], wb);
+        if (hpre)
+            hpre[n] = work[n];
     }
     if (readout_pre) {
         for (n = 0; n < N; ++n)
@@ -506,26 +506,31 @@ static int delta_matrix_step(int dk, int dv, int bits, int asym, int32_t *code, 
     float *u = (float *)malloc(sizeof(float) * (size_t)dv);
     float *w = (float *)malloc(sizeof(float) * (size_t)dv);
     float *Sn = (float *)malloc(sizeof(float) * (size_t)dk * dv);
+    float *Sh = (float *)malloc(sizeof(float) * (size_t)dk * dv);
     double *acc = (double *)malloc(sizeof(double) * (size_t)dv);
-    if (!u || !w || !Sn || !acc) {
+    if (!u || !w || !Sn || !Sh || !acc) {
         free(u);
         free(w);
         free(Sn);
+        free(Sh);
         free(acc);
         return -1;
     }
 
-    /* u = k^T S, or k^T Diag(avec) S (the state before the step) */
+    /* the state the step starts from, in fp32: a quantized state is reconstructed
+     * row by row, fl(s_i*fl(c_ij - z_i)) */
+    if (bits == 0)
+        memcpy(Sh, S, sizeof(float) * (size_t)dk * dv);
+    else
+        for (i = 0; i < dk; ++i)
+            orc_dequantize_row(code + (int64_t)i * dv, dv, s[i], z[i], Sh + (int64_t)i * dv);
+
+    /* u = k^T S, or k^T Diag(avec) S */
     for (j = 0; j < dv; ++j) {
         double a = 0.0;
         for (i = 0; i < dk; ++i) {
             double kd = avec ? (double)k[i] * (double)avec[i] : (double)k[i];
-            if (bits == 0) {
-                a += kd * (double)S[(int64_t)i * dv + j];
-            } else {
-                float d = (float)code[(int64_t)i * dv + j] - z[i];
-                a += (kd * (double)s[i]) * (double)d;
-            }
+            a += kd * (double)Sh[(int64_t)i * dv + j];
         }
         u[j] = (float)a;
     }
@@ -543,18 +548,9 @@ static int delta_matrix_step(int dk, int dv, int bits, int asym, int32_t *code, 
     /* S' = alpha*S + k w^T, alpha the key channel's own decay with avec */
     for (i = 0; i < dk; ++i) {
         float al = avec ? avec[i] : alpha;
-        if (bits == 0) {
-            for (j = 0; j < dv; ++j) {
-                float kw = k[i] * w[j];
-                Sn[(int64_t)i * dv + j] = fmaf(al, S[(int64_t)i * dv + j], kw);
-            }
-        } else {
-            float as = al * s[i];
-            float az = as * z[i];
-            for (j = 0; j < dv; ++j) {
-                float kw = fmaf(k[i], w[j], -az);
-                Sn[(int64_t)i * dv + j] = fmaf(as, (float)code[(int64_t)i * dv + j], kw);
-            }
+        for (j = 0; j < dv; ++j) {
+            float kw = k[i] * w[j];
+            Sn[(int64_t)i * dv + j] = fmaf(al, Sh[(int64_t)i * dv + j], kw);
         }
     }
     if (Spre)
@@ -588,6 +584,7 @@ static int delta_matrix_step(int dk, int dv, int bits, int asym, int32_t *code, 
     free(u);
     free(w);
     free(Sn);
+    free(Sh);
     free(acc);
     return 0;
 }
@@ -811,9 +808,10 @@ static double hs(int j, int i)
  * coordinates the step is the scalar-decay delta rule with v rotated and o
  * rotated back (Hs is symmetric and Hs Hs = I/2):
  *   vt = Hs v  (exact in double, rounded once)
+ *   St = the stored rows in fp32: FP16 rows as they are, INT8 rows
+ *        reconstructed as fl(s_i*fl(c_ij - z_i))
  *   ut = k^T St  (double, rounded once), wt = fl(beta*fl(vt - fl(alpha*ut)))
- *   St'_ij = fma(alpha, St_ij, fl(k_i*wt_j))            (FP16 rows, i < nhi)
- *   St'_ij = fma(as_i, c_ij, fma(k_i, wt_j, -fl(as_i*z_i)))  (INT8 rows)
+ *   St'_ij = fma(alpha, St_ij, fl(k_i*wt_j))            (every row)
  *   FP16 rows stored rounded to half, INT8 rows refit and rounded (asymmetric)
  *   ot = St'^T q over the stored (post) or pre-rounding rows, o = 2 Hs ot
  *   (ot and o in double, o rounded once).
@@ -828,18 +826,19 @@ int orc_damp_step_sr(int Bsz, int H, int dk, int dv, int nhi, float *hi, int32_t
     int64_t m, nm = (int64_t)Bsz * H;
     int nlo = dk - nhi, i, j;
     int64_t rows = nm * nlo;
-    float *St, *vt, *ut, *wt, *U;
+    float *St, *Sh, *vt, *ut, *wt, *U;
     double *ot;
     if (Bsz <= 0 || H <= 0 || dk <= 0 || dv != 128 || nhi < 0 || nhi > dk)
         return -1;
     St = (float *)malloc(sizeof(float) * (size_t)dk * dv);
+    Sh = (float *)malloc(sizeof(float) * (size_t)dk * dv);
     vt = (float *)malloc(sizeof(float) * (size_t)dv);
     ut = (float *)malloc(sizeof(float) * (size_t)dv);
     wt = (float *)malloc(sizeof(float) * (size_t)dv);
     U = (float *)malloc(sizeof(float) * (size_t)dv);
     ot = (double *)malloc(sizeof(double) * (size_t)dv);
-    if (!St || !vt || !ut || !wt || !U || !ot) {
-        free(St); free(vt); free(ut); free(wt); free(U); free(ot);
+    if (!St || !Sh || !vt || !ut || !wt || !U || !ot) {
+        free(St); free(Sh); free(vt); free(ut); free(wt); free(U); free(ot);
         return -1;
     }
     for (m = 0; m < nm; ++m) {
@@ -855,18 +854,20 @@ int orc_damp_step_sr(int Bsz, int H, int dk, int dv, int nhi, float *hi, int32_t
                 a += hs(j, i) * (double)vm[i];
             vt[j] = (float)a;
         }
-        /* ut = k^T St over the stored rows (exact values: half rows, s*(c - z) rows) */
+        /* the stored matrix in fp32: half rows as they are, uint8 rows reconstructed,
+         * fl(s*fl(c - z)) */
+        for (i = 0; i < dk; ++i) {
+            if (i < nhi)
+                memcpy(Sh + (int64_t)i * dv, him + (int64_t)i * dv, sizeof(float) * (size_t)dv);
+            else
+                orc_dequantize_row(cm + (int64_t)(i - nhi) * dv, dv, sm[i - nhi], zm[i - nhi],
+                                   Sh + (int64_t)i * dv);
+        }
+        /* ut = k^T St */
         for (j = 0; j < dv; ++j) {
             double a = 0.0;
-            for (i = 0; i < dk; ++i) {
-                if (i < nhi) {
-                    a += (double)km[i] * (double)him[(int64_t)i * dv + j];
-                } else {
-                    int li = i - nhi;
-                    float d = (float)cm[(int64_t)li * dv + j] - zm[li];
-                    a += ((double)km[i] * (double)sm[li]) * (double)d;
-                }
-            }
+            for (i = 0; i < dk; ++i)
+                a += (double)km[i] * (double)Sh[(int64_t)i * dv + j];
             ut[j] = (float)a;
         }
         for (j = 0; j < dv; ++j) {
@@ -874,22 +875,11 @@ int orc_damp_step_sr(int Bsz, int H, int dk, int dv, int nhi, float *hi, int32_t
             float vmj = vt[j] - au;
             wt[j] = be * vmj;
         }
-        for (i = 0; i < dk; ++i) {
+        for (i = 0; i < dk; ++i)
             for (j = 0; j < dv; ++j) {
-                float nv;
-                if (i < nhi) {
-                    float kw = km[i] * wt[j];
-                    nv = fmaf(al, him[(int64_t)i * dv + j], kw);
-                } else {
-                    int li = i - nhi;
-                    float as = al * sm[li];
-                    float az = as * zm[li];
-                    float kw = fmaf(km[i], wt[j], -az);
-                    nv = fmaf(as, (float)cm[(int64_t)li * dv + j], kw);
-                }
-                St[(int64_t)i * dv + j] = nv;
+                float kw = km[i] * wt[j];
+                St[(int64_t)i * dv + j] = fmaf(al, Sh[(int64_t)i * dv + j], kw);
             }
-        }
         if (Spre)
             memcpy(Spre + m * (int64_t)dk * dv, St, sizeof(float) * (size_t)dk * dv);
         for (j = 0; j < dv; ++j)
@@ -926,7 +916,7 @@ int orc_damp_step_sr(int Bsz, int H, int dk, int dv, int nhi, float *hi, int32_t
             o[m * dv + j] = (float)(2.0 * a);
         }
     }
-    free(St); free(vt); free(ut); free(wt); free(U); free(ot);
+    free(St); free(Sh); free(vt); free(ut); free(wt); free(U); free(ot);
     return 0;
 }
 

@@ -21,6 +21,7 @@ import pytest
 
 import oracle
 import synth
+from tests.test_oracle_pins import delta_rounding_bound
 
 F64 = np.float64
 NHI = oracle.DAMP_NHI
@@ -91,6 +92,13 @@ def test_step_is_the_delta_rule_in_rotated_coordinates(readout):
         Snew = F64(al[b, hh]) * (np.eye(128) - F64(be[b, hh]) * np.outer(kk, kk)) @ S \
             + F64(be[b, hh]) * np.outer(kk, v[b, hh].astype(F64))
         assert block_rel(Spre[m], Snew @ Hs) < 1e-5
+        # entry by entry: one fp32 step of the rule in rotated coordinates from the stored
+        # matrix, v rotated in (rounded once)
+        vt = Hs @ v[b, hh].astype(F64)
+        Sstar, bound = delta_rounding_bound(before[m], k[b, hh], vt, be[b, hh], alpha=al[b, hh],
+                                            v_err=2.0 ** -24 * np.abs(vt))
+        assert np.allclose(Sstar, Snew @ Hs, rtol=1e-9, atol=1e-9)
+        assert np.all(np.abs(Spre[m].astype(F64) - Sstar) <= bound)
         stored = st.rotated()[m].astype(F64)
         # half rows are the rounded pre-rounding values; int8 rows within half a step
         assert np.array_equal(stored[:NHI], Spre[m][:NHI].astype(np.float16).astype(F64))

@@ -16,6 +16,7 @@ import pytest
 
 import oracle
 import synth
+from tests.test_oracle_pins import delta_rounding_bound
 
 F64 = np.float64
 U = 2.0 ** -24
@@ -102,11 +103,14 @@ def test_kda_quantized_state_within_half_step(fmt):
     q, k, v, _, be = synth.delta_inputs(35, 0, Bsz, H, dk, dv)
     al = synth.kda_alpha(35, 0, Bsz, H, dk)
     o, Spre, _ = oracle.kda_step(st, q, k, v, al, be, Bsz, H, diag=True)
-    ref = np.empty_like(S_start)
+    Spre4 = Spre.reshape(Bsz, H, dk, dv).astype(F64)
     for b in range(Bsz):
         for hh in range(H):
-            ref[b, hh] = _dense(S_start[b, hh], k[b, hh], v[b, hh], al[b, hh], be[b, hh])
-    assert block_rel(Spre.reshape(Bsz, H, dk, dv), ref, axis=(2, 3)) < 1e-5
+            ref = _dense(S_start[b, hh], k[b, hh], v[b, hh], al[b, hh], be[b, hh])
+            # within the rounding of one fp32 step from the dequantized start
+            Sstar, bound = delta_rounding_bound(S_start[b, hh], k[b, hh], v[b, hh], be[b, hh], a_vec=al[b, hh])
+            assert np.allclose(Sstar, ref, rtol=1e-12, atol=1e-12)
+            assert np.all(np.abs(Spre4[b, hh] - ref) <= bound)
     deq = st.dequant().astype(F64)
     assert np.all(np.abs(deq - Spre.astype(F64))
                   <= st.scale.astype(F64)[:, None] * 0.5 * (1 + 2.0 ** -18) + 4 * U * np.abs(Spre))

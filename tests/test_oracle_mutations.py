@@ -25,9 +25,20 @@ SRC = open(os.path.join(os.path.dirname(oracle.__file__), "ssq_oracle.c")).read(
 MUTATIONS = [
     ("fp32 write term dropped", "            float wb = w * Bn[n];\n            h[n] = fmaf(lam, h[n], wb);",
      "            float wb = 0.0f * Bn[n];\n            h[n] = fmaf(lam, h[n], wb);"),
-    ("quantized write term dropped", "float wb = fmaf(w, Bn[n], -lz);", "float wb = fmaf(0.0f, Bn[n], -lz);"),
-    ("zero-point offset not folded in", "float wb = fmaf(w, Bn[n], -lz);", "float wb = w * Bn[n];"),
-    ("zero point added instead of subtracted", "float lz = ls * (*z);", "float lz = -ls * (*z);"),
+    ("quantized write term dropped",
+     "        float wb = w * Bn[n];\n        work[n] = fmaf(lam, work[n], wb);",
+     "        float wb = 0.0f * Bn[n];\n        work[n] = fmaf(lam, work[n], wb);"),
+    ("quantized update in the fused order (decay on the scale, offset in the write term)",
+     "    orc_dequantize_row(code, N, *s, *z, work);\n    for (n = 0; n < N; ++n) {\n"
+     "        float wb = w * Bn[n];\n        work[n] = fmaf(lam, work[n], wb);",
+     "    for (n = 0; n < N; ++n) {\n        float ls = lam * (*s);\n"
+     "        float wb = fmaf(w, Bn[n], -(ls * (*z)));\n        work[n] = fmaf(ls, (float)code[n], wb);"),
+    ("quantized update rounds the decayed term", "        work[n] = fmaf(lam, work[n], wb);",
+     "        work[n] = lam * work[n] + wb;"),
+    ("zero point added instead of subtracted", "        float d = (float)code[i] - z;",
+     "        float d = (float)code[i] + z;"),
+    ("zero point dropped in reconstruction", "        float d = (float)code[i] - z;",
+     "        float d = (float)code[i];"),
     ("zero point sign flipped", "float z = (float)(-rne_sum((double)mn * (double)inv, 0.0)) + 0.0f;",
      "float z = (float)(rne_sum((double)mn * (double)inv, 0.0)) + 0.0f;"),
     ("zero point from the max", "float z = (float)(-rne_sum((double)mn * (double)inv, 0.0)) + 0.0f;",
@@ -37,7 +48,7 @@ MUTATIONS = [
     ("asymmetric grid off by one", "const float cmax = (float)((1 << bits) - 1);",
      "const float cmax = (float)((1 << bits));"),
     ("Euler decay instead of exp", "return (float)exp((double)e);", "return (float)(1.0 + (double)e);"),
-    ("decay applied twice", "float ls = lam * (*s);", "float ls = lam * lam * (*s);"),
+    ("decay applied twice", "        work[n] = fmaf(lam, work[n], wb);", "        work[n] = fmaf(lam * lam, work[n], wb);"),
     ("readouts swapped", "    if (readout_pre) {\n        for (n = 0; n < N; ++n)",
      "    if (!readout_pre) {\n        for (n = 0; n < N; ++n)"),
     ("D*x dropped", "float dx = D * x;", "float dx = 0.0f * x;"),
@@ -52,7 +63,21 @@ MUTATIONS = [
     ("prefill group index wrong", "            int g = hh / (H / G);\n            for (p = 0; p < P; ++p) {",
      "            int g = hh % G;\n            for (p = 0; p < P; ++p) {"),
     ("delta correction sign", "            vm = v[j] - au;", "            vm = v[j] + au;"),
-    ("delta decay not applied to the state", "float as = al * s[i];", "float as = s[i];"),
+    ("delta decay not applied to the state", "Sn[(int64_t)i * dv + j] = fmaf(al, Sh[(int64_t)i * dv + j], kw);",
+     "Sn[(int64_t)i * dv + j] = Sh[(int64_t)i * dv + j] + kw;"),
+    ("delta state reconstructed without its scale",
+     "            orc_dequantize_row(code + (int64_t)i * dv, dv, s[i], z[i], Sh + (int64_t)i * dv);",
+     "            orc_dequantize_row(code + (int64_t)i * dv, dv, 1.0f, z[i], Sh + (int64_t)i * dv);"),
+    ("delta update in the fused order",
+     "            float kw = k[i] * w[j];\n            Sn[(int64_t)i * dv + j] = fmaf(al, Sh[(int64_t)i * dv + j], kw);",
+     "            float kw = bits ? fmaf(k[i], w[j], -((al * s[i]) * z[i])) : k[i] * w[j];\n"
+     "            Sn[(int64_t)i * dv + j] = bits ? fmaf(al * s[i], (float)code[(int64_t)i * dv + j], kw)\n"
+     "                                           : fmaf(al, Sh[(int64_t)i * dv + j], kw);"),
+    ("two-tier uint8 rows updated in the fused order",
+     "                float kw = km[i] * wt[j];\n                St[(int64_t)i * dv + j] = fmaf(al, Sh[(int64_t)i * dv + j], kw);",
+     "                float kw = i < nhi ? km[i] * wt[j] : fmaf(km[i], wt[j], -((al * sm[i - nhi]) * zm[i - nhi]));\n"
+     "                St[(int64_t)i * dv + j] = i < nhi ? fmaf(al, Sh[(int64_t)i * dv + j], kw)\n"
+     "                    : fmaf(al * sm[i - nhi], (float)cm[(int64_t)(i - nhi) * dv + j], kw);"),
     ("delta readout with k instead of q",
      "                for (j = 0; j < dv; ++j)\n                    acc[j] += (double)q[i] * (double)Sn[(int64_t)i * dv + j];\n            }\n        }",
      "                for (j = 0; j < dv; ++j)\n                    acc[j] += (double)k[i] * (double)Sn[(int64_t)i * dv + j];\n            }\n        }"),
@@ -104,8 +129,9 @@ MUTATIONS = [
     ("half tier keeps the unrounded value", "him[(int64_t)i * dv + j] = orc_round_half(row[j]);",
      "him[(int64_t)i * dv + j] = row[j];"),
     ("half rounding ties away from zero", "r = rint((double)x / q) * q;", "r = round((double)x / q) * q;"),
-    ("two-tier u ignores the half rows", "a += (double)km[i] * (double)him[(int64_t)i * dv + j];",
-     "a += 0.0 * (double)him[(int64_t)i * dv + j];"),
+    ("two-tier u ignores the half rows",
+     "                memcpy(Sh + (int64_t)i * dv, him + (int64_t)i * dv, sizeof(float) * (size_t)dv);",
+     "                memset(Sh + (int64_t)i * dv, 0, sizeof(float) * (size_t)dv);"),
 ]
 
 

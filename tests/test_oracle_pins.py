@@ -282,7 +282,6 @@ def test_error_recurrence(fmt):
     for t in range(T):
         x, dt, Bm, Cm, A, D = synth.mamba2_step_inputs(6, 0, Bsz, H, G, P, N, t=t)
         hq_prev, hf_prev = sq.dequant().astype(F64), sf.h.astype(F64)
-        sz_prev = (sq.scale.astype(F64) * sq.zero.astype(F64))[:, None]  # the folded offset s*z
         _, htil, _ = oracle.mamba2_step(sq, x, dt, A, Bm, Cm, D, diag=True)
         oracle.mamba2_step(sf, x, dt, A, Bm, Cm, D)
         lam = np.float32(np.exp(np.float32(dt * A).astype(F64)))  # the fp32 decay [B][H]
@@ -293,10 +292,12 @@ def test_error_recurrence(fmt):
         delta = hq - hf
         R = hq - ht
         lhs = np.abs(delta - lam_r * d_prev - R)
-        # first-order rounding of both updates: the decayed term, the write, the new value,
-        # and (quantized side) the offset lambda*s*z folded into the write term
-        bound = 3 * U * (np.abs(lam_r * hq_prev) + np.abs(lam_r * hf_prev) + 2 * np.abs(W)
-                         + np.abs(ht) + np.abs(hf) + 2 * np.abs(lam_r * sz_prev)) + 1e-30
+        # Both sides apply the same fp32 update to the state they hold (the quantized side to
+        # its reconstructed row), h' = fma(lambda, h, fl(fl(dt*x)*B)): the product lambda*h is
+        # exact inside the fma, so each side is off the exact recurrence only by the two
+        # roundings of the write term and the one of the result,
+        # |h' - lambda*h - W| <= (2u + u^2)|W| + u|h'|.  lhs is the difference of the two.
+        bound = U * (1 + 2.0 ** -20) * (4 * (1 + 2.0 ** -20) * np.abs(W) + np.abs(ht) + np.abs(hf)) + 1e-37
         assert np.all(lhs <= bound), t
         d_prev = delta
     # the injected residual is the rounding: at most half a step per entry
@@ -306,6 +307,40 @@ def test_error_recurrence(fmt):
 # --------------------------------------------------------------------------
 # P7: the delta rule
 # --------------------------------------------------------------------------
+def delta_rounding_bound(Sh, k, v, beta, alpha=None, a_vec=None, v_err=None):
+    """Entrywise bound on |S' - S*| for one fp32 delta-rule step of one matrix.
+
+    S* = A S + beta k v^T is the exact step from the fp32 matrix Sh [dk][dv] (the state the
+    step starts from: the reconstructed rows of a quantized state), with A = alpha (I - beta k k^T)
+    (one decay) or (I - beta k k^T) Diag(a_vec) (a decay per key row).  S' is what an fp32
+    evaluation returns when u = k^T S (or k^T Diag(a) S) is summed in double and rounded once,
+    w = beta (v - alpha u) (or beta (v - u)) is taken one rounding per operation, and each entry
+    is fma(a_i, S_ij, fl(k_i w_j)): the product a_i S_ij sits inside the fma, so apart from the
+    propagated error of w only the roundings of k_i w_j and of the result remain.  v_err bounds
+    an error already in v (a rotated v rounded once).  First order in u, with slack."""
+    u32 = U * (1 + 2.0 ** -18)
+    Sh = np.asarray(Sh, F64)
+    k = np.asarray(k, F64)
+    v = np.asarray(v, F64)
+    a = np.full(k.shape, F64(alpha)) if a_vec is None else np.asarray(a_vec, F64)
+    kap = k * (a if a_vec is not None else 1.0)
+    ustar = kap @ Sh
+    e_u = u32 * np.abs(ustar) + 2.0 ** -45 * (np.abs(kap) @ np.abs(Sh))
+    if a_vec is None:
+        vm = v - F64(alpha) * ustar
+        e_vm = F64(alpha) * e_u + u32 * np.abs(F64(alpha) * ustar) + u32 * np.abs(vm)
+    else:
+        vm = v - ustar
+        e_vm = e_u + u32 * np.abs(vm)
+    if v_err is not None:
+        e_vm = e_vm + v_err
+    w = F64(beta) * vm
+    e_w = F64(beta) * e_vm + u32 * np.abs(w)
+    Sstar = a[:, None] * Sh + np.outer(k, w)
+    bound = np.abs(k)[:, None] * e_w[None, :] + u32 * np.abs(np.outer(k, w)) + u32 * np.abs(Sstar)
+    return Sstar, bound * (1 + 2.0 ** -16) + 1e-37
+
+
 @pytest.mark.parametrize("dk,dv", [(4, 4), (8, 8), (8, 4)])
 def test_delta_fp32_matches_dense_form(dk, dv):
     Bsz, H, T = 2, 2, 3
@@ -363,20 +398,59 @@ def test_delta_quantized_state_within_half_step(fmt):
     S_start = st.dequant().astype(F64).reshape(Bsz, H, dk, dv)
     q, k, v, al, be = synth.delta_inputs(13, 0, Bsz, H, dk, dv)
     o, Spre, _ = oracle.delta_step(st, q, k, v, al, be, Bsz, H, diag=True)
-    # the pre-rounding matrix is the dense delta rule applied to the dequantized start
-    ref = np.empty_like(S_start)
+    # the pre-rounding matrix is the dense delta rule applied to the dequantized start, up to
+    # the rounding of one fp32 step
+    Spre4 = Spre.reshape(Bsz, H, dk, dv).astype(F64)
     for b in range(Bsz):
         for hh in range(H):
             kk = k[b, hh].astype(F64)
-            ref[b, hh] = F64(al[b, hh]) * (np.eye(dk) - F64(be[b, hh]) * np.outer(kk, kk)) @ S_start[b, hh] \
+            ref = F64(al[b, hh]) * (np.eye(dk) - F64(be[b, hh]) * np.outer(kk, kk)) @ S_start[b, hh] \
                 + F64(be[b, hh]) * np.outer(kk, v[b, hh].astype(F64))
-    assert block_rel(Spre.reshape(Bsz, H, dk, dv), ref, axis=(2, 3)) < 1e-5
+            Sstar, bound = delta_rounding_bound(S_start[b, hh], k[b, hh], v[b, hh], be[b, hh], alpha=al[b, hh])
+            assert np.allclose(Sstar, ref, rtol=1e-12, atol=1e-12)
+            assert np.all(np.abs(Spre4[b, hh] - ref) <= bound)
     deq = st.dequant().astype(F64)
     err = np.abs(deq - Spre.astype(F64))
     assert np.all(err <= st.scale.astype(F64)[:, None] * 0.5 * (1 + 2.0 ** -18) + 4 * U * np.abs(Spre))
     # readout from the quantized matrix
     oref = np.einsum("bhij,bhi->bhj", deq.reshape(Bsz, H, dk, dv), q.astype(F64))
     assert block_rel(o, oref) < 1e-6
+
+
+@pytest.mark.parametrize("fmt", ["int8_asym", "int4_asym", "int8_sym"])
+def test_delta_error_recurrence(fmt):
+    """Delta_t = A_t Delta_(t-1) + R_t for the delta rule, A_t = alpha (I - beta k k^T): the
+    quantized and the fp32 state, started from the same values and fed the same inputs,
+    differ after each step by the decayed difference plus the injected rounding residual,
+    within the rounding of one fp32 step on each side."""
+    Bsz, H, dk, dv, T = 1, 3, 32, 128, 12
+    rows = Bsz * H * dk
+    sq = oracle.make_state(fmt, rows, dv, synth.init_state(14, 0, rows, dv))
+    sf = oracle.make_state("fp32", rows, dv, sq.dequant())
+    d_prev = np.zeros((Bsz * H, dk, dv))
+    for t in range(T):
+        q, k, v, al, be = synth.delta_inputs(14, 0, Bsz, H, dk, dv, t=t)
+        hq_prev = sq.dequant().astype(F64).reshape(Bsz * H, dk, dv)
+        hf_prev = sf.h.astype(F64).reshape(Bsz * H, dk, dv)
+        _, ht, _ = oracle.delta_step(sq, q, k, v, al, be, Bsz, H, diag=True)
+        oracle.delta_step(sf, q, k, v, al, be, Bsz, H)
+        hq = sq.dequant().astype(F64).reshape(Bsz * H, dk, dv)
+        hf = sf.h.astype(F64).reshape(Bsz * H, dk, dv)
+        ht = ht.astype(F64).reshape(Bsz * H, dk, dv)
+        for m in range(Bsz * H):
+            b, hh = divmod(m, H)
+            kk = k[b, hh].astype(F64)
+            Aop = F64(al[b, hh]) * (np.eye(dk) - F64(be[b, hh]) * np.outer(kk, kk))
+            delta, R = hq[m] - hf[m], hq[m] - ht[m]
+            lhs = np.abs(delta - Aop @ d_prev[m] - R)
+            _, bq = delta_rounding_bound(hq_prev[m], k[b, hh], v[b, hh], be[b, hh], alpha=al[b, hh])
+            _, bf = delta_rounding_bound(hf_prev[m], k[b, hh], v[b, hh], be[b, hh], alpha=al[b, hh])
+            # the two exact steps differ by exactly A (hq_prev - hf_prev); A is applied in double
+            slack = 2.0 ** -40 * (np.abs(Aop) @ np.abs(d_prev[m]))
+            assert np.all(lhs <= bq + bf + slack), (t, m)
+            d_prev[m] = delta
+    # the injected residual is the rounding: at most half a step per entry
+    assert np.all(np.abs(R) <= sq.scale.astype(F64)[-dk:, None] * 0.5 * (1 + 2.0 ** -18) + 4 * U * np.abs(ht[-1]))
 
 
 # --------------------------------------------------------------------------
