@@ -17,8 +17,8 @@
 // rows in registers, then the 32 partial rows meet in LDS.  u is accumulated in
 // double and rounded once, so its reduction order only matters where the sum
 // lies within double rounding of an fp32 midpoint; o is an output only.  The whole matrix (16 KiB of int8
-// codes) is read once and written once.  The codes stay packed in registers between
-// the two phases (4 waves per SIMD, 4 matrices per CU in flight).
+// codes) is read once and written once.  Each key row is reconstructed once,
+// fl(s*fl(c - z)), and the fp32 values stay in registers from u to the update.
 #include "ssq_device.h"
 #include "ssq_internal.h"
 
@@ -27,6 +27,9 @@ namespace ssq {
 // waves per SIMD the register budget is sized for
 #ifndef SSQ_DELTA_WAVES
 #define SSQ_DELTA_WAVES 4
+#endif
+#ifndef SSQ_DAMP_WAVES
+#define SSQ_DAMP_WAVES 3
 #endif
 
 // A quantized key row's piece (4*NW bytes at `off` within the block's rows) stored through a
@@ -39,31 +42,15 @@ __device__ __forceinline__ void store_row_piece(uint8_t* rows_base, uint32_t row
     buf_store_words<NW, kAuxStoreWhole>(make_rsrc(rows_base, rows_bytes), off, 0u, w);
 }
 
-// Exact kap*c in one fma for an unsigned integer code c.  The code's bits as the low word of a
-// double (high word zero) read as the subnormal c*2^-1074, so fma(kap*2^562, that, acc*2^-512)
-// is the exact sum kap*c + acc scaled by 2^-512.  kap is a product of at most three fp32 values
-// (k, the decay, the scale), so it lies below 2^384 (kap*2^562 stays finite) and is a multiple
-// of 2^-447, and so is every exact product and sum of the accumulation; scaled, each is zero or
-// at least 2^-959, in the normal range, where rounding commutes with a power-of-two scaling.
-// The accumulation therefore rounds exactly as fma(kap, (double)c, acc) does, for every finite
-// input, and saves the code's conversion to double.
-constexpr double kSubScale = 0x1p562, kSubUnscale = 0x1p512;
-// Code e (0-based, in unpacking order) of a row part held as packed BITS-wide fields
-template <int BITS>
-__device__ __forceinline__ double code_as_subnormal(const uint32_t* w, int e)
-{
-    static_assert(BITS == 4 || BITS == 8, "packed codes");
-    constexpr int per = 32 / BITS;
-    const uint32_t c = (w[e / per] >> (BITS * (e % per))) & ((1u << BITS) - 1u);
-    return __builtin_bit_cast(double, (uint64_t)c);
-}
-
 // Partial rows in LDS: element j of row group r sits at r*kPartPitch + j + j/16.  A wave
 // writes 8 row groups x 8 segments of 16 columns at once; without the padding every lane
 // of it lands on the same bank.
 constexpr int kPartPitch = 136;
 __device__ __forceinline__ int part_idx(int r, int j) { return r * kPartPitch + j + (j >> 4); }
 
+// The matrix the step starts from, reconstructed in fp32 (fl(s_i*fl(c_ij - z_i)) for a
+// quantized key row), stays in registers from the u reduction to the update: each entry is
+// reconstructed once.
 // KDA: a decay per key channel (alpha [matrices][128]), S' = (I - beta k k^T) Diag(alpha) S
 // + beta k v^T, evaluated as u = k^T Diag(alpha) S, w = beta*(v - u), S' = alpha_i*S + k w^T
 template <int F, bool PRE, bool SR, bool KDA>
@@ -72,10 +59,9 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_delta_step(DeltaArgs a
     using Tr = Traits<F>;
     constexpr int LPR = 8, E = 16, RG = 32, KR = 4; // lanes per row, columns per lane, row groups, rows per thread
     constexpr int NW = Tr::quant ? E * Tr::bits / 32 : E;
-    constexpr int NS = NW; // registers per row part (packed codes, or fp32 values)
     constexpr int ROWB = Tr::quant ? 128 * Tr::bits / 8 : 512;
     __shared__ double part_u[RG * kPartPitch]; // reused for the fp32 partials of o
-    __shared__ float w_s[128];
+    __shared__ __attribute__((aligned(16))) float w_s[128];
 
     const int t = threadIdx.x;
     const int rg = t >> 3, part = t & 7, j0 = part * E;
@@ -83,74 +69,51 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_delta_step(DeltaArgs a
     const int64_t mrow0 = mat * 128; // first state row of the matrix
     const float alpha = KDA ? 0.0f : a.alpha[mat], beta = a.beta[mat];
 
-    float kk[KR], qq[KR], s_old[KR], z_old[KR], al[KR];
-    // the codes stay packed in registers (or the fp32 rows, for the fp32 state) and are
-    // unpacked where they are used, once for u and once for the update: fewer live
-    // registers, more waves per SIMD to overlap the matrix loads
-    uint32_t cw[KR][NW];
+    float kk[KR], qq[KR], al[KR];
+    float Sh[KR][E]; // this thread's 16 columns of its four key rows, in fp32
+    {
+        uint32_t cw[KR][NW];
+        float s_old[KR], z_old[KR];
 #pragma unroll
-    for (int r = 0; r < KR; ++r) {
-        const int i = rg + RG * r;
-        kk[r] = a.k[mrow0 + i];
-        qq[r] = a.q[mrow0 + i];
-        al[r] = KDA ? a.alpha[mrow0 + i] : alpha; // the key row's decay
-        const int64_t row = mrow0 + i;
+        for (int r = 0; r < KR; ++r) {
+            const int i = rg + RG * r;
+            kk[r] = a.k[mrow0 + i];
+            qq[r] = a.q[mrow0 + i];
+            al[r] = KDA ? a.alpha[mrow0 + i] : alpha; // the key row's decay
+            const int64_t row = mrow0 + i;
+            if constexpr (Tr::quant) {
+                load_words<NW>(a.codes + row * ROWB + part * (NW * 4), cw[r]);
+                s_old[r] = a.scale[row];
+                z_old[r] = Tr::asym ? a.zero[row] : 0.0f;
+            } else {
+                load_f32<E>(a.h32 + row * 128 + j0, Sh[r]);
+            }
+        }
         if constexpr (Tr::quant) {
-            load_words<NW>(a.codes + row * ROWB + part * (NW * 4), cw[r]);
-            s_old[r] = a.scale[row];
-            z_old[r] = Tr::asym ? a.zero[row] : 0.0f;
-        } else {
-            load_f32<E>(a.h32 + row * 128 + j0, reinterpret_cast<float*>(cw[r]));
-            s_old[r] = 1.0f;
-            z_old[r] = 0.0f;
+#pragma unroll
+            for (int r = 0; r < KR; ++r) {
+                unpack_codes<F, E>(cw[r], Sh[r]);
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float d = Tr::asym ? Sh[r][e] - z_old[r] : Sh[r][e];
+                    Sh[r][e] = s_old[r] * d;
+                }
+            }
         }
     }
-    auto row_values = [&](int r, float* f) {
-        if constexpr (Tr::quant) unpack_codes<F, E>(cw[r], f); // the codes c_ij as floats
-        else {
-#pragma unroll
-            for (int e = 0; e < E; ++e) f[e] = __uint_as_float(cw[r][e]);
-        }
-    };
     // column t's value of v, for the threads that form w_t
     const float vcol = t < 128 ? a.v[mrow0 + t] : 0.0f;
 
-    // u = k^T S in double: sum_i kap_i*c_ij - sum_i kap_i*z_i with kap_i = k_i*s_i exact
-    // (quantized), or sum_i k_i*S_ij (fp32); the z term is the same for every column.
-    // KDA folds the row's decay in: kap_i = (k_i*alpha_i)*s_i.
+    // u = k^T S (KDA: k^T Diag(alpha) S), products and sums in double, rounded once
     {
-        double kaps[KR];
+        double up[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) up[e] = 0.0;
 #pragma unroll
         for (int r = 0; r < KR; ++r) {
             const double kd = KDA ? (double)kk[r] * (double)al[r] : (double)kk[r];
-            kaps[r] = Tr::quant ? kd * (double)s_old[r] : kd;
-        }
-        double up[E];
-        if constexpr (Tr::asym) {
-            double zt = 0.0;
 #pragma unroll
-            for (int r = 0; r < KR; ++r) zt = __builtin_fma(kaps[r], (double)z_old[r], zt);
-            // unsigned codes: the same sums 2^512 lower, without converting the codes (the
-            // column sums are scaled back once they are complete)
-#pragma unroll
-            for (int e = 0; e < E; ++e) up[e] = -zt * (1.0 / kSubUnscale);
-#pragma unroll
-            for (int r = 0; r < KR; ++r) {
-                const double K = kaps[r] * kSubScale;
-#pragma unroll
-                for (int e = 0; e < E; ++e) up[e] = __builtin_fma(K, code_as_subnormal<Tr::bits>(cw[r], e), up[e]);
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < E; ++e) up[e] = 0.0;
-#pragma unroll
-            for (int r = 0; r < KR; ++r) {
-                const double kap = kaps[r];
-                float f[E];
-                row_values(r, f);
-#pragma unroll
-                for (int e = 0; e < E; ++e) up[e] = __builtin_fma(kap, (double)f[e], up[e]);
-            }
+            for (int e = 0; e < E; ++e) up[e] = __builtin_fma(kd, (double)Sh[r][e], up[e]);
         }
 #pragma unroll
         for (int e = 0; e < E; ++e) part_u[part_idx(rg, j0 + e)] = up[e];
@@ -162,40 +125,30 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_delta_step(DeltaArgs a
         for (int r = 0; r < RG; ++r) acc += part_u[part_idx(r, t)];
         // w_t = beta*(v_t - alpha*u_t), or beta*(v_t - u_t) for KDA (the decay is
         // already in u), formed once per column and shared
-        const float u = (float)(Tr::asym ? acc * kSubUnscale : acc);
+        const float u = (float)acc;
         const float au = KDA ? u : alpha * u;
         const float vm = vcol - au;
         w_s[t] = beta * vm;
     }
     __syncthreads();
 
-    float ww[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) ww[e] = w_s[j0 + e];
-
-    // S' = alpha*S + k w^T, row by row; refit, round and store each row
+    // S' = alpha*S + k w^T, row by row; refit, round and store each row.  w is read from LDS
+    // for each row (four 16-byte reads) rather than held in 16 registers across the rows.
     float op[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) op[e] = 0.0f;
 #pragma unroll
     for (int r = 0; r < KR; ++r) {
         const int64_t row = mrow0 + rg + RG * r;
-        // unpack again rather than keep the first unpacking alive across the u reduction
+        float* const S = Sh[r];
 #pragma unroll
-        for (int q = 0; q < NS; ++q) asm volatile("" : "+v"(cw[r][q]));
-        float S[E];
-        row_values(r, S);
-        if constexpr (Tr::quant) {
-            // alpha*s*(c - z) + k*w = fma(as, c, fma(k, w, -as*z)): the decay acts on the scale
-            const float as = al[r] * s_old[r];
-            const float az = as * z_old[r];
+        for (int q = 0; q < E / 4; ++q) {
+            const float4 w4 = reinterpret_cast<const float4*>(w_s + j0)[q];
+            const float wq[4] = {w4.x, w4.y, w4.z, w4.w};
 #pragma unroll
-            for (int e = 0; e < E; ++e) S[e] = __builtin_fmaf(as, S[e], __builtin_fmaf(kk[r], ww[e], -az));
-        } else {
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const float kw = kk[r] * ww[e];
-                S[e] = __builtin_fmaf(al[r], S[e], kw);
+            for (int k = 0; k < 4; ++k) {
+                const float kw = kk[r] * wq[k];
+                S[4 * q + k] = __builtin_fmaf(al[r], S[4 * q + k], kw);
             }
         }
         if constexpr (!Tr::quant || PRE) {
@@ -241,9 +194,8 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_delta_step(DeltaArgs a
             }
             uint32_t ow[NW];
             pack_codes<F, E>(f, ow);
-            if constexpr (Tr::quant)
-                store_row_piece<NW>(a.codes + mrow0 * ROWB, 128u * ROWB,
-                                    (uint32_t)((row - mrow0) * ROWB + part * (NW * 4)), ow);
+            store_row_piece<NW>(a.codes + mrow0 * ROWB, 128u * ROWB,
+                                (uint32_t)((row - mrow0) * ROWB + part * (NW * 4)), ow);
             if (part == 0) {
                 a.scale[row] = g.s;
                 if constexpr (Tr::asym) a.zero[row] = g.z;
@@ -372,12 +324,12 @@ __device__ __forceinline__ double wht128(double x, double* xch)
 // k = 0 of threads 0..127 (waves 0 and 1) is a half row, every other row a uint8 row, so
 // the tier of a row is uniform across its wave.
 template <bool PRE, bool SR>
-__global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_damp_step(DeltaArgs a)
+__global__ __launch_bounds__(256, SSQ_DAMP_WAVES) void k_damp_step(DeltaArgs a)
 {
     constexpr int F = INT8_ASYM;
     constexpr int LPR = 8, E = 16, RG = 32, KR = 4, NW = 4, ROWB = 128;
     __shared__ double part_u[RG * kPartPitch]; // reused for the fp32 partials of the readout
-    __shared__ float w_s[128];
+    __shared__ __attribute__((aligned(16))) float w_s[128];
     __shared__ double xch[128];
 
     const int t = threadIdx.x;
@@ -389,80 +341,70 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_damp_step(DeltaArgs a)
 
     const double vj = t < 128 ? (double)a.v[mrow0 + t] : 0.0;
 
-    float kk[KR], qq[KR], s_old[KR], z_old[KR];
-    uint32_t cw[KR][2 * NW]; // uint8 rows: 4 words of codes; half rows: 8 words of halves
-#pragma unroll
-    for (int r = 0; r < KR; ++r) {
-        const int i = rg + RG * r;
-        kk[r] = a.k[mrow0 + i];
-        qq[r] = a.q[mrow0 + i];
-        if (r == 0 && hi_wave) {
-            load_words<2 * NW, false>(a.hi + (mat * kNhi + i) * 128 + j0, cw[r]);
-            s_old[r] = 1.0f;
-            z_old[r] = 0.0f;
-        } else {
-            const int64_t lrow = mat * kNlo + (i - kNhi);
-            load_words<NW>(a.codes + lrow * ROWB + part * (NW * 4), cw[r]);
-            s_old[r] = a.scale[lrow];
-            z_old[r] = a.zero[lrow];
-        }
-    }
-    auto row_values = [&](int r, float* f) {
-        if (r == 0 && hi_wave) {
-#pragma unroll
-            for (int q = 0; q < NW * 2; ++q) {
-                f[2 * q] = half_bits_to_float(cw[r][q] & 0xFFFFu);
-                f[2 * q + 1] = half_bits_to_float(cw[r][q] >> 16);
-            }
-        } else {
-            unpack_codes<F, E>(cw[r], f);
-        }
-    };
-    // vt = Hs v, rounded once; thread t < 128 holds column t
-    const float vt = (float)(wht128(vj, xch) * 0.0625);
-
-    // ut = k^T St in double: half rows contribute k_i*St_ij, uint8 rows kap_i*(c_ij - z_i)
+    float kk[KR], qq[KR];
+    float Sh[KR][E]; // the stored rows in fp32: half values, or fl(s*fl(c - z)) of the uint8 rows
     {
-        double up[E];
-        double zt = 0.0;
-#pragma unroll
-        for (int r = 0; r < KR; ++r) zt = __builtin_fma((double)kk[r] * (double)s_old[r], (double)z_old[r], zt);
-        // the uint8 rows' codes as subnormals, the sums 2^512 lower until the column sums are done
-#pragma unroll
-        for (int e = 0; e < E; ++e) up[e] = -zt * (1.0 / kSubUnscale);
+        uint32_t cw[KR][2 * NW]; // uint8 rows: 4 words of codes; half rows: 8 words of halves
+        float s_old[KR], z_old[KR];
 #pragma unroll
         for (int r = 0; r < KR; ++r) {
-            const double kap = (double)kk[r] * (double)s_old[r];
+            const int i = rg + RG * r;
+            kk[r] = a.k[mrow0 + i];
+            qq[r] = a.q[mrow0 + i];
             if (r == 0 && hi_wave) {
-                const double kh = kap * (1.0 / kSubUnscale);
-                float f[E];
-                row_values(r, f);
-#pragma unroll
-                for (int e = 0; e < E; ++e) up[e] = __builtin_fma(kh, (double)f[e], up[e]);
+                load_words<2 * NW, false>(a.hi + (mat * kNhi + i) * 128 + j0, cw[r]);
+                s_old[r] = 1.0f;
+                z_old[r] = 0.0f;
             } else {
-                const double K = kap * kSubScale;
-#pragma unroll
-                for (int e = 0; e < E; ++e) up[e] = __builtin_fma(K, code_as_subnormal<8>(cw[r], e), up[e]);
+                const int64_t lrow = mat * kNlo + (i - kNhi);
+                load_words<NW>(a.codes + lrow * ROWB + part * (NW * 4), cw[r]);
+                s_old[r] = a.scale[lrow];
+                z_old[r] = a.zero[lrow];
             }
+        }
+#pragma unroll
+        for (int r = 0; r < KR; ++r) {
+            if (r == 0 && hi_wave) {
+#pragma unroll
+                for (int q = 0; q < NW * 2; ++q) {
+                    Sh[r][2 * q] = half_bits_to_float(cw[r][q] & 0xFFFFu);
+                    Sh[r][2 * q + 1] = half_bits_to_float(cw[r][q] >> 16);
+                }
+            } else {
+                unpack_codes<F, E>(cw[r], Sh[r]);
+#pragma unroll
+                for (int e = 0; e < E; ++e) Sh[r][e] = s_old[r] * (Sh[r][e] - z_old[r]);
+            }
+        }
+    }
+    // ut = k^T St in double, rounded once
+    {
+        double up[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) up[e] = 0.0;
+#pragma unroll
+        for (int r = 0; r < KR; ++r) {
+            const double kd = (double)kk[r];
+#pragma unroll
+            for (int e = 0; e < E; ++e) up[e] = __builtin_fma(kd, (double)Sh[r][e], up[e]);
         }
 #pragma unroll
         for (int e = 0; e < E; ++e) part_u[part_idx(rg, j0 + e)] = up[e];
     }
+    // vt = Hs v, rounded once; thread t < 128 holds column t (here, where the partial sums
+    // of u no longer hold registers)
+    const float vt = (float)(wht128(vj, xch) * 0.0625);
     __syncthreads();
     if (t < 128) {
         double acc = 0.0;
 #pragma unroll 8
         for (int r = 0; r < RG; ++r) acc += part_u[part_idx(r, t)];
         // wt = beta*(vt - alpha*ut), formed once per column and shared
-        const float au = alpha * (float)(acc * kSubUnscale);
+        const float au = alpha * (float)acc;
         const float vm = vt - au;
         w_s[t] = beta * vm;
     }
     __syncthreads();
-
-    float ww[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) ww[e] = w_s[j0 + e];
 
     float op[E];
 #pragma unroll
@@ -470,21 +412,24 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_damp_step(DeltaArgs a)
 #pragma unroll
     for (int r = 0; r < KR; ++r) {
         const int i = rg + RG * r;
+        float* const S = Sh[r];
+        // every row: St' = fma(alpha, St, fl(k*wt)), wt read from LDS for each row
 #pragma unroll
-        for (int q = 0; q < 2 * NW; ++q) asm volatile("" : "+v"(cw[r][q]));
-        float S[E];
-        row_values(r, S);
+        for (int q = 0; q < E / 4; ++q) {
+            const float4 w4 = reinterpret_cast<const float4*>(w_s + j0)[q];
+            const float wq[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float kw = kk[r] * wq[k];
+                S[4 * q + k] = __builtin_fmaf(alpha, S[4 * q + k], kw);
+            }
+        }
+        if constexpr (PRE) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) op[e] = __builtin_fmaf(qq[r], S[e], op[e]);
+        }
         if (r == 0 && hi_wave) {
-            // half row: the fp32 order, then round to half
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const float kw = kk[r] * ww[e];
-                S[e] = __builtin_fmaf(alpha, S[e], kw);
-            }
-            if constexpr (PRE) {
-#pragma unroll
-                for (int e = 0; e < E; ++e) op[e] = __builtin_fmaf(qq[r], S[e], op[e]);
-            }
+            // half row: round to half
             uint32_t hw[2 * NW];
 #pragma unroll
             for (int q = 0; q < 2 * NW; ++q) {
@@ -500,14 +445,6 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_damp_step(DeltaArgs a)
             }
         } else {
             const int64_t lrow = mat * kNlo + (i - kNhi);
-            const float as = alpha * s_old[r];
-            const float az = as * z_old[r];
-#pragma unroll
-            for (int e = 0; e < E; ++e) S[e] = __builtin_fmaf(as, S[e], __builtin_fmaf(kk[r], ww[e], -az));
-            if constexpr (PRE) {
-#pragma unroll
-                for (int e = 0; e < E; ++e) op[e] = __builtin_fmaf(qq[r], S[e], op[e]);
-            }
             float mn = S[0], mx = S[0];
 #pragma unroll
             for (int e = 1; e < E; ++e) {

@@ -7,9 +7,9 @@
 //
 // Evaluation order (identical in every kernel, so that the decode step, the
 // scan and the state initialisation round the same way):
-//   lambda  = fl32(exp_double(fl(dt*A)))
-//   ls      = fl(lambda*s),  w = fl(dt*x)
-//   h'_n    = fma(ls, c_n, fma(w, B_n, -fl(ls*z)))   (z = 0: symmetric grid)
+//   lambda  = fl32(exp_double(fl(dt*A))),  w = fl(dt*x)
+//   hh_n    = fl(s*fl(c_n - z))                    the stored entry (z = 0: symmetric grid)
+//   h'_n    = fma(lambda, hh_n, fl(w*B_n))         the fp32 recurrence on it
 //   refit   (asymmetric) s' = fl(fl(mx-mn)/(2^b-1)), inv = fl(1/s'),
 //           z' = -rne(mn*inv);  (symmetric) s' = fl(amax/(2^(b-1)-1))
 //   code    = clamp(rne(h'*inv + z')), the product exact, ties to the even code
@@ -130,6 +130,17 @@ __device__ __forceinline__ float group_sum(float v)
 __device__ __forceinline__ void wait_vmem_all()
 {
     __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+// Orders the wave's LDS accesses on either side: writes of some lanes before reads of
+// others (and reads before a later overwrite).  A wave executes its LDS instructions in
+// order; this keeps the compiler from moving one across another when it cannot tell that
+// the lanes' addresses overlap.
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 __device__ __forceinline__ float readlane_f(float v, int lane)

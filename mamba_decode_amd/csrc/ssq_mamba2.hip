@@ -17,10 +17,42 @@
 // later iterations are in flight while the current one is processed.  Waves
 // share nothing, so there is no barrier; row reductions are DPP within the
 // row's lane group.
+#include <type_traits>
+
 #include "ssq_device.h"
 #include "ssq_internal.h"
 
 namespace ssq {
+
+// lanes per 128-entry row (each lane then holds 128/LPR entries): build-time tuning knobs.
+// The scan, prefill and row kernels use lanes_per_row, the decode step step_lanes_per_row.
+#ifndef SSQ_LPR_INT4
+#define SSQ_LPR_INT4 4
+#endif
+#ifndef SSQ_LPR_INT8
+#define SSQ_LPR_INT8 4
+#endif
+#ifndef SSQ_LPR_FP32
+#define SSQ_LPR_FP32 4
+#endif
+template <int F>
+constexpr int lanes_per_row()
+{
+    return F == FP32 ? SSQ_LPR_FP32 : (Traits<F>::bits == 8 ? SSQ_LPR_INT8 : SSQ_LPR_INT4);
+}
+// The decode step spreads an int8 row over 8 lanes: a lane then holds 16 contiguous bytes
+// of the row, one store instruction writes whole rows (with the write-through streaming
+// policy), and shorter waves keep more rows in flight; 8B-shaped int8 step 120.8 to about
+// 100 us.  The scan and prefill keep 4: they store the state once per launch, and with
+// 16 entries per lane their per-token refit would cost twice the VALU per entry.
+#ifndef SSQ_STEP_LPR_INT8
+#define SSQ_STEP_LPR_INT8 8
+#endif
+template <int F>
+constexpr int step_lanes_per_row()
+{
+    return F != FP32 && Traits<F>::bits == 8 ? SSQ_STEP_LPR_INT8 : lanes_per_row<F>();
+}
 
 // B and C of the decode step in LDS (quantized formats) rather than in registers
 #ifndef SSQ_BC_LDS
@@ -89,34 +121,52 @@ struct RowStep {
         __device__ __forceinline__ float4 c4(int q) const { return reinterpret_cast<const float4*>(Cp)[q]; }
     };
 
-    // quantized formats: the old codes as floats (h, overwritten) in -> the new packed codes
-    // ow out; returns y (valid in every lane of the row).  ls = fl(lambda*s) and
-    // lz = fl(ls*z) of the old row, w = fl(dt*x), dx = fl(D*x).
-    // PACK: pack the new codes into ow; otherwise h ends holding the new codes as floats
-    // (what the next token of a scan starts from).  SR: round stochastically with the
-    // uniforms of counters ctr0 .. ctr0 + E - 1.
-    template <bool PACK = true, bool SR = false, typename In>
-    __device__ __forceinline__ static float run_q(float* h, float ls, float lz, float w, float dx,
+    // The readout sum of E entries of this lane and its row's other lanes, sum_n C_n*val(n).
+    // Each lane sums chains of CH consecutive entries with fmas from zero; with two chains per
+    // lane their sum is taken first, then the lanes' partial sums meet in the DPP tree of
+    // group_sum.  A lane holding 2*CH entries on LPR lanes thus adds in the same order as one
+    // holding CH entries on 2*LPR lanes: the scan (4 lanes per int8 row) returns the y of the
+    // decode step (8 lanes per int8 row) bit for bit.
+    template <int CH, typename In, typename V>
+    __device__ __forceinline__ static float readout(const In& in, V val)
+    {
+        static_assert(E % CH == 0 && (E / CH == 1 || E / CH == 2), "one or two readout chains per lane");
+        float a0 = 0.0f;
+#pragma unroll
+        for (int e = 0; e < CH; ++e) a0 = __builtin_fmaf(in.c(e), val(e), a0);
+        if constexpr (E / CH == 2) {
+            float a1 = 0.0f;
+#pragma unroll
+            for (int e = CH; e < E; ++e) a1 = __builtin_fmaf(in.c(e), val(e), a1);
+            a0 = a0 + a1;
+        }
+        return group_sum<LPR>(a0);
+    }
+
+    // Quantized formats, one token.  d: the stored row up to its scale, d_n = fl(c_n - z) (the
+    // code itself on the symmetric grid), overwritten; s: the row's scale; lam = fl32(exp(dt*A)),
+    // w = fl(dt*x), dx = fl(D*x).  Every entry is reconstructed, hh_n = fl(s*d_n), and the fp32
+    // recurrence runs on it, h'_n = fma(lam, hh_n, fl(w*B_n)); the row is then refit and
+    // rounded, and y is read from the new codes (or from h' with PRE).  Returns y (valid in
+    // every lane of the row).
+    // PACK: the new codes are packed into ow; otherwise d ends holding fl(c'_n - z') of the
+    // new row, what the next token of a scan starts from.  SR: round stochastically with the
+    // uniforms of counters ctr0 .. ctr0 + E - 1.  CH: entries per readout chain (readout()).
+    template <bool PACK = true, bool SR = false, int CH = E, typename In>
+    __device__ __forceinline__ static float run_q(float* d, float s, float lam, float w, float dx,
                                                   const In& in, uint32_t* ow, RowGrid& g, uint64_t sr_seed = 0,
                                                   uint64_t ctr0 = 0)
     {
         using Tr = Traits<F>;
-        // lambda*s*(c - z) + w*B = fma(ls, c, fma(w, B, -ls*z)): the decay acts on the scale
-        if constexpr (Tr::asym) {
+        float* const h = d;
 #pragma unroll
-            for (int e = 0; e < E; ++e) h[e] = __builtin_fmaf(ls, h[e], __builtin_fmaf(w, in.b(e), -lz));
-        } else {
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const float wb = w * in.b(e);
-                h[e] = __builtin_fmaf(ls, h[e], wb);
-            }
+        for (int e = 0; e < E; ++e) {
+            const float hh = s * d[e];
+            const float wb = w * in.b(e);
+            h[e] = __builtin_fmaf(lam, hh, wb);
         }
-        float acc = 0.0f;
-        if constexpr (PRE) {
-#pragma unroll
-            for (int e = 0; e < E; ++e) acc = __builtin_fmaf(in.c(e), h[e], acc);
-        }
+        float y_pre = 0.0f;
+        if constexpr (PRE) y_pre = readout<CH>(in, [&](int e) { return h[e]; });
         float mn = 0.0f, mx = 0.0f, am = 0.0f;
         if constexpr (Tr::asym) {
             mn = h[0];
@@ -134,7 +184,8 @@ struct RowStep {
             am = group_max<LPR>(am);
         }
         // h becomes f = 1.5*2^23 + code in place
-        if (__all(refit_fast<F, SR>(mn, mx, am, g))) {
+        const bool fast = __all(refit_fast<F, SR>(mn, mx, am, g));
+        if (fast) {
             // every row of the wave is inside the verified ranges and needs no clamp
             if constexpr (SR) {
                 round_codes_sr<F, E, true>(h, g, sr_seed, ctr0, h);
@@ -152,23 +203,21 @@ struct RowStep {
             }
         }
         if constexpr (PACK) pack_codes<F, E>(h, ow);
-        if constexpr (PRE) {
-            if constexpr (!PACK) {
+        // h becomes d'_n = fl(c'_n - z') of the new row: f - Mr on the fast path, where
+        // |z'| < 2^21 makes Mr = 1.5*2^23 + z' and the difference exact; (f - 1.5*2^23) - z'
+        // otherwise.  It is the next token's input in a scan and the readout's operand:
+        // y = s' * sum_n C_n*d'_n + dx.
+        if constexpr (!PACK || !PRE) {
+            if (fast) {
 #pragma unroll
-                for (int e = 0; e < E; ++e) h[e] -= kMagic; // exact: the code
+                for (int e = 0; e < E; ++e) h[e] = h[e] - g.Mr;
+            } else {
+#pragma unroll
+                for (int e = 0; e < E; ++e) h[e] = (h[e] - kMagic) - g.z;
             }
-            return group_sum<LPR>(acc) + dx;
         }
-        // y = s * sum_n C_n*(c_n - z) + dx, read from the new codes: f - Mr is c - z exactly
-        // (within 2^-21 relative for a zero point beyond 2^22; y is an output)
-#pragma unroll
-        for (int e = 0; e < E; ++e) acc = __builtin_fmaf(in.c(e), h[e] - g.Mr, acc);
-        acc = group_sum<LPR>(acc);
-        if constexpr (!PACK) {
-#pragma unroll
-            for (int e = 0; e < E; ++e) h[e] -= kMagic; // exact: the code
-        }
-        return g.s * acc + dx;
+        if constexpr (PRE) return y_pre + dx;
+        return g.s * readout<CH>(in, [&](int e) { return h[e]; }) + dx;
     }
 
     // refit and round the fp32 row h in place: h becomes f = 1.5*2^23 + code, g the new grid
@@ -322,10 +371,14 @@ __global__ __launch_bounds__(256, W) void k_m2_step(M2Args a, int64_t it_base)
         bv = *reinterpret_cast<const float2*>(a.Bm + k * 128 + 2 * lane);
         cv = *reinterpret_cast<const float2*>(a.Cm + k * 128 + 2 * lane);
     };
+    // Lanes write entries that other lanes of the wave read: each write is ordered after the
+    // wave's earlier reads of the slice and before its later ones (wave_lds_sync).
     auto bc_stage = [&]() {
         const int n = 2 * lane, off = (n / E) * PITCH + n % E;
+        wave_lds_sync();
         *reinterpret_cast<float2*>(lds_b + off) = bv;
         *reinterpret_cast<float2*>(lds_c + off) = cv;
+        wave_lds_sync();
     };
     if constexpr (BCL) bc_fetch(key);
     else rin.load(a.Bm + key * 128 + part * E, a.Cm + key * 128 + part * E);
@@ -342,16 +395,20 @@ __global__ __launch_bounds__(256, W) void k_m2_step(M2Args a, int64_t it_base)
         const float lam = readlane_f(lam_l, li);
         const float dtv = readlane_f(dt_l, li);
         const float Dh = readlane_f(d_l, li);
-        float cf[E];
-        if constexpr (Tr::quant) unpack_codes<F, E>(ring[j], cf);
-        else {
+        float cf[E]; // quantized: fl(c - z) of the stored row; fp32: the row
+        if constexpr (Tr::quant) {
+            unpack_codes<F, E>(ring[j], cf);
+            if constexpr (Tr::asym) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) cf[e] = cf[e] - rz[j];
+            }
+        } else {
 #pragma unroll
             for (int e = 0; e < E; ++e) cf[e] = __uint_as_float(ring[j][e]);
         }
         const float w = dtv * rx[j];
         const float dx = Dh * rx[j];
-        const float ls = lam * rs[j];
-        const float lz = ls * rz[j];
+        const float sc = rs[j];
         if (i + DD < K) issue(j, i + DD);
 
         const int64_t k = b * a.G + gi;
@@ -372,8 +429,8 @@ __global__ __launch_bounds__(256, W) void k_m2_step(M2Args a, int64_t it_base)
                       (uint64_t)(part * E))
                    : 0;
             float yv;
-            if constexpr (BCL) yv = RS::template run_q<true, SR>(cf, ls, lz, w, dx, rin_l, ow, g, a.sr.seed, ctr0);
-            else yv = RS::template run_q<true, SR>(cf, ls, lz, w, dx, rin, ow, g, a.sr.seed, ctr0);
+            if constexpr (BCL) yv = RS::template run_q<true, SR>(cf, sc, lam, w, dx, rin_l, ow, g, a.sr.seed, ctr0);
+            else yv = RS::template run_q<true, SR>(cf, sc, lam, w, dx, rin, ow, g, a.sr.seed, ctr0);
             // a lane's 16 bytes of a row: one store instruction writes whole rows
             constexpr int AUXS = 128 * Tr::bits / 8 / LPR == 16 ? kAuxStoreWhole : kAuxStore;
             buf_store_words<NW, AUXS>(r_w, off_w, sw, ow);
@@ -438,14 +495,20 @@ __global__ __launch_bounds__(256, PRE ? SSQ_SCAN_WAVES - 1 : SSQ_SCAN_WAVES) voi
     const int T = a.T, H = a.H, P = a.P, G = a.G;
     const float Ah = a.A[h], Dh = a.D[h];
 
-    float cf[E]; // the row's codes as floats (quantized) or its fp32 values
-    float s = 0.0f, z = 0.0f;
+    // quantized: fl(c - z) of the row (the code itself on the symmetric grid), carried from
+    // token to token; fp32: the row's values
+    float cf[E];
+    float s = 0.0f;
     if constexpr (Tr::quant) {
         uint32_t cw[NW];
         load_words<NW>(a.codes + row * ROWB + part * (NW * 4), cw);
         s = a.scale[row];
-        if constexpr (Tr::asym) z = a.zero[row];
         unpack_codes<F, E>(cw, cf);
+        if constexpr (Tr::asym) {
+            const float z = a.zero[row];
+#pragma unroll
+            for (int e = 0; e < E; ++e) cf[e] = cf[e] - z;
+        }
     } else {
         load_f32<E>(a.h32 + row * 128 + part * E, cf);
     }
@@ -455,9 +518,12 @@ __global__ __launch_bounds__(256, PRE ? SSQ_SCAN_WAVES - 1 : SSQ_SCAN_WAVES) voi
     auto bc_at = [&](const float* base, int t) {
         return *reinterpret_cast<const float2*>(base + (((int64_t)b * T + t) * G + g) * 128 + n2);
     };
+    // lanes write entries that other lanes read (wave_lds_sync on both sides)
     auto stage = [&](int buf, float2 bv, float2 cv) {
+        wave_lds_sync();
         *reinterpret_cast<float2*>(wl + buf * (2 * LDSF) + st_off) = bv;
         *reinterpret_cast<float2*>(wl + buf * (2 * LDSF) + LDSF + st_off) = cv;
+        wave_lds_sync();
     };
     auto x_idx = [&](int t) { return (((int64_t)b * T + t) * H + h) * P + p; };
 
@@ -467,8 +533,14 @@ __global__ __launch_bounds__(256, PRE ? SSQ_SCAN_WAVES - 1 : SSQ_SCAN_WAVES) voi
     float2 bn = bc_at(a.Bm, t1), cn = bc_at(a.Cm, t1);
     float xv = a.x[x_idx(0)], xn = a.x[x_idx(t1)];
     float dt_l = 0.0f, lam_l = 0.0f;
+    // the y readout in the decode step's summation order: chains of 128/(its lanes per row)
+    constexpr int CH = 128 / step_lanes_per_row<F>();
+    uint32_t ow[NW];  // the packed codes after the last token
+    RowGrid gr;
 
-    for (int t = 0; t < T; ++t) {
+    // one token; LAST packs the new codes instead of carrying fl(c - z) on
+    auto token = [&](int t, auto last) {
+        constexpr bool LAST = decltype(last)::value;
         if ((t & 63) == 0) {
             const int tt = t + lane;
             if (tt < T) {
@@ -490,15 +562,11 @@ __global__ __launch_bounds__(256, PRE ? SSQ_SCAN_WAVES - 1 : SSQ_SCAN_WAVES) voi
         const float dx = Dh * xv;
         float yv;
         if constexpr (Tr::quant) {
-            RowGrid gr;
-            const float ls = lam * s;
-            const float lz = ls * z;
             const uint64_t ctr0 =
                 SR ? (((a.sr.step + (uint64_t)t) * (uint64_t)a.sr.rows + (uint64_t)row) * 128u + (uint64_t)(part * E))
                    : 0;
-            yv = RS::template run_q<false, SR>(cf, ls, lz, w, dx, in, nullptr, gr, a.sr.seed, ctr0);
+            yv = RS::template run_q<LAST, SR, CH>(cf, s, lam, w, dx, in, ow, gr, a.sr.seed, ctr0);
             s = gr.s;
-            z = gr.z;
         } else {
             yv = RS::run_f(cf, lam, w, dx, in);
         }
@@ -510,18 +578,15 @@ __global__ __launch_bounds__(256, PRE ? SSQ_SCAN_WAVES - 1 : SSQ_SCAN_WAVES) voi
         cn = cf2;
         xv = xn;
         xn = xf;
-    }
+    };
+    for (int t = 0; t < T - 1; ++t) token(t, std::false_type{});
+    token(T - 1, std::true_type{});
 
     if constexpr (Tr::quant) {
-        float f[E];
-#pragma unroll
-        for (int e = 0; e < E; ++e) f[e] = cf[e] + kMagic; // the codes in the form pack_codes takes
-        uint32_t cw[NW];
-        pack_codes<F, E>(f, cw);
-        store_words<NW>(a.codes + row * ROWB + part * (NW * 4), cw);
+        store_words<NW>(a.codes + row * ROWB + part * (NW * 4), ow);
         if (part == 0) {
-            a.scale[row] = s;
-            if constexpr (Tr::asym) a.zero[row] = z;
+            a.scale[row] = gr.s;
+            if constexpr (Tr::asym) a.zero[row] = gr.z;
         }
     } else {
         store_f32<E>(a.h32 + row * 128 + part * E, cf);
@@ -576,8 +641,10 @@ __global__ __launch_bounds__(256, PRE ? SSQ_PREFILL_WAVES - 1 : SSQ_PREFILL_WAVE
         return *reinterpret_cast<const float2*>(base + (((int64_t)b * T + t) * G + g) * 128 + n2);
     };
     auto stage = [&](int buf, float2 bv, float2 cv) {
+        wave_lds_sync();
         *reinterpret_cast<float2*>(wl + buf * (2 * LDSF) + st_off) = bv;
         *reinterpret_cast<float2*>(wl + buf * (2 * LDSF) + LDSF + st_off) = cv;
+        wave_lds_sync();
     };
     auto x_idx = [&](int t) { return (((int64_t)b * T + t) * H + h) * P + p; };
 
@@ -733,36 +800,6 @@ __global__ __launch_bounds__(256) void k_zero_fill(uint4* p, int64_t n16)
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-// lanes per 128-entry row (each lane then holds 128/LPR entries) and the depth
-// of the decode step's prefetch ring: build-time tuning knobs
-#ifndef SSQ_LPR_INT4
-#define SSQ_LPR_INT4 4
-#endif
-#ifndef SSQ_LPR_INT8
-#define SSQ_LPR_INT8 4
-#endif
-#ifndef SSQ_LPR_FP32
-#define SSQ_LPR_FP32 4
-#endif
-template <int F>
-constexpr int lanes_per_row()
-{
-    return F == FP32 ? SSQ_LPR_FP32 : (Traits<F>::bits == 8 ? SSQ_LPR_INT8 : SSQ_LPR_INT4);
-}
-// The decode step spreads an int8 row over 8 lanes: a lane then holds 16 contiguous bytes
-// of the row, one store instruction writes whole rows (with the write-through streaming
-// policy), and shorter waves keep more rows in flight; 8B-shaped int8 step 120.8 to about
-// 100 us.  The scan and prefill keep 4: they store the state once per launch, and with
-// 16 entries per lane their per-token refit would cost twice the VALU per entry.
-#ifndef SSQ_STEP_LPR_INT8
-#define SSQ_STEP_LPR_INT8 8
-#endif
-template <int F>
-constexpr int step_lanes_per_row()
-{
-    return F != FP32 && Traits<F>::bits == 8 ? SSQ_STEP_LPR_INT8 : lanes_per_row<F>();
-}
-
 // iterations per wave (straight-line code), prefetch distance and the waves per
 // SIMD the register budget is sized for (launch bounds), per code width.  With B
 // and C in LDS and buffer addressing both quantized widths fit 128 registers
