@@ -86,6 +86,8 @@ def bind(path: str):
     L.orc_quantize_row_sr.restype = None
     L.orc_mamba2_step_sr.argtypes = L.orc_mamba2_step.argtypes + [ci, u64, u64]
     L.orc_mamba2_step_sr.restype = ci
+    L.orc_mamba2_step_sr_part.argtypes = L.orc_mamba2_step_sr.argtypes + [cl, cl]
+    L.orc_mamba2_step_sr_part.restype = ci
     L.orc_mamba2_scan_sr.argtypes = L.orc_mamba2_scan.argtypes + [ci, u64, u64]
     L.orc_mamba2_scan_sr.restype = ci
     L.orc_mamba2_rows_scan_sr.argtypes = L.orc_mamba2_rows_scan.argtypes + [ci, u64, u64, cl, i64p]
@@ -427,3 +429,220 @@ def damp_step(st: DampState, q, k, v, alpha, beta, Bsz: int, H: int, readout: st
                                 _ro(readout), _f(Spre), *_sr_args(sr))
     assert rc == 0
     return (o, Spre) if diag else o
+
+
+# --------------------------------------------------------------------------
+# K host workers on disjoint slices.  Each worker runs the single-threaded oracle on
+# its own sequences (or rows) through the same C entry points as above; ctypes
+# releases the interpreter lock during each call, so the workers run in parallel.
+# The results are those of the single calls: the slices share nothing.
+# --------------------------------------------------------------------------
+def workers() -> int:
+    """Host workers for the parallel drivers: the CPUs this process may run on, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _slices(n: int, k: int):
+    k = max(1, min(k, n))
+    return [(i * n // k, (i + 1) * n // k) for i in range(k)]
+
+
+def _run_par(fn, parts, k: int):
+    from concurrent.futures import ThreadPoolExecutor
+    if k <= 1 or len(parts) <= 1:
+        for p in parts:
+            fn(*p)
+        return
+    with ThreadPoolExecutor(k) as ex:
+        for f in [ex.submit(fn, *p) for p in parts]:
+            f.result()
+
+
+def _rows(a, r0, r1):
+    return None if a is None else a[r0:r1]
+
+
+def mamba2_step_par(st: State, x, dt, A, Bm, Cm, D, readout: str = "post", diag: bool = False,
+                    k: int | None = None, sr=None):
+    """``mamba2_step`` with the sequences split over ``k`` host workers (``sr``: (seed, step)
+    for stochastic rounding, each row drawing the uniforms of its place in the whole state)."""
+    x, dt, A, Bm, Cm, D = map(_c32, (x, dt, A, Bm, Cm, D))
+    Bsz, H, P = x.shape
+    G, N = Bm.shape[1], Bm.shape[2]
+    assert st.rows == Bsz * H * P and st.n == N
+    k = k or workers()
+    y = np.empty((Bsz, H, P), np.float32)
+    hpre = np.empty((st.rows, N), np.float32) if diag else None
+    vq = np.empty((st.rows, N), np.float32) if diag and st.fmt != "fp32" else None
+
+    def run(b0, b1):
+        r0, r1 = b0 * H * P, b1 * H * P
+        rc = lib().orc_mamba2_step_sr_part(b1 - b0, H, G, P, N, st.bits, st.asym, _i(_rows(st.code, r0, r1)),
+                                           _f(_rows(st.scale, r0, r1)), _f(_rows(st.zero, r0, r1)),
+                                           _f(_rows(st.h, r0, r1)), _f(x[b0:b1]), _f(dt[b0:b1]), _f(A),
+                                           _f(Bm[b0:b1]), _f(Cm[b0:b1]), _f(D), _f(y[b0:b1]), _ro(readout),
+                                           _f(_rows(hpre, r0, r1)), _f(_rows(vq, r0, r1)), *_sr_args(sr), b0,
+                                           st.rows)
+        assert rc == 0
+
+    _run_par(run, _slices(Bsz, k), k)
+    return (y, hpre, vq) if diag else y
+
+
+def mamba2_scan_par(st: State, x, dt, A, Bm, Cm, D, readout: str = "post", k: int | None = None):
+    """``mamba2_scan`` (round to nearest) with the sequences split over ``k`` host workers."""
+    x, dt, A, Bm, Cm, D = map(_c32, (x, dt, A, Bm, Cm, D))
+    Bsz, T, H, P = x.shape
+    G, N = Bm.shape[2], Bm.shape[3]
+    assert st.rows == Bsz * H * P and st.n == N
+    k = k or workers()
+    y = np.empty((Bsz, T, H, P), np.float32)
+
+    def run(b0, b1):
+        r0, r1 = b0 * H * P, b1 * H * P
+        rc = lib().orc_mamba2_scan_sr(b1 - b0, T, H, G, P, N, st.bits, st.asym, _i(_rows(st.code, r0, r1)),
+                                      _f(_rows(st.scale, r0, r1)), _f(_rows(st.zero, r0, r1)),
+                                      _f(_rows(st.h, r0, r1)), _f(x[b0:b1]), _f(dt[b0:b1]), _f(A),
+                                      _f(Bm[b0:b1]), _f(Cm[b0:b1]), _f(D), _f(y[b0:b1]), _ro(readout), 0, 0, 0)
+        assert rc == 0
+
+    _run_par(run, _slices(Bsz, k), k)
+    return y
+
+
+def mamba2_rows_scan_par(st: State, x, dt, A, Bm, Cm, D, readout: str = "post", k: int | None = None):
+    """``mamba2_rows_scan`` (round to nearest) with the rows split over ``k`` host workers."""
+    x, dt, A, Bm, Cm, D = map(_c32, (x, dt, A, Bm, Cm, D))
+    R, T = x.shape
+    N = Bm.shape[2]
+    assert st.rows == R and st.n == N
+    k = k or workers()
+    y = np.empty((R, T), np.float32)
+
+    def run(r0, r1):
+        rc = lib().orc_mamba2_rows_scan_sr(r1 - r0, T, N, st.bits, st.asym, _i(_rows(st.code, r0, r1)),
+                                           _f(_rows(st.scale, r0, r1)), _f(_rows(st.zero, r0, r1)),
+                                           _f(_rows(st.h, r0, r1)), _f(x[r0:r1]), _f(dt[r0:r1]), _f(A[r0:r1]),
+                                           _f(Bm[r0:r1]), _f(Cm[r0:r1]), _f(D[r0:r1]), _f(y[r0:r1]),
+                                           _ro(readout), 0, 0, 0, 0, None)
+        assert rc == 0
+
+    _run_par(run, _slices(R, k), k)
+    return y
+
+
+def delta_step_par(st: State, q, k_vec, v, alpha, beta, Bsz: int, H: int, readout: str = "post",
+                   diag: bool = False, k: int | None = None):
+    """``delta_step`` (round to nearest) with the sequences split over ``k`` host workers."""
+    q, k_vec, v, alpha, beta = map(_c32, (q, k_vec, v, alpha, beta))
+    dk, dv = k_vec.shape[-1], v.shape[-1]
+    assert st.rows == Bsz * H * dk and st.n == dv
+    k = k or workers()
+    o = np.empty((Bsz, H, dv), np.float32)
+    Spre = np.empty((st.rows, dv), np.float32) if diag else None
+    vq = np.empty((st.rows, dv), np.float32) if diag and st.fmt != "fp32" else None
+
+    def run(b0, b1):
+        r0, r1 = b0 * H * dk, b1 * H * dk
+        rc = lib().orc_delta_step_sr(b1 - b0, H, dk, dv, st.bits, st.asym, _i(_rows(st.code, r0, r1)),
+                                     _f(_rows(st.scale, r0, r1)), _f(_rows(st.zero, r0, r1)),
+                                     _f(_rows(st.h, r0, r1)), _f(q[b0:b1]), _f(k_vec[b0:b1]), _f(v[b0:b1]),
+                                     _f(alpha[b0:b1]), _f(beta[b0:b1]), _f(o[b0:b1]), _ro(readout),
+                                     _f(_rows(Spre, r0, r1)), _f(_rows(vq, r0, r1)), 0, 0, 0)
+        assert rc == 0
+
+    _run_par(run, _slices(Bsz, k), k)
+    return (o, Spre, vq) if diag else o
+
+
+def kda_step_par(st: State, q, k_vec, v, alpha, beta, Bsz: int, H: int, readout: str = "post",
+                 k: int | None = None):
+    """``kda_step`` (round to nearest) with the sequences split over ``k`` host workers."""
+    q, k_vec, v, alpha, beta = map(_c32, (q, k_vec, v, alpha, beta))
+    dk, dv = k_vec.shape[-1], v.shape[-1]
+    assert st.rows == Bsz * H * dk and st.n == dv and alpha.size == Bsz * H * dk
+    k = k or workers()
+    o = np.empty((Bsz, H, dv), np.float32)
+
+    def run(b0, b1):
+        r0, r1 = b0 * H * dk, b1 * H * dk
+        rc = lib().orc_kda_step_sr(b1 - b0, H, dk, dv, st.bits, st.asym, _i(_rows(st.code, r0, r1)),
+                                   _f(_rows(st.scale, r0, r1)), _f(_rows(st.zero, r0, r1)),
+                                   _f(_rows(st.h, r0, r1)), _f(q[b0:b1]), _f(k_vec[b0:b1]), _f(v[b0:b1]),
+                                   _f(alpha[b0:b1]), _f(beta[b0:b1]), _f(o[b0:b1]), _ro(readout), None, None,
+                                   0, 0, 0)
+        assert rc == 0
+
+    _run_par(run, _slices(Bsz, k), k)
+    return o
+
+
+def damp_step_par(st: "DampState", q, k_vec, v, alpha, beta, Bsz: int, H: int, readout: str = "post",
+                  k: int | None = None):
+    """``damp_step`` (round to nearest) with the sequences split over ``k`` host workers."""
+    q, k_vec, v, alpha, beta = map(_c32, (q, k_vec, v, alpha, beta))
+    assert st.mats == Bsz * H
+    k = k or workers()
+    o = np.empty((Bsz, H, st.dv), np.float32)
+    nlo = st.dk - st.nhi
+
+    def run(b0, b1):
+        m0, m1 = b0 * H, b1 * H
+        rc = lib().orc_damp_step_sr(b1 - b0, H, st.dk, st.dv, st.nhi, _f(st.hi[m0:m1]),
+                                    _i(st.code[m0 * nlo:m1 * nlo]), _f(st.scale[m0 * nlo:m1 * nlo]),
+                                    _f(st.zero[m0 * nlo:m1 * nlo]), _f(q[b0:b1]), _f(k_vec[b0:b1]), _f(v[b0:b1]),
+                                    _f(alpha[b0:b1]), _f(beta[b0:b1]), _f(o[b0:b1]), _ro(readout), None, 0, 0, 0)
+        assert rc == 0
+
+    _run_par(run, _slices(Bsz, k), k)
+    return o
+
+
+def mamba2_prefill_par(st: State, x, dt, A, Bm, Cm, D, chunk: int, readout: str = "post",
+                       k: int | None = None):
+    """``mamba2_prefill`` (round to nearest) with the sequences split over ``k`` host workers."""
+    x, dt, A, Bm, Cm, D = map(_c32, (x, dt, A, Bm, Cm, D))
+    Bsz, T, H, P = x.shape
+    G, N = Bm.shape[2], Bm.shape[3]
+    assert st.rows == Bsz * H * P and st.n == N
+    k = k or workers()
+    y = np.empty((Bsz, T, H, P), np.float32)
+
+    def run(b0, b1):
+        r0, r1 = b0 * H * P, b1 * H * P
+        rc = lib().orc_mamba2_prefill_sr(b1 - b0, T, chunk, H, G, P, N, st.bits, st.asym,
+                                         _i(_rows(st.code, r0, r1)), _f(_rows(st.scale, r0, r1)),
+                                         _f(_rows(st.zero, r0, r1)), _f(_rows(st.h, r0, r1)), _f(x[b0:b1]),
+                                         _f(dt[b0:b1]), _f(A), _f(Bm[b0:b1]), _f(Cm[b0:b1]), _f(D), _f(y[b0:b1]),
+                                         _ro(readout), 0, 0, 0)
+        assert rc == 0
+
+    _run_par(run, _slices(Bsz, k), k)
+    return y
+
+
+def damp_from_fp32_par(S: np.ndarray, Bsz: int, H: int, nhi: int = DAMP_NHI, k: int | None = None) -> DampState:
+    """``damp_from_fp32`` with the sequences split over ``k`` host workers."""
+    S = _c32(S)
+    dk, dv = S.shape[-2], S.shape[-1]
+    mats = Bsz * H
+    nlo = dk - nhi
+    hi = np.empty((mats, nhi, dv), np.float32)
+    code = np.empty((mats * nlo, dv), np.int32)
+    s = np.empty(mats * nlo, np.float32)
+    z = np.empty(mats * nlo, np.float32)
+    k = k or workers()
+    S4 = S.reshape(Bsz, H, dk, dv)
+
+    def run(b0, b1):
+        m0, m1 = b0 * H, b1 * H
+        rc = lib().orc_damp_from_fp32(b1 - b0, H, dk, dv, nhi, _f(S4[b0:b1]), _f(hi[m0:m1]),
+                                      _i(code[m0 * nlo:m1 * nlo]), _f(s[m0 * nlo:m1 * nlo]), _f(z[m0 * nlo:m1 * nlo]))
+        assert rc == 0
+
+    _run_par(run, _slices(Bsz, k), k)
+    return DampState(mats, dk, dv, nhi, hi, code, s, z)

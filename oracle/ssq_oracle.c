@@ -342,15 +342,20 @@ static float mamba2_row_step(int N, int bits, int asym, int32_t *code, float *s,
  *   x [Bsz][H][P], dt [Bsz][H], A [H], Bm/Cm [Bsz][G][N], D [H], y [Bsz][H][P]
  *   hpre, vq: optional [Bsz][H][P][N] diagnostics.
  * Returns 0, or -1 on bad sizes. */
-int orc_mamba2_step_sr(int Bsz, int H, int G, int P, int N, int bits, int asym, int32_t *code,
-                       float *s, float *z, float *h, const float *x, const float *dt, const float *A,
-                       const float *Bm, const float *Cm, const float *D, float *y, int readout_pre,
-                       float *hpre, float *vq, int sr, uint64_t seed, uint64_t step)
+/* As orc_mamba2_step_sr for the sequences of a larger state: the arrays hold sequences
+ * b0 .. b0+Bsz-1 of a state of rows_total rows, and stochastic rounding draws the uniforms of
+ * those rows' places in it (row r of the slice is state row b0*H*P + r). */
+int orc_mamba2_step_sr_part(int Bsz, int H, int G, int P, int N, int bits, int asym, int32_t *code,
+                            float *s, float *z, float *h, const float *x, const float *dt,
+                            const float *A, const float *Bm, const float *Cm, const float *D,
+                            float *y, int readout_pre, float *hpre, float *vq, int sr,
+                            uint64_t seed, uint64_t step, int64_t b0, int64_t rows_total)
 {
     int b, hh, p;
     float *work, *U;
-    int64_t rows = (int64_t)Bsz * H * P;
-    if (Bsz <= 0 || H <= 0 || G <= 0 || P <= 0 || N <= 0 || H % G != 0)
+    int64_t rows = rows_total, row0 = b0 * H * P;
+    if (Bsz <= 0 || H <= 0 || G <= 0 || P <= 0 || N <= 0 || H % G != 0 || b0 < 0 ||
+        row0 + (int64_t)Bsz * H * P > rows_total)
         return -1;
     work = (float *)malloc(sizeof(float) * (size_t)N);
     U = (float *)malloc(sizeof(float) * (size_t)N);
@@ -368,7 +373,7 @@ int orc_mamba2_step_sr(int Bsz, int H, int G, int P, int N, int bits, int asym, 
             for (p = 0; p < P; ++p) {
                 int64_t r = ((int64_t)b * H + hh) * P + p;
                 if (sr)
-                    orc_sr_row_uniforms(seed, step, rows, r, N, U);
+                    orc_sr_row_uniforms(seed, step, rows, row0 + r, N, U);
                 y[r] = mamba2_row_step(N, bits, asym, code ? code + r * N : NULL, s ? s + r : NULL,
                                        z ? z + r : NULL, h ? h + r * N : NULL, x[r], dtv, A[hh],
                                        Bn, Cn, D[hh], readout_pre, hpre ? hpre + r * N : NULL,
@@ -378,6 +383,16 @@ int orc_mamba2_step_sr(int Bsz, int H, int G, int P, int N, int bits, int asym, 
     free(work);
     free(U);
     return 0;
+}
+
+int orc_mamba2_step_sr(int Bsz, int H, int G, int P, int N, int bits, int asym, int32_t *code,
+                       float *s, float *z, float *h, const float *x, const float *dt, const float *A,
+                       const float *Bm, const float *Cm, const float *D, float *y, int readout_pre,
+                       float *hpre, float *vq, int sr, uint64_t seed, uint64_t step)
+{
+    return orc_mamba2_step_sr_part(Bsz, H, G, P, N, bits, asym, code, s, z, h, x, dt, A, Bm, Cm, D,
+                                   y, readout_pre, hpre, vq, sr, seed, step, 0,
+                                   (int64_t)Bsz * H * P);
 }
 
 int orc_mamba2_step(int Bsz, int H, int G, int P, int N, int bits, int asym, int32_t *code,

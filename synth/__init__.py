@@ -118,24 +118,50 @@ def mamba2_head_params(seed: int, layer: int, H: int):
     return A, D, bias
 
 
-def mamba2_scan_inputs(seed: int, layer: int, Bsz: int, T: int, H: int, G: int, P: int, N: int):
-    """Inputs of a ``T``-token scan of one layer.
-
-    Returns ``(x, dt, Bm, Cm, A, D)`` with ``x`` [Bsz][T][H][P], ``dt`` [Bsz][T][H] (already through
-    softplus, > 0), ``Bm``/``Cm`` [Bsz][T][G][N], ``A``/``D`` [H], all float32 C-contiguous.
-    """
-    A, D, bias = mamba2_head_params(seed, layer, H)
-    b, t, h = np.meshgrid(np.arange(Bsz), np.arange(T), np.arange(H), indexing="ij")
+def _scan_block(seed, layer, Bsz, t0, t1, H, G, P, N, bias):
+    """dt, x, Bm, Cm of tokens t0 .. t1-1 ([Bsz][t1-t0][...]), indexed as in a full scan."""
+    b, t, h = np.meshgrid(np.arange(Bsz), np.arange(t0, t1), np.arange(H), indexing="ij")
     dt_idx = ((t.astype(np.uint64) * Bsz + b) * H + h).astype(np.uint64)
     dt = _f32(_softplus(normal(seed, STREAMS["dt"], layer, dt_idx) + bias[h]))
     x_idx = (dt_idx[..., None] * np.uint64(P) + np.arange(P, dtype=np.uint64))
     x = _f32(normal(seed, STREAMS["x"], layer, x_idx))
-    b2, t2, g2 = np.meshgrid(np.arange(Bsz), np.arange(T), np.arange(G), indexing="ij")
+    b2, t2, g2 = np.meshgrid(np.arange(Bsz), np.arange(t0, t1), np.arange(G), indexing="ij")
     bc_idx = (((t2.astype(np.uint64) * Bsz + b2) * G + g2)[..., None] * np.uint64(N)
               + np.arange(N, dtype=np.uint64))
     sc = 1.0 / math.sqrt(N)
     Bm = _f32(normal(seed, STREAMS["B"], layer, bc_idx) * sc)
     Cm = _f32(normal(seed, STREAMS["C"], layer, bc_idx) * sc)
+    return x, dt, Bm, Cm
+
+
+def mamba2_scan_inputs(seed: int, layer: int, Bsz: int, T: int, H: int, G: int, P: int, N: int,
+                       threads: int = 1):
+    """Inputs of a ``T``-token scan of one layer.
+
+    Returns ``(x, dt, Bm, Cm, A, D)`` with ``x`` [Bsz][T][H][P], ``dt`` [Bsz][T][H] (already through
+    softplus, > 0), ``Bm``/``Cm`` [Bsz][T][G][N], ``A``/``D`` [H], all float32 C-contiguous.
+    ``threads`` > 1 draws blocks of tokens concurrently (same values: the generator is counter
+    based).
+    """
+    A, D, bias = mamba2_head_params(seed, layer, H)
+    if threads <= 1 or Bsz * T * H * P < (1 << 22):
+        x, dt, Bm, Cm = _scan_block(seed, layer, Bsz, 0, T, H, G, P, N, bias)
+        return x, dt, Bm, Cm, A, D
+    from concurrent.futures import ThreadPoolExecutor
+    x = np.empty((Bsz, T, H, P), np.float32)
+    dt = np.empty((Bsz, T, H), np.float32)
+    Bm = np.empty((Bsz, T, G, N), np.float32)
+    Cm = np.empty((Bsz, T, G, N), np.float32)
+    # blocks of about 2^20 values of x, so that the float64 temporaries stay small
+    step = max(1, min(T, (1 << 20) // max(1, Bsz * H * P)))
+
+    def fill(t0):
+        t1 = min(T, t0 + step)
+        x[:, t0:t1], dt[:, t0:t1], Bm[:, t0:t1], Cm[:, t0:t1] = _scan_block(seed, layer, Bsz, t0, t1, H, G, P, N,
+                                                                            bias)
+
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(fill, range(0, T, step)))
     return x, dt, Bm, Cm, A, D
 
 

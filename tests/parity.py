@@ -136,3 +136,22 @@ def read_gpu_damp(gst) -> dict:
     codes, scale, zero = gst.regions()
     return {"code": unpack_codes(codes.cpu().numpy(), "int8_asym"), "scale": scale.cpu().numpy().copy(),
             "zero": zero.cpu().numpy().copy(), "hi": gst.hi_region().cpu().numpy().astype(np.float32)}
+
+
+def y_within_sum_bound(yg, yo, Crows, rrows, dx, terms: int = 128):
+    """y read as an fp32 sum: |y_gpu - y_exact| <= 2*terms*u*sum_n |C_n r_n| + 2u|y_exact| + u|D x|
+    for every row, where r is the row the readout names (the dequantized new row, or the row
+    before rounding) and y_exact the oracle's (the sum in double, rounded once).  This bounds any
+    fp32 summation order of the terms; the head-relative tolerance alone cannot hold to 1e-5 when
+    a whole head's sum cancels (a zero start state makes every row of a head a multiple of B).
+    Crows [R][N] (the C each row reads), rrows [R][N], yg/yo/dx [R].  Returns the largest ratio
+    of the error to its bound."""
+    u = 2.0 ** -24
+    yg = np.asarray(yg, F64).reshape(-1)
+    yo = np.asarray(yo, F64).reshape(-1)
+    dx = np.asarray(dx, F64).reshape(-1)
+    mag = np.einsum("rn,rn->r", np.abs(np.asarray(Crows, np.float32)), np.abs(np.asarray(rrows, np.float32)),
+                    dtype=F64)
+    bound = 2 * terms * u * mag + 2 * u * np.abs(yo) + u * np.abs(dx) + 1e-37
+    err = np.abs(yg - yo)
+    return float(np.max(err / bound))
