@@ -47,7 +47,7 @@ WORKLOADS = {
     "m2_370m_int4_sr": dict(kind="m2", layers=48, B=256, H=32, P=64, fmt="int4_asym", init="random",
                             rounding="stochastic",
                             desc="as m2_370m_int4 with stochastic rounding of the codes (SplitMix64 "
-                                 "uniforms per entry); graph replays reuse the captured token"),
+                                 "uniforms per entry); each graph replay draws the next token"),
     "delta_int8": dict(kind="delta", layers=30, B=256, H=32, P=128, fmt="int8_asym", init="random",
                        desc="Delta-rule (GDN/KDA-style) decode step: 30 layers x 32 heads x 128 x 128, batch 256, "
                             "int8 asymmetric per-row state, seeded random state with 5% x20 outlier rows"),
@@ -82,6 +82,27 @@ WORKLOADS = {
     "m2_8b_scan_int4": dict(kind="scan", layers=1, B=8, H=128, P=64, fmt="int4_asym", init="zero", T=8192,
                             desc="Mamba-2 8B-shaped layer: batch 8, 8192-token scan, int4 asymmetric"),
 }
+
+# The pages' own figures for this path, with the hardware they were taken on (context; none of
+# them is a state-update GB/s, steps/s or fraction of HBM for this workload)
+PAGES_CONTEXT = [
+    {"figure": "24.3% of decode latency spent on recurrent-state updates; about 15 GB of FP32 "
+               "recurrent state at decode batch 256 (30 Gated DeltaNet layers)",
+     "hardware": "not stated in the excerpt",
+     "source": "Mamba state quantization for inference, Recurrent state is fixed per request, not free"},
+    {"figure": "DAMP's fused mixed FP16/INT8 recurrent-update kernel 1.46-1.65x (GDN) and 1.81-2.01x "
+               "(KDA) faster than FP32 from batch 32 to 256",
+     "hardware": "not stated in the excerpt",
+     "source": "Mamba state quantization for inference, Mixed precision spends bits on persistent channels"},
+    {"figure": "sequential per-token scan with the state rounded every step (fp32 Mamba-2 130M/370M); "
+               "no speed published",
+     "hardware": "one RTX 3070 (8 GB)",
+     "source": "ssm-state-quantization README, Setup"},
+    {"figure": "Quamba2 whole-model time per output token 22.73 ms (FP16) to 12.61 ms (W8A8), "
+               "Mamba2-8B at batch 1 (weight and activation quantization, not the state path)",
+     "hardware": "A5000",
+     "source": "Quamba2 summary"},
+]
 
 KERNEL_NAMES = {"m2": "k_m2_step", "delta": "k_delta_step", "kda": "k_delta_step", "scan": "k_m2_scan",
                 "prefill": "k_m2_prefill"}
@@ -277,18 +298,24 @@ def main():
         do_step()
     torch.cuda.synchronize()
 
-    # ---------------- timed region ----------------
+    # ---------------- timed region: `steps` steps in 5 consecutive blocks ----------------
+    # Events on the launch stream mark the blocks; the step time is the median over the
+    # blocks of their mean step time (the mean over all steps is reported beside it).
     log(f"[bench] timing {steps} step(s)")
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    nblk = min(5, steps)
+    bounds = [round(i * steps / nblk) for i in range(nblk + 1)]
+    evs_blk = [torch.cuda.Event(enable_timing=True) for _ in range(nblk + 1)]
     torch.cuda.synchronize()
-    e0.record()
-    for _ in range(steps):
-        do_step()
-    e1.record()
-    e1.synchronize()
+    evs_blk[0].record()
+    for b in range(nblk):
+        for _ in range(bounds[b], bounds[b + 1]):
+            do_step()
+        evs_blk[b + 1].record()
+    evs_blk[-1].synchronize()
     torch.cuda.synchronize()
-    ms_total = e0.elapsed_time(e1)
-    ms_per_step = ms_total / steps
+    block_ms = [evs_blk[b].elapsed_time(evs_blk[b + 1]) / (bounds[b + 1] - bounds[b]) for b in range(nblk)]
+    ms_per_step = float(np.median(block_ms))
+    ms_per_step_mean = evs_blk[0].elapsed_time(evs_blk[-1]) / steps
 
     # ---------------- eager per-launch time (events around each launch, same stream): context ----------------
     kreps = max(1, min(steps, 20 if not seq else 2))
@@ -351,8 +378,11 @@ def main():
     del src, dst
 
     total_bytes_step = bytes_per_launch * L
-    value = total_bytes_step / (ms_per_step * 1e-3) / 1e9
+    total_gbps = total_bytes_step / (ms_per_step * 1e-3) / 1e9
     state_gbps = state_bytes_layer * L / (ms_per_step * 1e-3) / 1e9 if not seq else None
+    # the headline: state-update GB/s (the state read and written once per step); the scans keep
+    # the state on-chip, so theirs is the GB/s of the per-token inputs and outputs
+    value = state_gbps if not seq else total_gbps
     achieved = bytes_per_launch / (kernel_ms_mean * 1e-3) / 1e9
 
     # traffic from the committed rocprofv3 counter runs, only while the kernels are unchanged
@@ -371,6 +401,9 @@ def main():
         "steps": steps,
         "warmup": warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "timing": {"blocks": nblk, "block_ms_per_step": [round(b, 5) for b in block_ms],
+                   "statistic": "median over the blocks of their mean step time",
+                   "ms_per_step_mean_all_steps": round(ms_per_step_mean, 5)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -388,7 +421,10 @@ def main():
             **({"layers_reduced_from": WORKLOADS[args.workload]["layers"]} if args.layers is not None else {}),
             **({"batch_changed_from": WORKLOADS[args.workload]["B"]} if args.batch is not None else {}),
         },
-        "hbm_frac": round(value / HBM_PEAK_GBPS, 4),
+        "value_kind": "state GB/s (state bytes read and written once per step)" if not seq
+                      else "GB/s of the per-token inputs and outputs (the state stays on-chip)",
+        "total_GBps": round(total_gbps, 2),
+        "hbm_frac": round(total_gbps / HBM_PEAK_GBPS, 4),
         # a rotated workload times one layer on several state instances: each launch is one token
         "decode_steps_per_s": (round(1000.0 * (L if wl.get("rotate") else 1) / ms_per_step, 2)
                                if not seq else None),
@@ -398,7 +434,7 @@ def main():
                                      if eager_ms_per_step else None),
         "copy_GBps": round(copy_gbps, 1),
         "copy_kind": "ssq_stream_copy, 2 GiB (4 GiB of traffic), same run",
-        "frac_of_copy": round(value / copy_gbps, 4),
+        "frac_of_copy": round(total_gbps / copy_gbps, 4),
         "runtime_copy_GBps": round(runtime_copy_gbps, 1),
         "roofline": {
             "bound": "hbm" if not seq else "alu",
@@ -414,6 +450,7 @@ def main():
             "eager_launch_ms_median": round(eager_ms_median, 5),
         },
         "device": torch.cuda.get_device_name(0),
+        "pages_context": PAGES_CONTEXT,
     }
     if seq:
         # the state stays on-chip for all T tokens: the scan is bound by VALU issue.  Algorithmic
@@ -439,6 +476,115 @@ def main():
 
 
 def cpu_baseline(args, wl, bytes_per_launch, rows_per_layer):
+    """The oracle as it stands on the host: K workers (the process's CPU affinity, at most 16),
+    each single-threaded on a disjoint slice of sequences, over the workload's rows (bounded for
+    the long scans); and one worker on a fixed slice for a bounded time."""
+    import oracle
+
+    k_leg = _cpu_kcore(args, wl, bytes_per_launch, rows_per_layer)
+    single = _cpu_single(args, wl, bytes_per_launch, rows_per_layer)
+    out = {"value": k_leg["GBps"], "unit": "GB/s", "cores": k_leg["cores"], "kind": "oracle",
+           "sample": k_leg["sample"], "wall_s": k_leg["wall_s"], "cpu": _cpu_model(),
+           "affinity_cpus": len(os.sched_getaffinity(0)), "workers_cap": 16}
+    for key in ("decode_steps_per_s", "tokens_per_s"):
+        if key in k_leg:
+            out[key] = k_leg[key]
+    out["single_core"] = single
+    assert k_leg["cores"] == oracle.workers()
+    return out
+
+
+def _cpu_kcore(args, wl, bytes_per_launch, rows_per_layer):
+    import numpy as np
+
+    import oracle
+    import synth
+
+    K = oracle.workers()
+    kind, fmt, B, H, P, N = wl["kind"], wl["fmt"], wl["B"], wl["H"], wl["P"], 128
+    T = wl.get("T", 1)
+    layers = 1 if wl.get("rotate") else wl["layers"]
+    wall = 0.0
+
+    def timed(fn, *a, **kw):
+        nonlocal wall
+        t0 = time.perf_counter()
+        r = fn(*a, **kw)
+        wall += time.perf_counter() - t0
+        return r
+
+    out = {"cores": K}
+    if kind == "m2":
+        # one step through every layer of the workload (each layer's own inputs), all rows; the
+        # layers start from copies of one drawn state
+        rows = B * H * P
+        base = (oracle.make_state(fmt, rows, N, synth.init_state(args.seed, 0, rows, N, threads=K))
+                if wl["init"] == "random" else oracle.make_state(fmt, rows, N))
+        sr = wl.get("rounding") == "stochastic"
+        for layer in range(layers):
+            st = base.copy()
+            x, dt, Bm, Cm, A, D = synth.mamba2_step_inputs(args.seed, layer, B, H, 1, P, N)
+            timed(oracle.mamba2_step_par, st, x, dt, A, Bm, Cm, D, k=K,
+                  sr=(args.seed * 1000 + layer, 0) if sr else None)
+            del st
+        done_bytes = bytes_per_launch * layers
+        out["decode_steps_per_s"] = round(1.0 / wall, 5)
+        out["sample"] = (f"one decode step of the whole workload: {layers} layer(s) x {rows} rows ({fmt}), "
+                         f"each layer from a copy of one drawn state")
+    elif kind in ("delta", "kda"):
+        rows = B * H * P
+        init = synth.init_state(args.seed, 0, rows, N, threads=K)
+        if fmt == "damp":
+            base = oracle.damp_from_fp32_par(init.reshape(B, H, P, N), B, H, k=K)
+        else:
+            base = oracle.make_state(fmt, rows, N, init)
+        del init
+        for layer in range(layers):
+            st = base.copy()
+            q, k, v, al, be = synth.delta_inputs(args.seed, layer, B, H, P, N)
+            if kind == "kda":
+                al = synth.kda_alpha(args.seed, layer, B, H, P)
+                timed(oracle.kda_step_par, st, q, k, v, al, be, B, H, k=K)
+            elif fmt == "damp":
+                timed(oracle.damp_step_par, st, q, k, v, al, be, B, H, k=K)
+            else:
+                timed(oracle.delta_step_par, st, q, k, v, al, be, B, H, k=K)
+            del st
+        done_bytes = bytes_per_launch * layers
+        out["decode_steps_per_s"] = round(1.0 / wall, 5)
+        out["sample"] = (f"one step of the whole workload: {layers} layer(s) x {B * H} matrices ({fmt}), "
+                         f"each layer from a copy of one drawn state")
+    elif kind in ("scan", "prefill") and H * P * B * T <= (1 << 27):
+        # one layer, the first min(B, K) sequences, every token
+        nb = min(B, K)
+        x, dt, Bm, Cm, A, D = synth.mamba2_scan_inputs(args.seed, 0, nb, T, H, 1, P, N, threads=K)
+        st = oracle.make_state(fmt, nb * H * P, N)
+        if kind == "prefill":
+            timed(oracle.mamba2_prefill_par, st, x, dt, A, Bm, Cm, D, chunk=wl["chunk"], k=K)
+        else:
+            timed(oracle.mamba2_scan_par, st, x, dt, A, Bm, Cm, D, k=K)
+        done_bytes = bytes_per_launch * nb / B
+        out["tokens_per_s"] = round(nb * T / wall, 1)
+        out["sample"] = f"{nb} of {B} sequences of one layer ({nb * H * P} rows, {fmt}), all {T} tokens"
+    else:
+        # long scans: four rows of every (sequence, head), every token (rows are independent: the
+        # oracle scans every sequence and head with those four rows' x)
+        psel = np.linspace(0, P - 1, 4).astype(int)
+        x, dt, Bm, Cm, A, D = synth.mamba2_scan_inputs(args.seed, 0, B, T, H, 1, P, N, threads=K)
+        xs = np.ascontiguousarray(x[:, :, :, psel])
+        del x
+        st = oracle.make_state(fmt, B * H * len(psel), N)
+        timed(oracle.mamba2_scan_par, st, xs, dt, A, Bm, Cm, D, k=K)
+        done_bytes = bytes_per_launch * len(psel) / P
+        out["tokens_per_s"] = round(B * T / wall * len(psel) / P, 1)
+        out["sample"] = (f"{B * H * len(psel)} rows of one layer (four in every (sequence, head), {fmt}), "
+                         f"all {T} tokens")
+    out["wall_s"] = round(wall, 3)
+    out["GBps"] = round(done_bytes / wall / 1e9, 4)
+    return out
+
+
+def _cpu_single(args, wl, bytes_per_launch, rows_per_layer):
     """The oracle as it stands, single-threaded, on a bounded sample of the same workload."""
     import numpy as np
 
@@ -489,8 +635,7 @@ def cpu_baseline(args, wl, bytes_per_launch, rows_per_layer):
     rows_per_s = done / el  # row updates (one row, one token) per second
     gbps = rows_per_s * (bytes_per_launch / (rows_per_layer * wl.get("T", 1))) / 1e9
     out = {"value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-           "sample": sample + f", repeated for {el:.1f} s", "rows_per_s": round(rows_per_s, 1),
-           "cpu": _cpu_model()}
+           "sample": sample + f", repeated for {el:.1f} s", "rows_per_s": round(rows_per_s, 1)}
     if kind not in ("scan", "prefill"):
         layers = 1 if wl.get("rotate") else wl["layers"]
         out["decode_steps_per_s"] = round(rows_per_s / (rows_per_layer * layers), 5)

@@ -28,9 +28,12 @@
  * are bit-reproducible and independent of the launch configuration):
  *   lambda = fl32(exp(fl(dt*A)))  (exp evaluated in double, rounded once)
  *   w      = fl(dt*x)
- *   quantized state (scale s, zero point z, codes c), the decay acting on
- *   the scale and the zero-point offset folded into the write term:
- *     ls = fl(lambda*s),  h'_n = fma(ls, c_n, fma(w, B_n, -fl(ls*z)))
+ *   quantized state (scale s, zero point z, codes c): each entry is
+ *   reconstructed, then the fp32 recurrence runs on it (the README's Setup
+ *   applies the decay and the write to the state; "Mamba state quantization
+ *   for inference", "Mixed precision spends bits on persistent channels":
+ *   reconstruct, recur in FP32, refit, write back):
+ *     hh_n = fl(s*fl(c_n - z)),  h'_n = fma(lambda, hh_n, fl(w*B_n))
  *   fp32 state:  h'_n = fma(lambda, h_n, fl(w*B_n))
  *   asymmetric refit: s' = fl(fl(max-min)/(2^b-1)), inv = fl(1/s'),
  *     z' = -rne(min*inv), c'_n = clamp(rne(h'_n*inv + z'), 0, 2^b-1)
@@ -41,7 +44,7 @@
  *     zero point of zero is stored as +0
  *   a zero or subnormal s' marks a degenerate row: asymmetric rows become the
  *     constant min (s' = |min|, z' = -sign(min), codes 0), symmetric rows zero
- *   y = sum_n C_n*r_n + D*x, r = the dequantized new row s'*(c'-z')
+ *   y = sum_n C_n*r_n + D*x, r = the dequantized new row s'*fl(c'-z')
  *     (default: the README reads the output from the quantized state) or the
  *     new row before rounding (SSQ_READ_PRE_QUANT); y and the delta-rule
  *     output o are outputs only, their summation order is unspecified.
@@ -104,9 +107,10 @@ typedef enum {
  * asymmetric uint8 codes with an fp32 scale and zero point, refit every step.
  * 9.44 bits per value.  A step is the scalar-decay delta rule in the rotated
  * coordinates: vt = Hs v (exact sum in double, rounded once), ut = k^T St,
- * wt = beta*(vt - alpha*ut), St' = alpha*St + k wt^T (fma order of the fp32
- * state for the half rows, of the quantized state for the uint8 rows), and
- * o = 2 Hs (St'^T q).  ssq_dequant returns S = 2 St Hs. */
+ * wt = beta*(vt - alpha*ut), St' = alpha*St + k wt^T on the stored rows in
+ * fp32 (half values, uint8 rows reconstructed as fl(s*fl(c - z))), each entry
+ * fma(alpha, St_ij, fl(k_i*wt_j)), and o = 2 Hs (St'^T q).  ssq_dequant
+ * returns S = 2 St Hs. */
 #define SSQ_DAMP_NHI 16
 
 typedef enum { SSQ_MAMBA2 = 0, SSQ_DELTA = 1 } ssq_kind;
@@ -136,7 +140,10 @@ typedef struct {
  *   SSQ_DAMP: codes, scale and zero hold the uint8 rows only,
  *          [batch][nheads][dk - SSQ_DAMP_NHI], and the half rows sit at
  *          hi_offset.  `rows` counts every key row.
- * Every region starts 256-byte aligned.  A zero state has all bytes 0. */
+ *   counter at counter_offset (quantized formats, else 0): the uint64 token
+ *          the next stochastically rounded call starts at (see ssq_set_rounding)
+ * Every region starts 256-byte aligned; ssq_alloc_state writes every byte of
+ * the storage (padding 0).  A zero state has all bytes 0. */
 typedef struct {
     size_t rows;
     size_t row_bytes;
@@ -145,6 +152,7 @@ typedef struct {
     size_t zero_offset;
     size_t total_bytes;
     size_t hi_offset; /* SSQ_DAMP: the half rows [batch][nheads][SSQ_DAMP_NHI][128]; else 0 */
+    size_t counter_offset; /* quantized formats: the stochastic-rounding token counter; else 0 */
 } ssq_layout;
 
 typedef struct ssq_state ssq_state; /* opaque handle: one layer's state */
@@ -171,9 +179,11 @@ ssq_status ssq_state_layout(const ssq_desc *desc, ssq_layout *layout);
 ssq_status ssq_alloc_state(const ssq_desc *desc, void *storage, const float *init, void *stream,
                            ssq_state **out);
 
-/* Destroy a handle; frees the storage only if the library allocated it.
- * NULL is accepted.  The caller must make sure no enqueued call still uses
- * the state. */
+/* Destroy a handle: the end of a request, whose fixed-size state is then no
+ * longer held ("Mamba state quantization for inference", "Recurrent state is
+ * fixed per request, not free": every active request owns one).  Frees the
+ * storage only if the library allocated it.  NULL is accepted.  The caller
+ * must make sure no enqueued call still uses the state. */
 ssq_status ssq_free_state(ssq_state *state);
 
 /* The description, storage pointer and layout of a state (any out pointer
@@ -192,19 +202,27 @@ ssq_status ssq_state_info(const ssq_state *state, ssq_desc *desc, void **storage
  * ctr/4 + 1 for `seed` (Steele, Lea and Flood, "Fast splittable pseudorandom
  * number generators", OOPSLA 2014), rows = the state's rows (for the two-tier
  * state, its uint8 rows).
- * `step` is the token the next call starts at: in SSQ_ROUND_STOCHASTIC mode
- * ssq_decode_step and ssq_delta_step use it and advance it by one, ssq_scan
- * uses step .. step+T-1 and advances it by T, at enqueue time (round to
- * nearest leaves it as it is).  The storage bytes plus this mode, seed and
- * step are all a state holds: restored into new storage under a new handle
- * they continue bit for bit.  A captured graph replays the tokens
- * it was captured with.  The fp32 state is never rounded:
- * SSQ_ROUND_STOCHASTIC on it gives SSQ_ERR_UNSUPPORTED.  Host-side only:
- * changes nothing already enqueued. */
-ssq_status ssq_set_rounding(ssq_state *state, int32_t mode, uint64_t seed, uint64_t step);
+ * `step` is the token the next call starts at.  It is kept in the state's
+ * storage (the layout's counter), so it belongs to the stream's order, not to
+ * the host: in SSQ_ROUND_STOCHASTIC mode ssq_decode_step and ssq_delta_step
+ * use it and advance it by one, ssq_scan and ssq_prefill use step .. step+T-1
+ * and advance it by T, with a one-thread kernel the call enqueues after its
+ * step kernels (round to nearest leaves it as it is, and enqueues none).  A call captured in a graph
+ * therefore draws the next tokens' uniforms at every replay.  The storage
+ * bytes plus this mode and seed are all a state holds: copied into new
+ * storage under a new handle with the same mode and seed they continue bit
+ * for bit.  The fp32 state is never rounded and has no counter:
+ * SSQ_ROUND_STOCHASTIC on it, or a non-zero step, gives SSQ_ERR_UNSUPPORTED.
+ * Mode and seed take effect for calls made after this one; the counter is
+ * written on `stream` (a one-thread kernel, so this call may also be
+ * captured). */
+ssq_status ssq_set_rounding(ssq_state *state, int32_t mode, uint64_t seed, uint64_t step, void *stream);
 
-/* The state's rounding mode, seed and next token (any out pointer may be NULL). */
-ssq_status ssq_get_rounding(const ssq_state *state, int32_t *mode, uint64_t *seed, uint64_t *step);
+/* The state's rounding mode, seed and next token (any out pointer may be
+ * NULL).  Reading the token copies it from device memory on `stream` and
+ * waits for the stream to reach that copy. */
+ssq_status ssq_get_rounding(const ssq_state *state, int32_t *mode, uint64_t *seed, uint64_t *step,
+                            void *stream);
 
 /* One Mamba-2 decode token for every row of the layer (README, Setup: decay
  * lambda = exp(dt*A) per head, write dt*B*x, per-row refit every step, round
@@ -218,9 +236,8 @@ ssq_status ssq_decode_step(ssq_state *state, const float *x, const float *dt, co
 
 /* T Mamba-2 tokens in one launch, the state rounded after every token (the
  * sequential per-token scan of the README's Setup, which rounds the state at
- * every step).  The state it leaves is bit-identical to T calls of
- * ssq_decode_step; y agrees to the order of its C.h sum (bit-identical too
- * for int4 and fp32 states, whose rows both kernels spread over the same lanes).
+ * every step).  The state it leaves and every y are bit-identical to T calls
+ * of ssq_decode_step, in every format.
  *   x [batch][T][nheads][P], dt [batch][T][nheads], B, C [batch][T][ngroups][N],
  *   A, D [nheads]; y [batch][T][nheads][P] is written. */
 ssq_status ssq_scan(ssq_state *state, int32_t T, const float *x, const float *dt, const float *A,
@@ -249,11 +266,10 @@ ssq_status ssq_prefill(ssq_state *state, int32_t T, int32_t chunk, const float *
  * ("Mamba state quantization for inference": the query reads the matrix,
  * decay and a delta-rule correction write the next version; the update
  * S_t = A_t S_(t-1) + W_t of "Quantization error returns on the next token"),
- * evaluated as u = k^T S (S_ij = s_i*(c_ij - z_i) taken as a real number,
- * products and sum in double, rounded once), w_j = fl(beta*fl(v_j - fl(alpha*u_j))),
- * S'_ij = fma(as_i, c_ij, fma(k_i, w_j, -fl(as_i*z_i))) with as_i = fl(alpha*s_i)
- * (fp32 state: fma(alpha, S_ij, fl(k_i*w_j))), then each key row refit and
- * rounded as above.
+ * evaluated on the reconstructed matrix S_ij = fl(s_i*fl(c_ij - z_i)) (the
+ * fp32 state as stored): u = k^T S (products and sum in double, rounded
+ * once), w_j = fl(beta*fl(v_j - fl(alpha*u_j))), S'_ij = fma(alpha, S_ij,
+ * fl(k_i*w_j)), then each key row refit and rounded as above.
  *   q, k [batch][nheads][dk], v [batch][nheads][dv], alpha, beta
  *   [batch][nheads]; o [batch][nheads][dv] is written. */
 ssq_status ssq_delta_step(ssq_state *state, const float *q, const float *k, const float *v,
@@ -264,11 +280,10 @@ ssq_status ssq_delta_step(ssq_state *state, const float *q, const float *k, cons
  * channel ("Mamba state quantization for inference" names KDA beside Gated
  * DeltaNet and reports persistence differing across KDA key channels):
  *   S' = (I - beta*k*k^T) * Diag(alpha) * S + beta*k*v^T,  o = S'^T q
- * evaluated as u = k^T Diag(alpha) S (S_ij = s_i*(c_ij - z_i) as a real
- * number, products and sum in double, rounded once), w_j = fl(beta*fl(v_j - u_j)),
- * S'_ij = fma(as_i, c_ij, fma(k_i, w_j, -fl(as_i*z_i))) with as_i =
- * fl(alpha_i*s_i) (fp32 state: fma(alpha_i, S_ij, fl(k_i*w_j))), then each key
- * row refit and rounded as above.
+ * evaluated on the reconstructed matrix S_ij = fl(s_i*fl(c_ij - z_i)):
+ * u = k^T Diag(alpha) S (products and sum in double, rounded once),
+ * w_j = fl(beta*fl(v_j - u_j)), S'_ij = fma(alpha_i, S_ij, fl(k_i*w_j)), then
+ * each key row refit and rounded as above.
  *   alpha [batch][nheads][dk] (each in (0, 1]); q, k, v, beta, o as in
  *   ssq_delta_step.  Errors as ssq_delta_step. */
 ssq_status ssq_kda_step(ssq_state *state, const float *q, const float *k, const float *v,
@@ -276,7 +291,11 @@ ssq_status ssq_kda_step(ssq_state *state, const float *q, const float *k, const 
                         void *stream);
 
 /* The fp32 value the state stands for, fl(s*fl(c - z)) per entry (the stored
- * fp32 for SSQ_FP32): out [batch][nheads][rows_per_head][row_len]. */
+ * fp32 for SSQ_FP32): the reconstruction every step starts from ("Mamba
+ * state quantization for inference", "Mixed precision spends bits on
+ * persistent channels": the low tier is reconstructed before the FP32
+ * recurrence; README, Setup: a row's value is its scale times its code
+ * offset by the zero point).  out [batch][nheads][rows_per_head][row_len]. */
 ssq_status ssq_dequant(const ssq_state *state, float *out, void *stream);
 
 /* A streaming copy of `bytes` bytes from device memory src to device memory dst,

@@ -53,7 +53,7 @@ class ssq_layout(ctypes.Structure):
     _fields_ = [("rows", ctypes.c_size_t), ("row_bytes", ctypes.c_size_t),
                 ("codes_offset", ctypes.c_size_t), ("scale_offset", ctypes.c_size_t),
                 ("zero_offset", ctypes.c_size_t), ("total_bytes", ctypes.c_size_t),
-                ("hi_offset", ctypes.c_size_t)]
+                ("hi_offset", ctypes.c_size_t), ("counter_offset", ctypes.c_size_t)]
 
 
 def _load():
@@ -93,9 +93,9 @@ def _load():
     L.ssq_kda_step.argtypes = [vp, f32p, f32p, f32p, f32p, f32p, f32p, ctypes.c_int32, vp]
     L.ssq_kda_step.restype = st
     u64 = ctypes.c_uint64
-    L.ssq_set_rounding.argtypes = [vp, ctypes.c_int32, u64, u64]
+    L.ssq_set_rounding.argtypes = [vp, ctypes.c_int32, u64, u64, vp]
     L.ssq_set_rounding.restype = st
-    L.ssq_get_rounding.argtypes = [vp, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(u64), ctypes.POINTER(u64)]
+    L.ssq_get_rounding.argtypes = [vp, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(u64), ctypes.POINTER(u64), vp]
     L.ssq_get_rounding.restype = st
     return L
 
@@ -234,15 +234,16 @@ def ssq_state_info(state: State):
     return d, ptr.value, lay
 
 
-def ssq_set_rounding(state: State, mode: int, seed: int = 0, step: int = 0):
-    """Round the state's codes to nearest or stochastically (seed, next token)."""
-    _check(lib.ssq_set_rounding(state.handle, mode, seed, step), "ssq_set_rounding")
+def ssq_set_rounding(state: State, mode: int, seed: int = 0, step: int = 0, stream=None):
+    """Round the state's codes to nearest or stochastically (seed; the next token is written to the
+    state's counter on ``stream``)."""
+    _check(lib.ssq_set_rounding(state.handle, mode, seed, step, _stream(stream)), "ssq_set_rounding")
 
 
-def ssq_get_rounding(state: State):
-    """(mode, seed, next token) of a state."""
+def ssq_get_rounding(state: State, stream=None):
+    """(mode, seed, next token) of a state; the token is read from the device on ``stream``."""
     m, sd, sp = ctypes.c_int32(), ctypes.c_uint64(), ctypes.c_uint64()
-    _check(lib.ssq_get_rounding(state.handle, ctypes.byref(m), ctypes.byref(sd), ctypes.byref(sp)),
+    _check(lib.ssq_get_rounding(state.handle, ctypes.byref(m), ctypes.byref(sd), ctypes.byref(sp), _stream(stream)),
            "ssq_get_rounding")
     return m.value, sd.value, sp.value
 

@@ -22,8 +22,7 @@ struct ssq_state {
     bool owned;
     int device;
     int32_t rounding; // ssq_rounding
-    uint64_t sr_seed; // stochastic rounding: generator seed
-    uint64_t sr_step; // stochastic rounding: the token the next call starts at
+    uint64_t sr_seed; // stochastic rounding: generator seed (the next token is in the storage)
 };
 
 namespace {
@@ -110,6 +109,12 @@ ssq_status check_desc(const ssq_desc* d, ssq_layout* lay)
         l.hi_offset = end;
         end = align256(end + hi_bytes);
     }
+    // quantized formats: the stochastic-rounding token counter
+    l.counter_offset = 0;
+    if (fmt_quant(d->format)) {
+        l.counter_offset = end;
+        end = align256(end + 8);
+    }
     l.total_bytes = end;
     if (lay) *lay = l;
     return SSQ_OK;
@@ -153,6 +158,10 @@ float* scale_ptr(const ssq_state* st)
 float* zero_ptr(const ssq_state* st)
 {
     return fmt_asym(st->desc.format) ? (float*)((uint8_t*)st->storage + st->lay.zero_offset) : nullptr;
+}
+uint64_t* counter_ptr(const ssq_state* st)
+{
+    return fmt_quant(st->desc.format) ? (uint64_t*)((uint8_t*)st->storage + st->lay.counter_offset) : nullptr;
 }
 uint16_t* hi_ptr(const ssq_state* st)
 {
@@ -213,7 +222,6 @@ ssq_status ssq_alloc_state(const ssq_desc* desc, void* storage, const float* ini
     st->storage = storage;
     st->rounding = SSQ_ROUND_NEAREST;
     st->sr_seed = 0;
-    st->sr_step = 0;
     if (!storage) {
         void* p = nullptr;
         e = hipMalloc(&p, lay.total_bytes);
@@ -226,7 +234,10 @@ ssq_status ssq_alloc_state(const ssq_desc* desc, void* storage, const float* ini
         st->owned = true;
     }
     hipStream_t hs = (hipStream_t)stream;
-    if (init) {
+    // every byte of the storage is written: zero first (padding, the token counter), then the
+    // quantized rows of `init`
+    e = ssq::launch_zero_fill(st->storage, lay.total_bytes, hs);
+    if (e == hipSuccess && init) {
         ssq::QArgs a{};
         a.codes = codes_ptr(st);
         a.scale = scale_ptr(st);
@@ -237,8 +248,6 @@ ssq_status ssq_alloc_state(const ssq_desc* desc, void* storage, const float* ini
         a.rows = (int64_t)lay.rows;
         e = desc->format == SSQ_DAMP ? ssq::launch_damp_rows(a, false, hs)
                                      : ssq::launch_rows(desc->format, a, false, hs);
-    } else {
-        e = ssq::launch_zero_fill(st->storage, lay.total_bytes, hs);
     }
     if (e != hipSuccess) {
         if (st->owned) (void)hipFree(st->storage);
@@ -267,42 +276,59 @@ ssq_status ssq_state_info(const ssq_state* st, ssq_desc* desc, void** storage, s
     return ok();
 }
 
-// the stochastic-rounding arguments of the next call on a state
+// the stochastic-rounding arguments of the next call on a state (the launcher sets the
+// call's wave count and the tokens it consumes)
 static ssq::SrArgs sr_args(const ssq_state* st)
 {
     ssq::SrArgs r{};
     r.on = st->rounding == SSQ_ROUND_STOCHASTIC;
     r.seed = st->sr_seed;
-    r.step = st->sr_step;
     r.rows = grid_rows(st);
+    r.ctr = counter_ptr(st);
     return r;
 }
 
-// a call that was enqueued consumed `tokens` tokens of the state's random stream
-static void advance(ssq_state* st, uint64_t tokens)
+// after a stochastically rounded call's step kernels: the state's next token moves on
+static ssq_status advance(const ssq_state* st, uint64_t tokens, hipStream_t stream)
 {
-    if (st->rounding == SSQ_ROUND_STOCHASTIC) st->sr_step += tokens;
+    if (st->rounding != SSQ_ROUND_STOCHASTIC) return ok();
+    return from_hip(ssq::launch_advance_counter(counter_ptr(st), tokens, stream), "token counter launch");
 }
 
-ssq_status ssq_set_rounding(ssq_state* st, int32_t mode, uint64_t seed, uint64_t step)
+ssq_status ssq_set_rounding(ssq_state* st, int32_t mode, uint64_t seed, uint64_t step, void* stream)
 {
     SSQ_REQUIRE(st, SSQ_ERR_INVALID_ARG, "state is NULL");
     SSQ_REQUIRE(mode == SSQ_ROUND_NEAREST || mode == SSQ_ROUND_STOCHASTIC, SSQ_ERR_INVALID_ARG,
                 "unknown rounding mode");
     SSQ_REQUIRE(mode == SSQ_ROUND_NEAREST || fmt_quant(st->desc.format), SSQ_ERR_UNSUPPORTED,
                 "the fp32 state is not rounded");
+    SSQ_REQUIRE(mode == SSQ_ROUND_STOCHASTIC || step == 0 || fmt_quant(st->desc.format), SSQ_ERR_UNSUPPORTED,
+                "the fp32 state has no token counter");
+    ssq_status s = check_device(st);
+    if (s != SSQ_OK) return s;
+    if (fmt_quant(st->desc.format)) {
+        s = from_hip(ssq::launch_set_counter(counter_ptr(st), step, (hipStream_t)stream), "token counter launch");
+        if (s != SSQ_OK) return s;
+    }
     st->rounding = mode;
     st->sr_seed = seed;
-    st->sr_step = step;
     return ok();
 }
 
-ssq_status ssq_get_rounding(const ssq_state* st, int32_t* mode, uint64_t* seed, uint64_t* step)
+ssq_status ssq_get_rounding(const ssq_state* st, int32_t* mode, uint64_t* seed, uint64_t* step, void* stream)
 {
     SSQ_REQUIRE(st, SSQ_ERR_INVALID_ARG, "state is NULL");
+    uint64_t next = 0;
+    if (step && fmt_quant(st->desc.format)) {
+        ssq_status s = check_device(st);
+        if (s != SSQ_OK) return s;
+        hipError_t e = hipMemcpyAsync(&next, counter_ptr(st), sizeof next, hipMemcpyDeviceToHost, (hipStream_t)stream);
+        if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+        if (e != hipSuccess) return from_hip(e, "reading the token counter");
+    }
     if (mode) *mode = st->rounding;
     if (seed) *seed = st->sr_seed;
-    if (step) *step = st->sr_step;
+    if (step) *step = next;
     return ok();
 }
 
@@ -349,8 +375,7 @@ ssq_status ssq_decode_step(ssq_state* st, const float* x, const float* dt, const
     s = from_hip(ssq::launch_m2_step(st->desc.format, a, readout == SSQ_READ_PRE_QUANT, num_cus(st->device),
                                      (hipStream_t)stream),
                  "decode step launch");
-    if (s == SSQ_OK) advance(st, 1);
-    return s;
+    return s == SSQ_OK ? advance(st, 1, (hipStream_t)stream) : s;
 }
 
 ssq_status ssq_scan(ssq_state* st, int32_t T, const float* x, const float* dt, const float* A, const float* B,
@@ -364,8 +389,7 @@ ssq_status ssq_scan(ssq_state* st, int32_t T, const float* x, const float* dt, c
     a.sr = sr_args(st);
     s = from_hip(ssq::launch_m2_scan(st->desc.format, a, readout == SSQ_READ_PRE_QUANT, (hipStream_t)stream),
                  "scan launch");
-    if (s == SSQ_OK) advance(st, (uint64_t)T);
-    return s;
+    return s == SSQ_OK ? advance(st, (uint64_t)T, (hipStream_t)stream) : s;
 }
 
 ssq_status ssq_prefill(ssq_state* st, int32_t T, int32_t chunk, const float* x, const float* dt, const float* A,
@@ -381,8 +405,7 @@ ssq_status ssq_prefill(ssq_state* st, int32_t T, int32_t chunk, const float* x, 
     s = from_hip(ssq::launch_m2_prefill(st->desc.format, a, chunk, readout == SSQ_READ_PRE_QUANT,
                                         (hipStream_t)stream),
                  "prefill launch");
-    if (s == SSQ_OK) advance(st, (uint64_t)T);
-    return s;
+    return s == SSQ_OK ? advance(st, (uint64_t)T, (hipStream_t)stream) : s;
 }
 
 static ssq_status delta_common(ssq_state* st, const float* q, const float* k, const float* v, const float* alpha,
@@ -421,8 +444,7 @@ static ssq_status delta_common(ssq_state* st, const float* q, const float* k, co
         s = from_hip(ssq::launch_delta_step(st->desc.format, a, readout == SSQ_READ_PRE_QUANT, (hipStream_t)stream),
                      kda ? "KDA step launch" : "delta step launch");
     }
-    if (s == SSQ_OK) advance(st, 1);
-    return s;
+    return s == SSQ_OK ? advance(st, 1, (hipStream_t)stream) : s;
 }
 
 ssq_status ssq_delta_step(ssq_state* st, const float* q, const float* k, const float* v, const float* alpha,

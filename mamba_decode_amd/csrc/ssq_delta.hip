@@ -42,11 +42,15 @@ __device__ __forceinline__ void store_row_piece(uint8_t* rows_base, uint32_t row
     buf_store_words<NW, kAuxStoreWhole>(make_rsrc(rows_base, rows_bytes), off, 0u, w);
 }
 
-// Partial rows in LDS: element j of row group r sits at r*kPartPitch + j + j/16.  A wave
-// writes 8 row groups x 8 segments of 16 columns at once; without the padding every lane
-// of it lands on the same bank.
-constexpr int kPartPitch = 136;
-__device__ __forceinline__ int part_idx(int r, int j) { return r * kPartPitch + j + (j >> 4); }
+// Partial rows in LDS: column j = 16*part + e of row group r (the thread (r, part) writes it)
+// sits at e*kPartPitch + 8*r + part.  The 64 lanes of a wave that write column offset e hold
+// eight consecutive row groups and all eight parts, so they write 64 consecutive elements;
+// the 64 lanes that read row group r in the column sums hold columns j = t .. t+63, i.e.
+// e = 0..15 and four parts, at e*kPartPitch + part: with kPartPitch = 4 (mod 32) that is
+// every residue mod 64 exactly once for floats and every even residue twice for doubles, so
+// neither the writes nor the reads have a bank conflict.
+constexpr int kPartPitch = 260;
+__device__ __forceinline__ int part_idx(int r, int j) { return (j & 15) * kPartPitch + 8 * r + (j >> 4); }
 
 // The matrix the step starts from, reconstructed in fp32 (fl(s_i*fl(c_ij - z_i)) for a
 // quantized key row), stays in registers from the u reduction to the update: each entry is
@@ -60,7 +64,7 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_delta_step(DeltaArgs a
     constexpr int LPR = 8, E = 16, RG = 32, KR = 4; // lanes per row, columns per lane, row groups, rows per thread
     constexpr int NW = Tr::quant ? E * Tr::bits / 32 : E;
     constexpr int ROWB = Tr::quant ? 128 * Tr::bits / 8 : 512;
-    __shared__ double part_u[RG * kPartPitch]; // reused for the fp32 partials of o
+    __shared__ double part_u[16 * kPartPitch]; // reused for the fp32 partials of o
     __shared__ __attribute__((aligned(16))) float w_s[128];
 
     const int t = threadIdx.x;
@@ -68,6 +72,7 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_delta_step(DeltaArgs a
     const int64_t mat = blockIdx.x;
     const int64_t mrow0 = mat * 128; // first state row of the matrix
     const float alpha = KDA ? 0.0f : a.alpha[mat], beta = a.beta[mat];
+    const uint64_t sr_step = SR ? sr_token(a.sr) : 0;
 
     float kk[KR], qq[KR], al[KR];
     float Sh[KR][E]; // this thread's 16 columns of its four key rows, in fp32
@@ -175,7 +180,7 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_delta_step(DeltaArgs a
             RowGrid g;
             float f[E];
             // stochastic rounding: this lane's first counter, (step*rows + row)*128 + j0
-            const uint64_t ctr0 = SR ? ((a.sr.step * (uint64_t)a.sr.rows + (uint64_t)row) * 128u + (uint64_t)j0) : 0;
+            const uint64_t ctr0 = SR ? ((sr_step * (uint64_t)a.sr.rows + (uint64_t)row) * 128u + (uint64_t)j0) : 0;
             if (__all(refit_fast<F, SR>(mn, mx, am, g))) {
                 if constexpr (SR) {
                     round_codes_sr<F, E, true>(S, g, a.sr.seed, ctr0, f);
@@ -328,7 +333,7 @@ __global__ __launch_bounds__(256, SSQ_DAMP_WAVES) void k_damp_step(DeltaArgs a)
 {
     constexpr int F = INT8_ASYM;
     constexpr int LPR = 8, E = 16, RG = 32, KR = 4, NW = 4, ROWB = 128;
-    __shared__ double part_u[RG * kPartPitch]; // reused for the fp32 partials of the readout
+    __shared__ double part_u[16 * kPartPitch]; // reused for the fp32 partials of the readout
     __shared__ __attribute__((aligned(16))) float w_s[128];
     __shared__ double xch[128];
 
@@ -338,6 +343,7 @@ __global__ __launch_bounds__(256, SSQ_DAMP_WAVES) void k_damp_step(DeltaArgs a)
     const int64_t mrow0 = mat * 128;
     const float alpha = a.alpha[mat], beta = a.beta[mat];
     const bool hi_wave = rg < kNhi; // row k = 0 of this thread is a half row
+    const uint64_t sr_step = SR ? sr_token(a.sr) : 0;
 
     const double vj = t < 128 ? (double)a.v[mrow0 + t] : 0.0;
 
@@ -455,7 +461,7 @@ __global__ __launch_bounds__(256, SSQ_DAMP_WAVES) void k_damp_step(DeltaArgs a)
             mx = group_max<LPR>(mx);
             RowGrid g;
             float f[E];
-            const uint64_t ctr0 = SR ? ((a.sr.step * (uint64_t)a.sr.rows + (uint64_t)lrow) * 128u + (uint64_t)j0) : 0;
+            const uint64_t ctr0 = SR ? ((sr_step * (uint64_t)a.sr.rows + (uint64_t)lrow) * 128u + (uint64_t)j0) : 0;
             if (__all(refit_fast<F, SR>(mn, mx, 0.0f, g))) {
                 if constexpr (SR) {
                     round_codes_sr<F, E, true>(S, g, a.sr.seed, ctr0, f);

@@ -26,6 +26,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "ssq_internal.h"
+
 namespace ssq {
 
 enum Format : int { FP32 = 0, INT8_SYM = 1, INT8_ASYM = 2, INT4_SYM = 3, INT4_ASYM = 4 };
@@ -409,6 +411,13 @@ __device__ __forceinline__ void sr_decide8_rd(const float* h, float A, float M, 
                    "+v"(kz[7])
                  : "v"(h[0]), "v"(h[1]), "v"(h[2]), "v"(h[3]), "v"(h[4]), "v"(h[5]), "v"(h[6]), "v"(h[7]),
                    "v"(A), "v"(M));
+}
+
+// The token the call's stochastic rounding starts at: the state's counter, read at the start
+// of every wave (the call's own counter kernel advances it after the step kernels).
+__device__ __forceinline__ uint64_t sr_token(const SrArgs& a)
+{
+    return *a.ctr;
 }
 
 template <int F, int E, bool FAST>

@@ -7,13 +7,16 @@
 
 namespace ssq {
 
-// stochastic rounding of the codes: off, or entry n of state row r at token t
-// draws the uniform of SplitMix64 output number ((step + t)*rows + r)*128 + n + 1
+// stochastic rounding of the codes: off, or entry n of state row r at token step + t
+// draws the uniform of counter ((step + t)*rows + r)*128 + n.  `step` is the state's token
+// counter in device memory (*ctr), read by every wave at its start; the call advances it with
+// a one-thread kernel enqueued after its step kernels (launch_advance_counter), so that a
+// call replayed from a graph draws the next tokens' uniforms.
 struct SrArgs {
     int on;
     uint64_t seed;
-    uint64_t step;
     int64_t rows;
+    const uint64_t* ctr; // the state's next token
 };
 
 // Mamba-2 decode step / scan of one layer
@@ -74,5 +77,7 @@ hipError_t launch_delta_step(int fmt, DeltaArgs a, bool pre, hipStream_t st);
 hipError_t launch_damp_step(DeltaArgs a, bool pre, hipStream_t st);
 hipError_t launch_damp_rows(QArgs a, bool dequant, hipStream_t st);
 hipError_t launch_stream_copy(void* dst, const void* src, int64_t bytes, hipStream_t st);
+hipError_t launch_set_counter(uint64_t* ctr, uint64_t value, hipStream_t st);
+hipError_t launch_advance_counter(uint64_t* ctr, uint64_t tokens, hipStream_t st);
 
 } // namespace ssq

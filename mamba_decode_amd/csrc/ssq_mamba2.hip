@@ -303,6 +303,7 @@ __global__ __launch_bounds__(256, W) void k_m2_step(M2Args a, int64_t it_base)
     const int64_t it0 = it_base + wave_id() * K; // round-robin over the XCDs: grouping the
     // decode's workgroups by XCD (as the scan does) made it 7-8% slower
     if (it0 + K > a.total_iters) return;
+    const uint64_t sr_step = SR ? sr_token(a.sr) : 0;
 
     const int ipH = a.P / RPW; // iterations per head (RPW divides P)
     int64_t bh = it0 / ipH;
@@ -425,7 +426,7 @@ __global__ __launch_bounds__(256, W) void k_m2_step(M2Args a, int64_t it_base)
             RowGrid g;
             // this lane's first counter of stochastic rounding: (step*rows + row)*128 + part*E
             const uint64_t ctr0 =
-                SR ? ((a.sr.step * (uint64_t)a.sr.rows + (uint64_t)(row_first + (int64_t)i * RPW + sub)) * 128u +
+                SR ? ((sr_step * (uint64_t)a.sr.rows + (uint64_t)(row_first + (int64_t)i * RPW + sub)) * 128u +
                       (uint64_t)(part * E))
                    : 0;
             float yv;
@@ -486,6 +487,7 @@ __global__ __launch_bounds__(256, PRE ? SSQ_SCAN_WAVES - 1 : SSQ_SCAN_WAVES) voi
     const int lane = threadIdx.x & 63, sub = lane / LPR, part = lane % LPR;
     const int64_t it = wave_id_xcd_grouped();
     if (it >= a.total_iters) return;
+    const uint64_t sr_step = SR ? sr_token(a.sr) : 0;
     const int64_t row0 = it * RPW;
     const int64_t bh = row0 / a.P;
     const int b = (int)(bh / a.H), h = (int)(bh % a.H);
@@ -563,7 +565,7 @@ __global__ __launch_bounds__(256, PRE ? SSQ_SCAN_WAVES - 1 : SSQ_SCAN_WAVES) voi
         float yv;
         if constexpr (Tr::quant) {
             const uint64_t ctr0 =
-                SR ? (((a.sr.step + (uint64_t)t) * (uint64_t)a.sr.rows + (uint64_t)row) * 128u + (uint64_t)(part * E))
+                SR ? (((sr_step + (uint64_t)t) * (uint64_t)a.sr.rows + (uint64_t)row) * 128u + (uint64_t)(part * E))
                    : 0;
             yv = RS::template run_q<LAST, SR, CH>(cf, s, lam, w, dx, in, ow, gr, a.sr.seed, ctr0);
             s = gr.s;
@@ -617,6 +619,7 @@ __global__ __launch_bounds__(256, PRE ? SSQ_PREFILL_WAVES - 1 : SSQ_PREFILL_WAVE
     const int lane = threadIdx.x & 63, sub = lane / LPR, part = lane % LPR;
     const int64_t it = wave_id_xcd_grouped();
     if (it >= a.total_iters) return;
+    const uint64_t sr_step = SR ? sr_token(a.sr) : 0;
     const int64_t row0 = it * RPW;
     const int64_t bh = row0 / a.P;
     const int b = (int)(bh / a.H), h = (int)(bh % a.H);
@@ -688,7 +691,7 @@ __global__ __launch_bounds__(256, PRE ? SSQ_PREFILL_WAVES - 1 : SSQ_PREFILL_WAVE
         if (end) {
             RowGrid gr;
             const uint64_t ctr0 =
-                SR ? (((a.sr.step + (uint64_t)t) * (uint64_t)a.sr.rows + (uint64_t)row) * 128u + (uint64_t)(part * E))
+                SR ? (((sr_step + (uint64_t)t) * (uint64_t)a.sr.rows + (uint64_t)row) * 128u + (uint64_t)(part * E))
                    : 0;
             RS::template requant<SR>(hv, gr, a.sr.seed, ctr0);
             pack_codes<F, E>(hv, cw);
@@ -788,6 +791,18 @@ __global__ __launch_bounds__(256) void k_dequant_rows(QArgs a)
         }
     }
     store_f32<E>(a.out + row * 128 + part * E, h);
+}
+
+// The state's stochastic-rounding token counter set to `value`, or advanced by `tokens` after
+// a call's step kernels (one thread, through a vector atomic; kernels rather than memsets or
+// copies, so that the calls may also sit in a captured graph).
+__global__ __launch_bounds__(64) void k_set_counter(uint64_t* ctr, uint64_t value)
+{
+    if (threadIdx.x == 0 && blockIdx.x == 0) atomicExch(reinterpret_cast<unsigned long long*>(ctr), value);
+}
+__global__ __launch_bounds__(64) void k_advance_counter(uint64_t* ctr, uint64_t tokens)
+{
+    if (threadIdx.x == 0 && blockIdx.x == 0) atomicAdd(reinterpret_cast<unsigned long long*>(ctr), tokens);
 }
 
 __global__ __launch_bounds__(256) void k_zero_fill(uint4* p, int64_t n16)
@@ -1002,6 +1017,18 @@ hipError_t launch_rows(int fmt, QArgs a, bool dequant, hipStream_t st)
     case INT4_ASYM: return launch_rows_f<INT4_ASYM>(a, dequant, st);
     }
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_set_counter(uint64_t* ctr, uint64_t value, hipStream_t st)
+{
+    hipLaunchKernelGGL(k_set_counter, dim3(1), dim3(64), 0, st, ctr, value);
+    return hipGetLastError();
+}
+
+hipError_t launch_advance_counter(uint64_t* ctr, uint64_t tokens, hipStream_t st)
+{
+    hipLaunchKernelGGL(k_advance_counter, dim3(1), dim3(64), 0, st, ctr, tokens);
+    return hipGetLastError();
 }
 
 hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t st)

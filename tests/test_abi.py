@@ -42,20 +42,23 @@ def test_layout(fmt, row_bytes):
     lay = ssq.ssq_state_layout(d)
     rows = 3 * 5 * 48
     assert lay.rows == rows and lay.row_bytes == row_bytes and lay.codes_offset == 0
-    for off in (lay.codes_offset, lay.scale_offset, lay.zero_offset, lay.total_bytes):
+    for off in (lay.codes_offset, lay.scale_offset, lay.zero_offset, lay.counter_offset, lay.total_bytes):
         assert off % 256 == 0
     if fmt == "fp32":
-        assert lay.scale_offset == 0 and lay.zero_offset == 0
+        assert lay.scale_offset == 0 and lay.zero_offset == 0 and lay.counter_offset == 0
         assert lay.total_bytes >= rows * 512
     else:
         assert lay.scale_offset >= rows * row_bytes
         if fmt.endswith("asym"):
             assert lay.zero_offset >= lay.scale_offset + 4 * rows
-            assert lay.total_bytes >= lay.zero_offset + 4 * rows
+            assert lay.counter_offset >= lay.zero_offset + 4 * rows
         else:
-            assert lay.zero_offset == 0 and lay.total_bytes >= lay.scale_offset + 4 * rows
+            assert lay.zero_offset == 0 and lay.counter_offset >= lay.scale_offset + 4 * rows
+        # the stochastic-rounding token counter (8 bytes)
+        assert lay.total_bytes >= lay.counter_offset + 8
     assert ssq.ssq_state_bytes(d) == lay.total_bytes
-    assert lay.total_bytes - (rows * row_bytes + (0 if fmt == "fp32" else 4 * rows * (2 if "asym" in fmt else 1))) < 3 * 256
+    payload = rows * row_bytes + (0 if fmt == "fp32" else 4 * rows * (2 if "asym" in fmt else 1) + 8)
+    assert lay.total_bytes - payload < 4 * 256
 
 
 def test_state_sizes_match_the_pages():
@@ -72,13 +75,14 @@ def test_state_sizes_match_the_pages():
 
 
 def test_quantized_footprints():
-    # int4 asym Mamba-2 370m-shaped layer at batch 256: 524288 rows x (64 B codes + 8 B metadata)
+    # int4 asym Mamba-2 370m-shaped layer at batch 256: 524288 rows x (64 B codes + 8 B metadata),
+    # plus the 256-byte region of the stochastic-rounding token counter
     d = ssq.make_desc(ssq.SSQ_MAMBA2, "int4_asym", 256, 32, 64)
-    assert ssq.ssq_state_bytes(d) == 524288 * 72
+    assert ssq.ssq_state_bytes(d) == 524288 * 72 + 256
     # int8 asym delta layer: 136 of 512 bytes per fp32 row
     d8 = ssq.make_desc(ssq.SSQ_DELTA, "int8_asym", 256, 32, 128)
     d32 = ssq.make_desc(ssq.SSQ_DELTA, "fp32", 256, 32, 128)
-    assert ssq.ssq_state_bytes(d8) * 512 == ssq.ssq_state_bytes(d32) * 136
+    assert (ssq.ssq_state_bytes(d8) - 256) * 512 == ssq.ssq_state_bytes(d32) * 136
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -122,8 +126,8 @@ def test_null_arguments_are_rejected_before_any_device_call():
     assert L.ssq_kda_step(None, None, None, None, None, None, None, 0, None) == ssq.SSQ_ERR_INVALID_ARG
     assert L.ssq_dequant(None, None, None) == ssq.SSQ_ERR_INVALID_ARG
     assert L.ssq_state_info(None, None, None, None) == ssq.SSQ_ERR_INVALID_ARG
-    assert L.ssq_set_rounding(None, ssq.SSQ_ROUND_STOCHASTIC, 1, 0) == ssq.SSQ_ERR_INVALID_ARG
-    assert L.ssq_get_rounding(None, None, None, None) == ssq.SSQ_ERR_INVALID_ARG
+    assert L.ssq_set_rounding(None, ssq.SSQ_ROUND_STOCHASTIC, 1, 0, None) == ssq.SSQ_ERR_INVALID_ARG
+    assert L.ssq_get_rounding(None, None, None, None, None) == ssq.SSQ_ERR_INVALID_ARG
     assert L.ssq_free_state(None) == ssq.SSQ_OK
 
 
@@ -152,11 +156,12 @@ def test_two_tier_layout():
     assert lay.rows == mats * 128 and lay.row_bytes == 128
     assert lay.scale_offset >= lo * 128 and lay.zero_offset >= lay.scale_offset + 4 * lo
     assert lay.hi_offset >= lay.zero_offset + 4 * lo
-    assert lay.total_bytes >= lay.hi_offset + mats * 16 * 128 * 2
-    for off in (lay.scale_offset, lay.zero_offset, lay.hi_offset, lay.total_bytes):
+    assert lay.counter_offset >= lay.hi_offset + mats * 16 * 128 * 2
+    assert lay.total_bytes >= lay.counter_offset + 8
+    for off in (lay.scale_offset, lay.zero_offset, lay.hi_offset, lay.counter_offset, lay.total_bytes):
         assert off % 256 == 0
     payload = lo * (128 + 8) + mats * 16 * 256
-    assert lay.total_bytes - payload < 4 * 256
+    assert lay.total_bytes - payload < 5 * 256
     assert payload * 8 / (mats * 128 * 128) == pytest.approx(9.4375)
     bad = ssq.make_desc(ssq.SSQ_MAMBA2, "damp", 1, 2, 64)
     h = ctypes.c_void_p()

@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import synth
 
 pytestmark = pytest.mark.gpu
@@ -107,22 +108,63 @@ def test_prefill_in_a_graph():
     _check_replays(st, start, eager_state, eager_y, y, g, "prefill")
 
 
-def test_stochastic_decode_in_a_graph():
-    """The counter of stochastic rounding is an argument fixed at capture: every replay draws
-    the uniforms of the token it was captured with."""
-    B, H, P = 4, 8, 64
+def test_stochastic_decode_in_a_graph_draws_the_next_token_per_replay():
+    """The token counter of stochastic rounding lives in the state's storage and every call
+    advances it on the device, so successive replays of one captured decode step draw the
+    uniforms of successive tokens: each replay equals the oracle's step at its own token."""
+    B, H, P, fmt = 4, 8, 64, "int4_asym"
     rows = B * H * P
     seed, step0 = 777, 5
     say("graph stochastic decode")
-    st = par.new_gpu_state(ssq.make_desc(ssq.SSQ_MAMBA2, "int4_asym", B, H, P), synth.init_state(75, 0, rows, 128))
-    x, dt, Bm, Cm, A, D = (par.dev(a) for a in synth.mamba2_step_inputs(75, 0, B, H, 1, P, 128))
+    init = synth.init_state(75, 0, rows, 128)
+    st = par.new_gpu_state(ssq.make_desc(ssq.SSQ_MAMBA2, fmt, B, H, P), init)
+    ost = oracle.make_state(fmt, rows, 128, init)
+    xn, dtn, Bn, Cn, An, Dn = synth.mamba2_step_inputs(75, 0, B, H, 1, P, 128)
+    x, dt, Bm, Cm, A, D = (par.dev(a) for a in (xn, dtn, Bn, Cn, An, Dn))
     y = torch.empty(x.shape, dtype=torch.float32, device="cuda")
-    start = st.storage.clone()
     ssq.ssq_set_rounding(st, ssq.SSQ_ROUND_STOCHASTIC, seed, step0)
-    g = _capture(lambda: ssq.ssq_decode_step(st, x, dt, A, Bm, Cm, D, y))  # warm call: step0, captured: step0 + 1
-    st.storage.copy_(start)
-    ssq.ssq_set_rounding(st, ssq.SSQ_ROUND_STOCHASTIC, seed, step0 + 1)
-    ssq.ssq_decode_step(st, x, dt, A, Bm, Cm, D, y)
-    torch.cuda.synchronize()
-    eager_state, eager_y = st.storage.clone(), y.clone()
-    _check_replays(st, start, eager_state, eager_y, y, g, "stochastic decode")
+    g = _capture(lambda: ssq.ssq_decode_step(st, x, dt, A, Bm, Cm, D, y))  # the warm call runs token step0
+    oracle.mamba2_step(ost, xn, dtn, An, Bn, Cn, Dn, sr=(seed, step0))
+    assert ssq.ssq_get_rounding(st)[2] == step0 + 1
+    prev = None
+    for rep in range(4):
+        y.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        yo = oracle.mamba2_step(ost, xn, dtn, An, Bn, Cn, Dn, sr=(seed, step0 + 1 + rep))
+        gs = par.read_gpu_state(st, fmt)
+        assert np.array_equal(gs["code"], ost.code), f"replay {rep}: codes differ from the oracle's token"
+        assert np.array_equal(gs["scale"].view(np.uint32), ost.scale.view(np.uint32)), rep
+        assert np.array_equal(gs["zero"], ost.zero), rep
+        assert par.block_rel(y.cpu().numpy(), yo, axis=2) <= 1e-5, rep
+        assert ssq.ssq_get_rounding(st)[2] == step0 + 2 + rep
+        # the same inputs at a new token: the rounding draws differ from the last replay's
+        cur = gs["code"].copy()
+        if prev is not None:
+            assert not np.array_equal(cur, prev)
+        prev = cur
+
+
+def test_stochastic_scan_in_a_graph_advances_by_T_per_replay():
+    B, H, P, T, fmt = 2, 4, 32, 6, "int8_asym"
+    rows = B * H * P
+    seed, step0 = 4321, 9
+    say("graph stochastic scan")
+    init = synth.init_state(76, 0, rows, 128)
+    st = par.new_gpu_state(ssq.make_desc(ssq.SSQ_MAMBA2, fmt, B, H, P), init)
+    ost = oracle.make_state(fmt, rows, 128, init)
+    arrs = synth.mamba2_scan_inputs(76, 0, B, T, H, 1, P, 128)
+    x, dt, Bm, Cm, A, D = (par.dev(a) for a in arrs)
+    y = torch.empty(x.shape, dtype=torch.float32, device="cuda")
+    ssq.ssq_set_rounding(st, ssq.SSQ_ROUND_STOCHASTIC, seed, step0)
+    g = _capture(lambda: ssq.ssq_scan(st, T, x, dt, A, Bm, Cm, D, y))
+    oracle.mamba2_scan(ost, *arrs[:2], arrs[4], arrs[2], arrs[3], arrs[5], sr=(seed, step0))
+    for rep in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        yo = oracle.mamba2_scan(ost, *arrs[:2], arrs[4], arrs[2], arrs[3], arrs[5], sr=(seed, step0 + T * (rep + 1)))
+        gs = par.read_gpu_state(st, fmt)
+        assert np.array_equal(gs["code"], ost.code), rep
+        assert np.array_equal(gs["scale"].view(np.uint32), ost.scale.view(np.uint32)), rep
+        assert par.block_rel(y.cpu().numpy(), yo, axis=(1, 3)) <= 1e-5, rep
+        assert ssq.ssq_get_rounding(st)[2] == step0 + T * (rep + 2)
