@@ -42,15 +42,18 @@ __device__ __forceinline__ void store_row_piece(uint8_t* rows_base, uint32_t row
     buf_store_words<NW, kAuxStoreWhole>(make_rsrc(rows_base, rows_bytes), off, 0u, w);
 }
 
-// Partial rows in LDS: column j = 16*part + e of row group r (the thread (r, part) writes it)
-// sits at e*kPartPitch + 8*r + part.  The 64 lanes of a wave that write column offset e hold
-// eight consecutive row groups and all eight parts, so they write 64 consecutive elements;
-// the 64 lanes that read row group r in the column sums hold columns j = t .. t+63, i.e.
-// e = 0..15 and four parts, at e*kPartPitch + part: with kPartPitch = 4 (mod 32) that is
-// every residue mod 64 exactly once for floats and every even residue twice for doubles, so
-// neither the writes nor the reads have a bank conflict.
-constexpr int kPartPitch = 260;
-__device__ __forceinline__ int part_idx(int r, int j) { return (j & 15) * kPartPitch + 8 * r + (j >> 4); }
+// Partial rows in LDS.  Thread (r, part) writes columns j = 16*part .. 16*part + 15 of row
+// group r as consecutive elements (16-byte writes), u in double at r*144 + part*18 + (j & 15)
+// and o in float at r*160 + part*20 + (j & 15).  A 16-byte write instruction is served 16
+// lanes at a time (two row groups, eight parts); with these pitches the 16 lanes' four-bank
+// windows tile the 64 banks exactly (double: 2*(144 r + 18 part) mod 64; float: 160 r +
+// 20 part mod 64), so the writes have no bank conflict.
+constexpr int kPartPitchU = 144, kPartStrideU = 18;
+constexpr int kPartPitchO = 160, kPartStrideO = 20;
+__device__ __forceinline__ int part_idx(int r, int j) { return r * kPartPitchU + (j >> 4) * kPartStrideU + (j & 15); }
+__device__ __forceinline__ int part_idx_o(int r, int j) { return r * kPartPitchO + (j >> 4) * kPartStrideO + (j & 15); }
+constexpr int kPartElems = 32 * kPartPitchU; // doubles; the float rows of o fit in the same bytes
+static_assert(32 * kPartPitchO <= 2 * kPartElems, "o's partial rows fit in u's buffer");
 
 // The matrix the step starts from, reconstructed in fp32 (fl(s_i*fl(c_ij - z_i)) for a
 // quantized key row), stays in registers from the u reduction to the update: each entry is
@@ -64,7 +67,7 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_delta_step(DeltaArgs a
     constexpr int LPR = 8, E = 16, RG = 32, KR = 4; // lanes per row, columns per lane, row groups, rows per thread
     constexpr int NW = Tr::quant ? E * Tr::bits / 32 : E;
     constexpr int ROWB = Tr::quant ? 128 * Tr::bits / 8 : 512;
-    __shared__ double part_u[16 * kPartPitch]; // reused for the fp32 partials of o
+    __shared__ __attribute__((aligned(16))) double part_u[kPartElems]; // reused for the fp32 partials of o
     __shared__ __attribute__((aligned(16))) float w_s[128];
 
     const int t = threadIdx.x;
@@ -221,12 +224,12 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_delta_step(DeltaArgs a
     // o = S'^T q: 32 partial rows meet in LDS
     float* part_o = reinterpret_cast<float*>(part_u);
 #pragma unroll
-    for (int e = 0; e < E; ++e) part_o[part_idx(rg, j0 + e)] = op[e];
+    for (int e = 0; e < E; ++e) part_o[part_idx_o(rg, j0 + e)] = op[e];
     __syncthreads();
     if (t < 128) {
         float acc = 0.0f;
 #pragma unroll 8
-        for (int r = 0; r < RG; ++r) acc += part_o[part_idx(r, t)];
+        for (int r = 0; r < RG; ++r) acc += part_o[part_idx_o(r, t)];
         a.o[mrow0 + t] = acc;
     }
 }
@@ -333,7 +336,7 @@ __global__ __launch_bounds__(256, SSQ_DAMP_WAVES) void k_damp_step(DeltaArgs a)
 {
     constexpr int F = INT8_ASYM;
     constexpr int LPR = 8, E = 16, RG = 32, KR = 4, NW = 4, ROWB = 128;
-    __shared__ double part_u[16 * kPartPitch]; // reused for the fp32 partials of the readout
+    __shared__ __attribute__((aligned(16))) double part_u[kPartElems]; // reused for the fp32 partials of the readout
     __shared__ __attribute__((aligned(16))) float w_s[128];
     __shared__ double xch[128];
 
@@ -499,12 +502,12 @@ __global__ __launch_bounds__(256, SSQ_DAMP_WAVES) void k_damp_step(DeltaArgs a)
     // ot = St'^T q meets in LDS; o = 2 Hs ot
     float* part_o = reinterpret_cast<float*>(part_u);
 #pragma unroll
-    for (int e = 0; e < E; ++e) part_o[part_idx(rg, j0 + e)] = op[e];
+    for (int e = 0; e < E; ++e) part_o[part_idx_o(rg, j0 + e)] = op[e];
     __syncthreads();
     float ot = 0.0f;
     if (t < 128) {
 #pragma unroll 8
-        for (int r = 0; r < RG; ++r) ot += part_o[part_idx(r, t)];
+        for (int r = 0; r < RG; ++r) ot += part_o[part_idx_o(r, t)];
     }
     const double x = wht128((double)ot, xch);
     if (t < 128) a.o[mrow0 + t] = (float)(x * 0.125);

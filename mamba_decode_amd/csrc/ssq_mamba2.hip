@@ -849,21 +849,34 @@ __global__ __launch_bounds__(256) void k_zero_fill(uint4* p, int64_t n16)
 #define SSQ_WAVES_FP32 3
 #endif
 
+// stochastic rounding keeps the generator's state live beside the ring: its own ring depth
+#ifndef SSQ_RING_INT4_SR
+#define SSQ_RING_INT4_SR 2
+#endif
+#ifndef SSQ_RING_INT8_SR
+#define SSQ_RING_INT8_SR SSQ_RING_INT8
+#endif
+#ifndef SSQ_WAVES_INT4_SR
+#define SSQ_WAVES_INT4_SR SSQ_WAVES_INT4
+#endif
+
 template <int F>
 constexpr int step_iters()
 {
     return F == FP32 ? SSQ_ITERS_FP32 : (Traits<F>::bits == 8 ? SSQ_ITERS_INT8 : SSQ_ITERS_INT4);
 }
-template <int F>
+template <int F, bool SR>
 constexpr int step_ring()
 {
+    if constexpr (SR) return Traits<F>::bits == 8 ? SSQ_RING_INT8_SR : SSQ_RING_INT4_SR;
     return F == FP32 ? SSQ_RING_FP32 : (Traits<F>::bits == 8 ? SSQ_RING_INT8 : SSQ_RING_INT4);
 }
 // the pre-rounding readout keeps C live through the update: one wave less
-template <int F, bool PRE>
+template <int F, bool PRE, bool SR>
 constexpr int step_waves()
 {
-    constexpr int w = F == FP32 ? SSQ_WAVES_FP32 : (Traits<F>::bits == 8 ? SSQ_WAVES_INT8 : SSQ_WAVES_INT4);
+    constexpr int w = F == FP32 ? SSQ_WAVES_FP32
+                                : (Traits<F>::bits == 8 ? SSQ_WAVES_INT8 : (SR ? SSQ_WAVES_INT4_SR : SSQ_WAVES_INT4));
     return PRE && w > 2 ? w - 1 : w;
 }
 
@@ -874,14 +887,14 @@ static hipError_t launch_step_fp(M2Args a, hipStream_t st)
     constexpr int RPW = 64 / LPR;
     a.total_iters = (int64_t)a.Bsz * a.H * a.P / RPW;
     constexpr int kStepIters = step_iters<F>();
-    constexpr int kStepRing = step_ring<F>();
+    constexpr int kStepRing = step_ring<F, SR>();
     static_assert(kStepRing >= 1 && kStepRing <= kStepIters, "prefetch ring deeper than the iterations");
     a.iters_per_wave = kStepIters;
     // main launch: whole groups of K iterations per wave
     const int64_t main_waves = a.total_iters / kStepIters;
     if (main_waves > 0) {
         const unsigned blocks = (unsigned)((main_waves + 3) / 4);
-        hipLaunchKernelGGL((k_m2_step<F, LPR, PRE, kStepIters, kStepRing, step_waves<F, PRE>(), SR>), dim3(blocks),
+        hipLaunchKernelGGL((k_m2_step<F, LPR, PRE, kStepIters, kStepRing, step_waves<F, PRE, SR>(), SR>), dim3(blocks),
                            dim3(256), 0, st, a,
                            (int64_t)0);
         hipError_t e = hipGetLastError();
