@@ -42,18 +42,40 @@ __device__ __forceinline__ void store_row_piece(uint8_t* rows_base, uint32_t row
     buf_store_words<NW, kAuxStoreWhole>(make_rsrc(rows_base, rows_bytes), off, 0u, w);
 }
 
-// Partial rows in LDS.  Thread (r, part) writes columns j = 16*part .. 16*part + 15 of row
-// group r as consecutive elements (16-byte writes), u in double at r*144 + part*18 + (j & 15)
-// and o in float at r*160 + part*20 + (j & 15).  A 16-byte write instruction is served 16
-// lanes at a time (two row groups, eight parts); with these pitches the 16 lanes' four-bank
-// windows tile the 64 banks exactly (double: 2*(144 r + 18 part) mod 64; float: 160 r +
-// 20 part mod 64), so the writes have no bank conflict.
-constexpr int kPartPitchU = 144, kPartStrideU = 18;
-constexpr int kPartPitchO = 160, kPartStrideO = 20;
-__device__ __forceinline__ int part_idx(int r, int j) { return r * kPartPitchU + (j >> 4) * kPartStrideU + (j & 15); }
-__device__ __forceinline__ int part_idx_o(int r, int j) { return r * kPartPitchO + (j >> 4) * kPartStrideO + (j & 15); }
-constexpr int kPartElems = 32 * kPartPitchU; // doubles; the float rows of o fit in the same bytes
-static_assert(32 * kPartPitchO <= 2 * kPartElems, "o's partial rows fit in u's buffer");
+// Partial rows in LDS, 128 columns per row group r, column c stored at r*128 + (c ^ x(c)):
+// u in double with x = 2*(c/16), o in float with x = 4*(c/32).  The XOR stays inside the
+// aligned pair (u) or quad (o) that one 16-byte write carries, so thread (r, part) still
+// writes its 16 columns with 16-byte writes.  gfx950's LDS serves a 16-byte write 8 lanes at
+// a time over 32 four-byte banks, an 8-byte read 16 lanes at a time and a 4-byte read 32
+// lanes at a time over the same 32 banks (and a 16-byte read 16 lanes at a time over 64
+// banks); with these swizzles the eight parts of a write land in eight distinct 16-byte bank
+// windows, and the 16 (u) or 32 (o) consecutive columns that one read serves land in
+// distinct banks, so neither side has a bank conflict.
+__device__ __forceinline__ int part_idx(int r, int c) { return r * 128 + (c ^ (2 * (c >> 4))); }
+__device__ __forceinline__ int part_idx_o(int r, int c) { return r * 128 + (c ^ (4 * (c >> 5))); }
+constexpr int kPartElems = 32 * 128; // doubles; the float rows of o use the first half of the bytes
+// thread (r, part)'s 16 columns 16*part .. 16*part + 15: pairs (u) or quads (o) at the
+// swizzled offsets, one 16-byte write each
+__device__ __forceinline__ void store_part_u(double* pu, int r, int part, const double* v)
+{
+    double* const row = pu + r * 128 + part * 16;
+#pragma unroll
+    for (int e2 = 0; e2 < 8; ++e2)
+        *reinterpret_cast<double2*>(row + 2 * (e2 ^ part)) = make_double2(v[2 * e2], v[2 * e2 + 1]);
+}
+__device__ __forceinline__ void store_part_o(float* po, int r, int part, const float* v)
+{
+    float* const row = po + r * 128 + part * 16;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4*>(row + 4 * (q ^ (part >> 1))) =
+            make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+}
+// w is shared through LDS with 4 floats of padding after every 64: column j sits at
+// j + 4*(j/64), so the eight parts' 16-byte reads (16 lanes, two row groups, per pass) fall in
+// eight distinct 16-byte windows of the 64 banks.
+constexpr int kWPad = 136;
+__device__ __forceinline__ int w_idx(int j) { return j + 4 * (j >> 6); }
 
 // The matrix the step starts from, reconstructed in fp32 (fl(s_i*fl(c_ij - z_i)) for a
 // quantized key row), stays in registers from the u reduction to the update: each entry is
@@ -68,7 +90,7 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_delta_step(DeltaArgs a
     constexpr int NW = Tr::quant ? E * Tr::bits / 32 : E;
     constexpr int ROWB = Tr::quant ? 128 * Tr::bits / 8 : 512;
     __shared__ __attribute__((aligned(16))) double part_u[kPartElems]; // reused for the fp32 partials of o
-    __shared__ __attribute__((aligned(16))) float w_s[128];
+    __shared__ __attribute__((aligned(16))) float w_s[kWPad];
 
     const int t = threadIdx.x;
     const int rg = t >> 3, part = t & 7, j0 = part * E;
@@ -123,8 +145,7 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_delta_step(DeltaArgs a
 #pragma unroll
             for (int e = 0; e < E; ++e) up[e] = __builtin_fma(kd, (double)Sh[r][e], up[e]);
         }
-#pragma unroll
-        for (int e = 0; e < E; ++e) part_u[part_idx(rg, j0 + e)] = up[e];
+        store_part_u(part_u, rg, part, up);
     }
     __syncthreads();
     if (t < 128) {
@@ -136,7 +157,7 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_delta_step(DeltaArgs a
         const float u = (float)acc;
         const float au = KDA ? u : alpha * u;
         const float vm = vcol - au;
-        w_s[t] = beta * vm;
+        w_s[w_idx(t)] = beta * vm;
     }
     __syncthreads();
 
@@ -151,7 +172,7 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_delta_step(DeltaArgs a
         float* const S = Sh[r];
 #pragma unroll
         for (int q = 0; q < E / 4; ++q) {
-            const float4 w4 = reinterpret_cast<const float4*>(w_s + j0)[q];
+            const float4 w4 = reinterpret_cast<const float4*>(w_s + w_idx(j0))[q];
             const float wq[4] = {w4.x, w4.y, w4.z, w4.w};
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
@@ -223,8 +244,7 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_delta_step(DeltaArgs a
 
     // o = S'^T q: 32 partial rows meet in LDS
     float* part_o = reinterpret_cast<float*>(part_u);
-#pragma unroll
-    for (int e = 0; e < E; ++e) part_o[part_idx_o(rg, j0 + e)] = op[e];
+    store_part_o(part_o, rg, part, op);
     __syncthreads();
     if (t < 128) {
         float acc = 0.0f;
@@ -337,7 +357,7 @@ __global__ __launch_bounds__(256, SSQ_DAMP_WAVES) void k_damp_step(DeltaArgs a)
     constexpr int F = INT8_ASYM;
     constexpr int LPR = 8, E = 16, RG = 32, KR = 4, NW = 4, ROWB = 128;
     __shared__ __attribute__((aligned(16))) double part_u[kPartElems]; // reused for the fp32 partials of the readout
-    __shared__ __attribute__((aligned(16))) float w_s[128];
+    __shared__ __attribute__((aligned(16))) float w_s[kWPad];
     __shared__ double xch[128];
 
     const int t = threadIdx.x;
@@ -397,8 +417,7 @@ __global__ __launch_bounds__(256, SSQ_DAMP_WAVES) void k_damp_step(DeltaArgs a)
 #pragma unroll
             for (int e = 0; e < E; ++e) up[e] = __builtin_fma(kd, (double)Sh[r][e], up[e]);
         }
-#pragma unroll
-        for (int e = 0; e < E; ++e) part_u[part_idx(rg, j0 + e)] = up[e];
+        store_part_u(part_u, rg, part, up);
     }
     // vt = Hs v, rounded once; thread t < 128 holds column t (here, where the partial sums
     // of u no longer hold registers)
@@ -411,7 +430,7 @@ __global__ __launch_bounds__(256, SSQ_DAMP_WAVES) void k_damp_step(DeltaArgs a)
         // wt = beta*(vt - alpha*ut), formed once per column and shared
         const float au = alpha * (float)acc;
         const float vm = vt - au;
-        w_s[t] = beta * vm;
+        w_s[w_idx(t)] = beta * vm;
     }
     __syncthreads();
 
@@ -425,7 +444,7 @@ __global__ __launch_bounds__(256, SSQ_DAMP_WAVES) void k_damp_step(DeltaArgs a)
         // every row: St' = fma(alpha, St, fl(k*wt)), wt read from LDS for each row
 #pragma unroll
         for (int q = 0; q < E / 4; ++q) {
-            const float4 w4 = reinterpret_cast<const float4*>(w_s + j0)[q];
+            const float4 w4 = reinterpret_cast<const float4*>(w_s + w_idx(j0))[q];
             const float wq[4] = {w4.x, w4.y, w4.z, w4.w};
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
@@ -501,8 +520,7 @@ __global__ __launch_bounds__(256, SSQ_DAMP_WAVES) void k_damp_step(DeltaArgs a)
 
     // ot = St'^T q meets in LDS; o = 2 Hs ot
     float* part_o = reinterpret_cast<float*>(part_u);
-#pragma unroll
-    for (int e = 0; e < E; ++e) part_o[part_idx_o(rg, j0 + e)] = op[e];
+    store_part_o(part_o, rg, part, op);
     __syncthreads();
     float ot = 0.0f;
     if (t < 128) {
