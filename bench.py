@@ -36,7 +36,9 @@ HBM_PEAK_GBPS = 8000.0
 # lanes x 2.4 GHz).  The kernels are built without packed fp32, so three-operand instructions
 # (fma, med3) issue at half of it, one wave64 instruction per 4 cycles per SIMD (36.4 T/s
 # measured with independent fma chains); two-operand ones issue faster (v_add_f32: 58.5 T/s).
-VALU_PEAK_TOPS = 256 * 4 * 32 * 2.4e9 / 1e12
+SIMDS = 256 * 4
+CLOCK_HZ = 2.4e9
+VALU_PEAK_TOPS = SIMDS * 32 * CLOCK_HZ / 1e12
 
 WORKLOADS = {
     # name: kind, layers, batch, heads, rows_per_head, format, init, tokens (scan), instances
@@ -385,13 +387,24 @@ def main():
     value = state_gbps if not seq else total_gbps
     achieved = bytes_per_launch / (kernel_ms_mean * 1e-3) / 1e9
 
-    # traffic from the committed rocprofv3 counter runs, only while the kernels are unchanged
+    # traffic and VALU instruction counts from the committed rocprofv3 counter runs, only while
+    # the kernels are unchanged
     traffic = None
+    valu = None
     tpath = os.path.join(ROOT, "profiles", "traffic.json")
     if os.path.exists(tpath):
         tr = json.load(open(tpath)).get(args.workload)
         if tr and tr.get("src_hash") == src_hash(kind) and args.batch is None:
             traffic = tr.get("hbm_bytes_per_launch")
+            if tr.get("valu_insts_per_launch"):
+                # wave64 VALU instructions issued per SIMD and cycle of this run's launch time: at
+                # 2.1-4.5 cycles per instruction (by kind), 0.25 or more means the instruction
+                # stream occupies most of the launch
+                per_cycle = tr["valu_insts_per_launch"] / (SIMDS * kernel_ms_mean * 1e-3 * CLOCK_HZ)
+                valu = {"insts_per_launch": tr["valu_insts_per_launch"],
+                        "insts_per_wave": tr.get("valu_insts_per_wave"),
+                        "insts_per_simd_cycle": round(per_cycle, 4),
+                        "source": tr.get("summary")}
 
     rec = {
         "metric": METRIC,
@@ -448,19 +461,21 @@ def main():
             "kernel_ms_mean": round(kernel_ms_mean, 5),
             "kernel_ms_source": "HIP events around the timed region, step time / launches per step",
             "eager_launch_ms_median": round(eager_ms_median, 5),
+            "valu": valu,
         },
         "device": torch.cuda.get_device_name(0),
         "pages_context": PAGES_CONTEXT,
     }
     if seq:
         # the state stays on-chip for all T tokens: the scan is bound by VALU issue.  Algorithmic
-        # work per entry-step, in VALU lane-instructions: the two fmas of the update, the
-        # row's extremes (min3 and max3 each take two new entries: one per entry; the
-        # symmetric grid's |.| max3: one half), the rounding fma, and (c - z) plus one fma
-        # for the readout of the new codes; fp32: the product, the fma and the readout fma.
-        # The prefill runs the fp32 step (3) and, once per chunk, the extremes, the rounding
-        # and the dequantization (c - z, times s): 4 more per chunk
-        ops = 3 if fmt == "fp32" else (6 if fmt.endswith("asym") else 5.5)
+        # work per entry-step, in VALU lane-instructions, of the reconstruct-then-recur step: the
+        # reconstruction s*(c - z) (the scan carries c - z from token to token), the write term
+        # w*B and the fma of the update, the row's extremes (min3 and max3 each take two new
+        # entries: one per entry; the symmetric grid's |.| max3: one half), the rounding fma,
+        # and c' - z' plus one fma for the readout of the new codes; fp32: w*B, the fma and the
+        # readout fma.  The prefill runs the fp32 step (3) and, once per chunk, the extremes,
+        # the rounding and the reconstruction (c - z, times s): 4 more per chunk
+        ops = 3 if fmt == "fp32" else (7 if fmt.endswith("asym") else 6.5)
         if kind == "prefill":
             ops = 3 + 4.0 / wl["chunk"]
         achieved_ops = rows * N * T * ops / (kernel_ms_mean * 1e-3) / 1e12
