@@ -82,9 +82,10 @@ def test_delta_step_teacher_forced(fmt, readout):
 @pytest.mark.parametrize("fmt", ["int8_asym", "int4_asym"])
 @pytest.mark.parametrize("mag", [2.0 ** -118, 2.0 ** 100])
 def test_delta_step_far_from_unit_scale(mag, fmt, kda):
-    """States, v and part of k far from unit size: the products k_i*s_i*c_ij of u sit near
-    2^-130 or 2^100 and some keys are tiny, which the codes-as-subnormal accumulation of u
-    must round exactly as the plain one."""
+    """States, v and part of k far from unit size: the reconstructed entries sit near 2^-118
+    or 2^100 (down to the subnormal range for the smallest), the products k_i*Sh_ij of u near
+    2^-180 or 2^100, and some keys are tiny; the double accumulation of u, the update and the
+    refit must still match the oracle under the contract."""
     B, H = 2, 2
     rows = B * H * 128
     init = (synth.init_state(98, 0, rows, 128).astype(np.float64) * mag).astype(np.float32)
