@@ -394,7 +394,7 @@ def main():
     tpath = os.path.join(ROOT, "profiles", "traffic.json")
     if os.path.exists(tpath):
         tr = json.load(open(tpath)).get(args.workload)
-        if tr and tr.get("src_hash") == src_hash(kind) and args.batch is None:
+        if tr and tr.get("src_hash") == src_hash(kind) and args.batch is None and not args.shared_state:
             traffic = tr.get("hbm_bytes_per_launch")
             if tr.get("valu_insts_per_launch"):
                 # wave64 VALU instructions issued per SIMD and cycle of this run's launch time: at
