@@ -71,6 +71,25 @@ __device__ __forceinline__ void store_part_o(float* po, int r, int part, const f
         *reinterpret_cast<float4*>(row + 4 * (q ^ (part >> 1))) =
             make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
 }
+// Column c's sum over the 32 partial rows, as four interleaved chains (rows r = k mod 4)
+// added pairwise at the end: a dependent chain of 8 + 2 adds instead of 32.  u is summed in
+// double and rounded once and o is an output, so neither fixes this order.
+// T = double: the partial rows of u (part_idx); T = float: those of o (part_idx_o).
+template <typename T>
+__device__ __forceinline__ T column_sum(const T* rows, int c)
+{
+    auto at = [&](int r) { return rows[sizeof(T) == 8 ? part_idx(r, c) : part_idx_o(r, c)]; };
+    T a0 = 0, a1 = 0, a2 = 0, a3 = 0;
+#pragma unroll
+    for (int r = 0; r < 32; r += 4) {
+        a0 += at(r);
+        a1 += at(r + 1);
+        a2 += at(r + 2);
+        a3 += at(r + 3);
+    }
+    return (a0 + a1) + (a2 + a3);
+}
+
 // w is shared through LDS with 4 floats of padding after every 64: column j sits at
 // j + 4*(j/64), so the eight parts' 16-byte reads (16 lanes, two row groups, per pass) fall in
 // eight distinct 16-byte windows of the 64 banks.
@@ -149,9 +168,7 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_delta_step(DeltaArgs a
     }
     __syncthreads();
     if (t < 128) {
-        double acc = 0.0;
-#pragma unroll 8
-        for (int r = 0; r < RG; ++r) acc += part_u[part_idx(r, t)];
+        const double acc = column_sum(part_u, t);
         // w_t = beta*(v_t - alpha*u_t), or beta*(v_t - u_t) for KDA (the decay is
         // already in u), formed once per column and shared
         const float u = (float)acc;
@@ -247,10 +264,7 @@ __global__ __launch_bounds__(256, SSQ_DELTA_WAVES) void k_delta_step(DeltaArgs a
     store_part_o(part_o, rg, part, op);
     __syncthreads();
     if (t < 128) {
-        float acc = 0.0f;
-#pragma unroll 8
-        for (int r = 0; r < RG; ++r) acc += part_o[part_idx_o(r, t)];
-        a.o[mrow0 + t] = acc;
+        a.o[mrow0 + t] = column_sum(part_o, t);
     }
 }
 
@@ -424,9 +438,7 @@ __global__ __launch_bounds__(256, SSQ_DAMP_WAVES) void k_damp_step(DeltaArgs a)
     const float vt = (float)(wht128(vj, xch) * 0.0625);
     __syncthreads();
     if (t < 128) {
-        double acc = 0.0;
-#pragma unroll 8
-        for (int r = 0; r < RG; ++r) acc += part_u[part_idx(r, t)];
+        const double acc = column_sum(part_u, t);
         // wt = beta*(vt - alpha*ut), formed once per column and shared
         const float au = alpha * (float)acc;
         const float vm = vt - au;
@@ -523,10 +535,7 @@ __global__ __launch_bounds__(256, SSQ_DAMP_WAVES) void k_damp_step(DeltaArgs a)
     store_part_o(part_o, rg, part, op);
     __syncthreads();
     float ot = 0.0f;
-    if (t < 128) {
-#pragma unroll 8
-        for (int r = 0; r < RG; ++r) ot += part_o[part_idx_o(r, t)];
-    }
+    if (t < 128) ot = column_sum(part_o, t);
     const double x = wht128((double)ot, xch);
     if (t < 128) a.o[mrow0 + t] = (float)(x * 0.125);
 }
