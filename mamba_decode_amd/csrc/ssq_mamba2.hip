@@ -305,6 +305,24 @@ __device__ __forceinline__ void step_priority(int i)
     }
 }
 
+// The same for the token loop of a scan of a quantized state: 3 for the first half of the T
+// tokens, then 2, 1, 0 (t is uniform, so these are scalar compares).  A/B on one box: the 130m
+// int8 scans 7% faster, the 8B int4 scan 12%; the fp32 scan unchanged and the prefill 4%
+// slower, so those two keep priority 0.
+#ifndef SSQ_SCAN_PRIO
+#define SSQ_SCAN_PRIO 1
+#endif
+template <bool ON>
+__device__ __forceinline__ void token_priority(int t, int T)
+{
+    if constexpr (ON && SSQ_SCAN_PRIO != 0) {
+        if (t == 0) __builtin_amdgcn_s_setprio(3);
+        else if (t == T / 2) __builtin_amdgcn_s_setprio(2);
+        else if (t == 3 * (T / 4)) __builtin_amdgcn_s_setprio(1);
+        else if (t == 7 * (T / 8)) __builtin_amdgcn_s_setprio(0);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // decode step
 // ---------------------------------------------------------------------------
@@ -569,6 +587,7 @@ __global__ __launch_bounds__(256, PRE ? SSQ_SCAN_WAVES - 1 : SSQ_SCAN_WAVES) voi
     // one token; LAST packs the new codes instead of carrying fl(c - z) on
     auto token = [&](int t, auto last) {
         constexpr bool LAST = decltype(last)::value;
+        token_priority<Tr::quant>(t, T);
         if ((t & 63) == 0) {
             const int tt = t + lane;
             if (tt < T) {
