@@ -23,6 +23,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -134,12 +135,19 @@ KERNEL_SOURCES = {"m2": "ssq_mamba2.hip", "scan": "ssq_mamba2.hip", "prefill": "
                   "delta": "ssq_delta.hip", "kda": "ssq_delta.hip"}
 
 
+def _code_only(text: str) -> str:
+    """C++ source without its comments and whitespace: what the compiler sees."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return "".join(text.split())
+
+
 def src_hash(kind: str) -> str:
-    """Hash of the sources a workload's kernel is built from (the committed traffic figures
-    hold only while it is unchanged)."""
+    """Hash of the code a workload's kernel is built from, comments and whitespace left out
+    (the committed traffic figures hold only while it is unchanged)."""
     h = hashlib.sha256()
     for name in ("ssq_device.h", "ssq_internal.h", KERNEL_SOURCES[kind]):
-        h.update(open(os.path.join(ROOT, "mamba_decode_amd", "csrc", name), "rb").read())
+        h.update(_code_only(open(os.path.join(ROOT, "mamba_decode_amd", "csrc", name)).read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -285,12 +285,12 @@ struct RowStep {
 // after about half the launch while the last ones finished alone on a half-idle SIMD (370m
 // int4 layer: waves ending 10.7-21.2 us, the last wave of every SIMD at 19.1-21.2 us).  A wave
 // therefore lowers its own priority as it gets ahead: 3 for the first half of its K iterations,
-// then 2, 1 and 0 for the last quarter's halves (3,3,3,3,2,2,1,0 for K = 8), so that the
-// waves behind it are issued first.  Measured on the 370m int4 layer, A/B on one box: 7.8%
-// faster (stochastic rounding: 10%), the 8B int4 layer unchanged; of the schedules tried this
-// one was fastest (3,3,2,2,1,1,0,0: 6%; 3,2,1,0,...: 3%; the reverse order: no gain).  The
-// int8 step (four iterations per wave, held by memory) keeps priority 0.  SSQ_STEP_PRIO=0
-// switches it off.
+// 2 for the third quarter, 1 and 0 for the two halves of the last quarter (3,3,3,3,2,2,1,0 for
+// K = 8), so that the waves behind it are issued first.  Measured on the 370m int4 layer, A/B
+// on one box: 7.8% faster (stochastic rounding: 10%), the 8B int4 layer unchanged; of the
+// schedules tried this one was fastest (3,3,2,2,1,1,0,0: 6%; 3,2,1,0,...: 3%; the reverse
+// order: no gain).  The int8 step (four iterations per wave, held by memory) keeps priority 0;
+// the fp32 step (eight iterations) takes the same schedule.  SSQ_STEP_PRIO=0 switches it off.
 #ifndef SSQ_STEP_PRIO
 #define SSQ_STEP_PRIO 1
 #endif
