@@ -119,6 +119,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None, help="timed steps (default depends on the workload)")
     ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--device-warmup-ms", type=float, default=DEVICE_WARMUP_MS,
+                    help="wall time of the workload's kernel on a scratch state before the warm-up steps")
     ap.add_argument("--workload", default="m2_370m_int4", choices=sorted(WORKLOADS))
     ap.add_argument("--eager", action="store_true", help="time back-to-back launches instead of graph replays")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -344,7 +346,7 @@ def main():
     t_warm = time.perf_counter()
     warm_launches = 0
     ws = vp(torch.cuda.current_stream().cuda_stream)
-    while (time.perf_counter() - t_warm) * 1e3 < DEVICE_WARMUP_MS:
+    while (time.perf_counter() - t_warm) * 1e3 < args.device_warmup_ms:
         for _ in range(8):
             if launch(0, ws, warm_state) != 0:
                 raise RuntimeError(f"launch failed: {ssq.ssq_last_error()}")
