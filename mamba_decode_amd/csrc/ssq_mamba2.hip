@@ -327,10 +327,12 @@ __device__ __forceinline__ void token_priority(int t, int T)
 // decode step
 // ---------------------------------------------------------------------------
 // Wave w takes iterations [it_base + w*K, it_base + (w+1)*K), all of them
-// valid, as straight-line code: the state words of iteration i + D are loaded
-// while iteration i is processed.  With no loop and no optional store, the
-// compiler's s_waitcnt before each use covers exactly the loads that use needs;
-// a loop-carried prefetch made it wait for younger loads as well.  Every lane
+// valid: the state words of iteration i + D are loaded while iteration i is
+// processed.  K = 8 compiles to straight-line code, where the compiler's
+// s_waitcnt before each use covers exactly the loads that use needs (a
+// loop-carried prefetch made it wait for younger loads as well); the compiler
+// keeps a loop for K = 16 and 32, which pay off only where they spare the
+// launch later rounds of waves (see the launcher).  Every lane
 // of a row stores the row's scale, zero point and y (the same value to the same
 // address), so no store sits behind a branch either.  Leftover iterations (fewer
 // than K) are run by a second launch with K = 1.
@@ -934,13 +936,12 @@ constexpr int step_waves()
     return PRE && w > 2 ? w - 1 : w;
 }
 
-template <int F, bool PRE, bool SR>
-static hipError_t launch_step_fp(M2Args a, hipStream_t st)
+template <int F, bool PRE, bool SR, int kStepIters>
+static hipError_t launch_step_k(M2Args a, hipStream_t st)
 {
     constexpr int LPR = step_lanes_per_row<F>();
     constexpr int RPW = 64 / LPR;
     a.total_iters = (int64_t)a.Bsz * a.H * a.P / RPW;
-    constexpr int kStepIters = step_iters<F>();
     constexpr int kStepRing = step_ring<F, SR>();
     static_assert(kStepRing >= 1 && kStepRing <= kStepIters, "prefetch ring deeper than the iterations");
     a.iters_per_wave = kStepIters;
@@ -965,13 +966,34 @@ static hipError_t launch_step_fp(M2Args a, hipStream_t st)
     return hipSuccess;
 }
 
+// Iterations per wave for this layer: int4 rows (16 per wave-iteration) take 16 or 32 when the
+// layer has enough of them to give every resident wave slot that many, so that the waves
+// run in one round (8B-shaped layer: 4.6% faster with 32 than with four rounds of 8, A/B on one
+// box).  The longer forms are compiled as a loop; the 370m-shaped layer, one round of 8, is
+// slower with them (fewer waves than slots).  int8 rows (8 per wave-iteration) keep 4 at
+// every size (8 or 16 on the 8B-shaped layer: 7% and 16% slower), as does stochastic
+// rounding.
+template <int F, bool PRE, bool SR>
+static hipError_t launch_step_fp(M2Args a, int num_cus, hipStream_t st)
+{
+    constexpr int K0 = step_iters<F>();
+    if constexpr (Traits<F>::quant && Traits<F>::bits == 4 && !SR) {
+        constexpr int RPW = 64 / step_lanes_per_row<F>();
+        const int64_t iters = (int64_t)a.Bsz * a.H * a.P / RPW;
+        const int64_t slots = (int64_t)num_cus * 16; // 4 SIMDs x 4 waves: every int4 form fits 128 registers
+        if (iters >= 4 * K0 * slots) return launch_step_k<F, PRE, SR, 4 * K0>(a, st);
+        if (iters >= 2 * K0 * slots) return launch_step_k<F, PRE, SR, 2 * K0>(a, st);
+    }
+    return launch_step_k<F, PRE, SR, K0>(a, st);
+}
+
 template <int F>
-static hipError_t launch_step_f(M2Args a, bool pre, int /*num_cus*/, hipStream_t st)
+static hipError_t launch_step_f(M2Args a, bool pre, int num_cus, hipStream_t st)
 {
     if constexpr (Traits<F>::quant) {
-        if (a.sr.on) return pre ? launch_step_fp<F, true, true>(a, st) : launch_step_fp<F, false, true>(a, st);
+        if (a.sr.on) return pre ? launch_step_fp<F, true, true>(a, num_cus, st) : launch_step_fp<F, false, true>(a, num_cus, st);
     }
-    return pre ? launch_step_fp<F, true, false>(a, st) : launch_step_fp<F, false, false>(a, st);
+    return pre ? launch_step_fp<F, true, false>(a, num_cus, st) : launch_step_fp<F, false, false>(a, num_cus, st);
 }
 
 hipError_t launch_m2_step(int fmt, M2Args a, bool pre, int num_cus, hipStream_t st)

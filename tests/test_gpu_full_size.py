@@ -8,6 +8,9 @@ run is printed with K.
   seeded random state with 5% x20 outlier rows): every one of the 524,288 rows.
 * Mamba-2 8B-shaped decode layer (batch 256 x 128 heads x 64 x 128), int8 symmetric and
   int4 asymmetric, two steps from a zero state: every one of the 2,097,152 rows.
+* int4 decode layers of 1,048,576 and 2,097,152 rows (the sizes at which a wave takes 16
+  and 32 iterations), both int4 formats and both readouts, from a seeded random state:
+  every row.
 * Delta-rule layer (batch 256 x 32 heads of 128 x 128, int8 asymmetric, seeded random
   state): every one of the 8,192 matrices.
 * Mamba-2 130m-shaped layer (batch 32 x 24 heads x 64 x 128, 2048 tokens, state rounded
@@ -59,13 +62,14 @@ def m2desc(fmt, B, H, P, G=1):
     return ssq.make_desc(ssq.SSQ_MAMBA2, fmt, B, H, P, 128, G)
 
 
-def run_step(gst, x, dt, A, Bm, Cm, D):
+def run_step(gst, x, dt, A, Bm, Cm, D, readout="post"):
     y = torch.empty(x.shape, dtype=torch.float32, device="cuda")
-    ssq.ssq_decode_step(gst, par.dev(x), par.dev(dt), par.dev(A), par.dev(Bm), par.dev(Cm), par.dev(D), y)
+    ro = ssq.SSQ_READ_PRE_QUANT if readout == "pre" else ssq.SSQ_READ_POST_QUANT
+    ssq.ssq_decode_step(gst, par.dev(x), par.dev(dt), par.dev(A), par.dev(Bm), par.dev(Cm), par.dev(D), y, readout=ro)
     return y.cpu().numpy()
 
 
-def _decode_every_row(fmt, B, H, P, init_seed, steps, seed):
+def _decode_every_row(fmt, B, H, P, init_seed, steps, seed, readout="post"):
     rows = B * H * P
     if init_seed is not None:
         say(f"  drawing the fp32 state of {rows} rows")
@@ -83,16 +87,17 @@ def _decode_every_row(fmt, B, H, P, init_seed, steps, seed):
     for t in range(steps):
         say(f"  {fmt} step {t}: {rows} rows")
         x, dt, Bm, Cm, A, D = synth.mamba2_step_inputs(seed, 0, B, H, 1, P, 128, t=t)
-        yg = run_step(gst, x, dt, A, Bm, Cm, D)
-        yo, _, vq = oracle_timed(f"decode step of {rows} rows", oracle.mamba2_step_par, ost, x, dt, A, Bm, Cm, D,
-                                 diag=True)
+        yg = run_step(gst, x, dt, A, Bm, Cm, D, readout)
+        yo, hpre, vq = oracle_timed(f"decode step of {rows} rows", oracle.mamba2_step_par, ost, x, dt, A, Bm, Cm, D,
+                                    readout=readout, diag=True)
         g = par.read_gpu_state(gst, fmt)
         flips = par.check_codes(g, ost.code, ost.scale, ost.zero, vq, fmt, f"{fmt} step {t}")
         err = par.block_rel(yg, yo, axis=2)
         # y against the exact readout of the new row: within the error of an fp32 sum of its 128
         # terms for every row, and within the contract's head-relative tolerance for quantized y
         crow = np.broadcast_to(Cm[:, :, None, :], (B, H, P, 128)).reshape(rows, 128)
-        ratio = par.y_within_sum_bound(yg, yo, crow, ost.dequant(), (D[None, :, None] * x).astype(np.float32))
+        terms = hpre if readout == "pre" else ost.dequant()  # the row the readout sums over
+        ratio = par.y_within_sum_bound(yg, yo, crow, terms, (D[None, :, None] * x).astype(np.float32))
         say(f"  {fmt} step {t}: {flips} codes at a rounding boundary differ, y max relative error {err:.2e}, "
             f"largest error / fp32-sum bound {ratio:.3f}")
         assert ratio <= 1.0
@@ -111,6 +116,17 @@ def test_370m_decode_layer_every_row():
 def test_8b_decode_layer_every_row(fmt):
     say(f"8B decode layer, {fmt}, every row")
     _decode_every_row(fmt, 256, 128, 64, init_seed=None, steps=2, seed=4)
+
+
+@pytest.mark.parametrize("fmt,readout,B", [("int4_sym", "post", 128), ("int4_asym", "post", 128),
+                                           ("int4_sym", "post", 256), ("int4_asym", "pre", 256),
+                                           ("int4_sym", "pre", 128)])
+def test_int4_decode_long_waves_every_row(fmt, readout, B):
+    """int4 layers large enough for the step to give each wave 16 (B = 128: 1,048,576 rows) or
+    32 (B = 256: 2,097,152 rows) iterations on a 256-CU part, both readouts, from a seeded
+    random state, every row compared for two teacher-forced steps."""
+    say(f"int4 decode, {fmt}, {readout} readout, batch {B} x 128 heads x 64, every row")
+    _decode_every_row(fmt, B, 128, 64, init_seed=7, steps=2, seed=9, readout=readout)
 
 
 def test_delta_layer_every_matrix():
