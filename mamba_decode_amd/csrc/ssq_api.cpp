@@ -387,7 +387,8 @@ ssq_status ssq_scan(ssq_state* st, int32_t T, const float* x, const float* dt, c
     SSQ_REQUIRE(T > 0, SSQ_ERR_INVALID_ARG, "T must be positive");
     a.T = T;
     a.sr = sr_args(st);
-    s = from_hip(ssq::launch_m2_scan(st->desc.format, a, readout == SSQ_READ_PRE_QUANT, (hipStream_t)stream),
+    s = from_hip(ssq::launch_m2_scan(st->desc.format, a, readout == SSQ_READ_PRE_QUANT, num_cus(st->device),
+                                     (hipStream_t)stream),
                  "scan launch");
     return s == SSQ_OK ? advance(st, (uint64_t)T, (hipStream_t)stream) : s;
 }
@@ -402,7 +403,7 @@ ssq_status ssq_prefill(ssq_state* st, int32_t T, int32_t chunk, const float* x, 
     SSQ_REQUIRE(chunk > 0, SSQ_ERR_INVALID_ARG, "chunk must be positive");
     a.T = T;
     a.sr = sr_args(st);
-    s = from_hip(ssq::launch_m2_prefill(st->desc.format, a, chunk, readout == SSQ_READ_PRE_QUANT,
+    s = from_hip(ssq::launch_m2_prefill(st->desc.format, a, chunk, readout == SSQ_READ_PRE_QUANT, num_cus(st->device),
                                         (hipStream_t)stream),
                  "prefill launch");
     return s == SSQ_OK ? advance(st, (uint64_t)T, (hipStream_t)stream) : s;

@@ -69,8 +69,8 @@ struct DeltaArgs {
 };
 
 hipError_t launch_m2_step(int fmt, M2Args a, bool pre, int num_cus, hipStream_t st);
-hipError_t launch_m2_scan(int fmt, M2Args a, bool pre, hipStream_t st);
-hipError_t launch_m2_prefill(int fmt, M2Args a, int chunk, bool pre, hipStream_t st);
+hipError_t launch_m2_scan(int fmt, M2Args a, bool pre, int num_cus, hipStream_t st);
+hipError_t launch_m2_prefill(int fmt, M2Args a, int chunk, bool pre, int num_cus, hipStream_t st);
 hipError_t launch_rows(int fmt, QArgs a, bool dequant, hipStream_t st);
 hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t st);
 hipError_t launch_delta_step(int fmt, DeltaArgs a, bool pre, hipStream_t st);

@@ -531,8 +531,8 @@ __global__ __launch_bounds__(256, W) void k_m2_step(M2Args a, int64_t it_base)
 #ifndef SSQ_SCAN_WAVES
 #define SSQ_SCAN_WAVES 4
 #endif
-template <int F, int LPR, bool PRE, bool SR>
-__global__ __launch_bounds__(256, PRE ? SSQ_SCAN_WAVES - 1 : SSQ_SCAN_WAVES) void k_m2_scan(M2Args a)
+template <int F, int LPR, bool PRE, bool SR, int W>
+__global__ __launch_bounds__(256, PRE ? W - 1 : W) void k_m2_scan(M2Args a)
 {
     using Tr = Traits<F>;
     using RS = RowStep<F, LPR, PRE>;
@@ -1008,8 +1008,8 @@ hipError_t launch_m2_step(int fmt, M2Args a, bool pre, int num_cus, hipStream_t 
     return hipErrorInvalidValue;
 }
 
-template <int F>
-static hipError_t launch_scan_f(M2Args a, bool pre, hipStream_t st)
+template <int F, bool PRE, int W>
+static hipError_t launch_scan_k(M2Args a, hipStream_t st)
 {
     constexpr int LPR = lanes_per_row<F>();
     constexpr int RPW = 64 / LPR;
@@ -1018,25 +1018,36 @@ static hipError_t launch_scan_f(M2Args a, bool pre, hipStream_t st)
     const unsigned blocks = (unsigned)((a.total_iters + 3) / 4);
     if constexpr (Traits<F>::quant) {
         if (a.sr.on) {
-            if (pre)
-                hipLaunchKernelGGL((k_m2_scan<F, LPR, true, true>), dim3(blocks), dim3(256), 0, st, a);
-            else
-                hipLaunchKernelGGL((k_m2_scan<F, LPR, false, true>), dim3(blocks), dim3(256), 0, st, a);
+            hipLaunchKernelGGL((k_m2_scan<F, LPR, PRE, true, W>), dim3(blocks), dim3(256), 0, st, a);
             return hipGetLastError();
         }
     }
-    if (pre)
-        hipLaunchKernelGGL((k_m2_scan<F, LPR, true, false>), dim3(blocks), dim3(256), 0, st, a);
-    else
-        hipLaunchKernelGGL((k_m2_scan<F, LPR, false, false>), dim3(blocks), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_m2_scan<F, LPR, PRE, false, W>), dim3(blocks), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
+// Rows with a zero point need more than 128 registers in the scan: with a budget of 4 waves
+// per SIMD they spill to scratch, with 3 they do not.  The 3-wave form is taken where every
+// wave of the scan fits at 3 per SIMD (130m-shaped layer, 3,072 waves: int8 asymmetric scan 2%
+// faster); a layer with more waves keeps 4 per SIMD rather than run a second round (8B-shaped
+// int4 scan, 4,096 waves: 45% slower with 3).
 template <int F>
-static hipError_t launch_prefill_f(M2Args a, int chunk, bool pre, hipStream_t st)
+static hipError_t launch_scan_f(M2Args a, bool pre, int num_cus, hipStream_t st)
+{
+    if (pre) return launch_scan_k<F, true, SSQ_SCAN_WAVES>(a, st);
+    if constexpr (Traits<F>::asym) {
+        const int64_t waves = (int64_t)a.Bsz * a.H * a.P / (64 / lanes_per_row<F>());
+        if (waves <= (int64_t)num_cus * 4 * (SSQ_SCAN_WAVES - 1))
+            return launch_scan_k<F, false, SSQ_SCAN_WAVES - 1>(a, st);
+    }
+    return launch_scan_k<F, false, SSQ_SCAN_WAVES>(a, st);
+}
+
+template <int F>
+static hipError_t launch_prefill_f(M2Args a, int chunk, bool pre, int num_cus, hipStream_t st)
 {
     if constexpr (!Traits<F>::quant) {
-        return launch_scan_f<F>(a, pre, st); // the fp32 state's prefill is the scan
+        return launch_scan_f<F>(a, pre, num_cus, st); // the fp32 state's prefill is the scan
     } else {
         constexpr int LPR = lanes_per_row<F>();
         constexpr int RPW = 64 / LPR;
@@ -1058,26 +1069,26 @@ static hipError_t launch_prefill_f(M2Args a, int chunk, bool pre, hipStream_t st
     }
 }
 
-hipError_t launch_m2_prefill(int fmt, M2Args a, int chunk, bool pre, hipStream_t st)
+hipError_t launch_m2_prefill(int fmt, M2Args a, int chunk, bool pre, int num_cus, hipStream_t st)
 {
     switch (fmt) {
-    case FP32: return launch_prefill_f<FP32>(a, chunk, pre, st);
-    case INT8_SYM: return launch_prefill_f<INT8_SYM>(a, chunk, pre, st);
-    case INT8_ASYM: return launch_prefill_f<INT8_ASYM>(a, chunk, pre, st);
-    case INT4_SYM: return launch_prefill_f<INT4_SYM>(a, chunk, pre, st);
-    case INT4_ASYM: return launch_prefill_f<INT4_ASYM>(a, chunk, pre, st);
+    case FP32: return launch_prefill_f<FP32>(a, chunk, pre, num_cus, st);
+    case INT8_SYM: return launch_prefill_f<INT8_SYM>(a, chunk, pre, num_cus, st);
+    case INT8_ASYM: return launch_prefill_f<INT8_ASYM>(a, chunk, pre, num_cus, st);
+    case INT4_SYM: return launch_prefill_f<INT4_SYM>(a, chunk, pre, num_cus, st);
+    case INT4_ASYM: return launch_prefill_f<INT4_ASYM>(a, chunk, pre, num_cus, st);
     }
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_m2_scan(int fmt, M2Args a, bool pre, hipStream_t st)
+hipError_t launch_m2_scan(int fmt, M2Args a, bool pre, int num_cus, hipStream_t st)
 {
     switch (fmt) {
-    case FP32: return launch_scan_f<FP32>(a, pre, st);
-    case INT8_SYM: return launch_scan_f<INT8_SYM>(a, pre, st);
-    case INT8_ASYM: return launch_scan_f<INT8_ASYM>(a, pre, st);
-    case INT4_SYM: return launch_scan_f<INT4_SYM>(a, pre, st);
-    case INT4_ASYM: return launch_scan_f<INT4_ASYM>(a, pre, st);
+    case FP32: return launch_scan_f<FP32>(a, pre, num_cus, st);
+    case INT8_SYM: return launch_scan_f<INT8_SYM>(a, pre, num_cus, st);
+    case INT8_ASYM: return launch_scan_f<INT8_ASYM>(a, pre, num_cus, st);
+    case INT4_SYM: return launch_scan_f<INT4_SYM>(a, pre, num_cus, st);
+    case INT4_ASYM: return launch_scan_f<INT4_ASYM>(a, pre, num_cus, st);
     }
     return hipErrorInvalidValue;
 }
