@@ -118,15 +118,16 @@ def test_8b_decode_layer_every_row(fmt):
     _decode_every_row(fmt, 256, 128, 64, init_seed=None, steps=2, seed=4)
 
 
-@pytest.mark.parametrize("fmt,readout,B", [("int4_sym", "post", 128), ("int4_asym", "post", 128),
-                                           ("int4_sym", "post", 256), ("int4_asym", "pre", 256),
-                                           ("int4_sym", "pre", 128)])
-def test_int4_decode_long_waves_every_row(fmt, readout, B):
-    """int4 layers large enough for the step to give each wave 16 (B = 128: 1,048,576 rows) or
-    32 (B = 256: 2,097,152 rows) iterations on a 256-CU part, both readouts, from a seeded
-    random state, every row compared for two teacher-forced steps."""
-    say(f"int4 decode, {fmt}, {readout} readout, batch {B} x 128 heads x 64, every row")
-    _decode_every_row(fmt, B, 128, 64, init_seed=7, steps=2, seed=9, readout=readout)
+@pytest.mark.parametrize("fmt,readout,B,H,P", [("int4_sym", "post", 128, 128, 64), ("int4_asym", "post", 128, 128, 64),
+                                               ("int4_sym", "post", 256, 128, 64), ("int4_asym", "pre", 256, 128, 64),
+                                               ("int4_sym", "pre", 128, 128, 64), ("int4_asym", "post", 131100, 1, 16)])
+def test_int4_decode_long_waves_every_row(fmt, readout, B, H, P):
+    """int4 layers large enough for the step to give each wave 16 (1,048,576 rows) or 32
+    (2,097,152 rows) iterations on a 256-CU part, both readouts, from a seeded random state,
+    every row compared for two teacher-forced steps.  131,100 sequences of one 16-row head
+    make 131,100 iterations: 4,096 waves of 32 and 28 left over for the one-iteration launch."""
+    say(f"int4 decode, {fmt}, {readout} readout, batch {B} x {H} heads x {P}, every row")
+    _decode_every_row(fmt, B, H, P, init_seed=7, steps=2, seed=9, readout=readout)
 
 
 def test_delta_layer_every_matrix():
