@@ -37,12 +37,22 @@ HBM_PEAK_GBPS = 8000.0
 DEVICE_WARMUP_MS = 150.0
 # VALU roofline of the on-chip paths, in lane-operations/s: the fp32 vector peak (157.3 TFLOP/s,
 # an fma counted as two flops) is 78.6 T fp32 operations per second (256 CUs x 4 SIMDs x 32
-# lanes x 2.4 GHz).  The kernels are built without packed fp32, so three-operand instructions
-# (fma, med3) issue at half of it, one wave64 instruction per 4 cycles per SIMD (36.4 T/s
-# measured with independent fma chains); two-operand ones issue faster (v_add_f32: 58.5 T/s).
+# lanes x 2.4 GHz).  The kernels are built without packed fp32: a wave64 fp32 add, multiply or
+# fma issues in 2.5-2.7 cycles per SIMD (about 60 T lane-ops/s over the part), conversions,
+# min3/max3, perm, DPP forms and fp64 in 4.3-4.8 (about 35 T/s), measured.
 SIMDS = 256 * 4
 CLOCK_HZ = 2.4e9
 VALU_PEAK_TOPS = SIMDS * 32 * CLOCK_HZ / 1e12
+# What holds each kernel, from the profiles: every step kernel but the int8 one takes the same
+# time with its state cache-resident (--shared-state) and issues VALU instructions for most of
+# its launch; the int8 decode runs at about 90% of the streaming copy; the scans and the
+# prefill keep the state on-chip for all their tokens.
+LIMITED_BY = {
+    "valu_issue": "the launch takes the same time with the state cache-resident (--shared-state), and its "
+                  "VALU instructions at their measured issue costs fill most of it (roofline.valu)",
+    "hbm": "about 90% of the streaming copy's bandwidth in the same run (frac_of_copy)",
+    "valu_issue_on_chip": "the state stays on-chip for all T tokens: VALU issue",
+}
 
 WORKLOADS = {
     # name: kind, layers, batch, heads, rows_per_head, format, init, tokens (scan), instances
@@ -442,6 +452,7 @@ def main():
                         "insts_per_simd_cycle": round(per_cycle, 4),
                         "source": tr.get("summary")}
 
+    limited = ("valu_issue_on_chip" if seq else ("hbm" if fmt.startswith("int8") and kind == "m2" else "valu_issue"))
     rec = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -501,6 +512,8 @@ def main():
             "kernel_ms_source": "HIP events around the timed region, step time / launches per step",
             "eager_launch_ms_median": round(eager_ms_median, 5),
             "valu": valu,
+            "limited_by": limited,
+            "limited_by_evidence": LIMITED_BY[limited],
         },
         "device": torch.cuda.get_device_name(0),
         "pages_context": PAGES_CONTEXT,
