@@ -876,7 +876,8 @@ __global__ __launch_bounds__(256) void k_zero_fill(uint4* p, int64_t n16)
 // and C in LDS and buffer addressing both quantized widths fit 128 registers
 // (4 waves per SIMD); int4: K = 8 makes one round of resident waves at 370m shape;
 // int8 (8 rows per wave-iteration): K = 4 with every iteration's loads issued up front
-// measured fastest (K = 8 with a ring of 4 about 3% slower, K = 1 or a ring of 3 about 20%).
+// measured fastest (K = 8 with a ring of 4 about 3% slower, K = 1 or a ring of 3 about 20%;
+// on the 8B-shaped layer K = 2 31% slower and K = 8 with all eight up front 9%).
 #ifndef SSQ_ITERS_INT4
 #define SSQ_ITERS_INT4 8
 #endif
