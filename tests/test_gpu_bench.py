@@ -12,9 +12,11 @@ pytestmark = pytest.mark.gpu
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-@pytest.mark.parametrize("workload,bound", [("m2_370m_int4", "hbm"), ("delta_int8", "hbm"),
-                                            ("m2_130m_scan_int8asym", "alu")])
-def test_bench_json_line(workload, bound):
+@pytest.mark.parametrize("workload,bound,limited", [("m2_370m_int4", "hbm", "valu_issue"),
+                                                    ("delta_int8", "hbm", "valu_issue"),
+                                                    ("m2_8b_int8sym", "hbm", "hbm"),
+                                                    ("m2_130m_scan_int8asym", "alu", "valu_issue_on_chip")])
+def test_bench_json_line(workload, bound, limited):
     print(f"bench {workload}", file=sys.stderr, flush=True)
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", workload, "--layers", "2",
                         "--steps", "2", "--warmup", "1", "--no-cpu-baseline"],
@@ -33,4 +35,5 @@ def test_bench_json_line(workload, bound):
     assert rf["bound"] == bound and rf["peak"] > 0 and 0 < rf["frac"] < 1.5
     assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3
     assert rf["unit"] == ("GB/s" if bound == "hbm" else "T lane-ops/s")
+    assert rf["limited_by"] == limited and rf["limited_by_evidence"]
     assert d["copy_GBps"] > 1000 and "cpu_baseline" not in d
